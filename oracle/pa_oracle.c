@@ -1,0 +1,410 @@
+/*
+ * pa_oracle.c -- plain CPU float64 reference for paged KV append and paged attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or call this
+ * file; only the test suite, the smoke check and the benchmark's CPU-baseline leg do.
+ * It shares no code with the HIP library: the pool layout, the dtype decoders, the fp8
+ * encoder and the attention arithmetic are all written out here from their definitions.
+ *
+ * What it computes (sources are the four scraped pages on paged KV caches):
+ *   - attention is softmax(Q K^T / sqrt(d)) V                (page 1, section 2 "what the
+ *     KV cache stores", the Attention(Q,K,V) formula);
+ *   - each sequence's KV lives in fixed-size physical blocks reached through a per-sequence
+ *     block table that maps logical block i to a physical block  (page 1, section 4
+ *     "PagedAttention", the logical->physical mapping figure; page 3, section 2.1, which
+ *     gives 16 tokens as the default block size and says the kernel reads KV block by
+ *     block through the table instead of assuming contiguity);
+ *   - several query heads share one KV head (GQA)            (page 1, section 10);
+ *   - the KV cache may be stored as 8-bit floats, e4m3 preferred over e5m2, with
+ *     per-tensor or per-head scales                          (page 1, section 15; page 2,
+ *     "quantisation"; page 3, section 2.4).
+ * Each decode step produces the new token's K/V and stores it in the cache, and the new
+ * query attends over all stored positions including that one (page 1, section 1, the
+ * prefill/decode diagram).
+ *
+ * The attention is evaluated token by token, walking the block table: for each query row
+ * the scores z_t = scale * <q, K_t> are formed for every visible position t, then the plain
+ * two-pass softmax  w_t = exp(z_t - max z),  out = sum_t w_t V_t / sum_t w_t  is applied.
+ * There is no online-softmax trick, no blocking and no reordering.
+ *
+ * Pool layout (a format both sides must agree on; the pages give none).  Let e be the
+ * element size in bytes (4 fp32, 2 bf16, 1 fp8), W = 64 / e, and B the block size.  The
+ * K pool and the V pool are each [num_blocks][num_kv_heads][B * D] elements; inside one
+ * (block, kv head) tile of B*D elements, token o (0 <= o < B) and channel d are at
+ *     K:  (d / W) * (B * W) + o * W + (d % W)
+ *     V:  (d / W) * (B * W) + (o / 2) * (2 * W) + (d % W) * 2 + (o % 2)
+ * i.e. K is split into 64-byte channel slices stored token-major, and V the same but with
+ * the two tokens of each even/odd pair interleaved element by element.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8_E4M3 = 2 };
+
+enum {
+    OR_OK = 0,
+    OR_ERR_ARG = 1,
+    OR_ERR_DTYPE = 2,
+    OR_ERR_BOUNDS = 3,
+    OR_ERR_NOMEM = 4,
+};
+
+static int elem_bytes(int dtype)
+{
+    switch (dtype) {
+    case OR_F32: return 4;
+    case OR_BF16: return 2;
+    case OR_FP8_E4M3: return 1;
+    default: return 0;
+    }
+}
+
+/* ---- layout ----------------------------------------------------------------------- */
+
+int64_t oracle_k_elem_index(int64_t block, int kv_head, int token, int d,
+                            int num_kv_heads, int head_dim, int block_size, int dtype)
+{
+    int e = elem_bytes(dtype);
+    if (e == 0) return -1;
+    int64_t W = 64 / e;
+    int64_t tile = ((int64_t)block * num_kv_heads + kv_head) * (int64_t)block_size * head_dim;
+    return tile + (d / W) * ((int64_t)block_size * W) + (int64_t)token * W + (d % W);
+}
+
+int64_t oracle_v_elem_index(int64_t block, int kv_head, int token, int d,
+                            int num_kv_heads, int head_dim, int block_size, int dtype)
+{
+    int e = elem_bytes(dtype);
+    if (e == 0) return -1;
+    int64_t W = 64 / e;
+    int64_t tile = ((int64_t)block * num_kv_heads + kv_head) * (int64_t)block_size * head_dim;
+    return tile + (d / W) * ((int64_t)block_size * W) + (int64_t)(token / 2) * (2 * W)
+           + (d % W) * 2 + (token % 2);
+}
+
+/* The layout needs whole 64-byte channel slices and whole token pairs. */
+static int layout_ok(int head_dim, int block_size, int dtype)
+{
+    int e = elem_bytes(dtype);
+    if (e == 0 || head_dim <= 0 || block_size <= 0) return 0;
+    return (head_dim % (64 / e)) == 0 && (block_size % 2) == 0;
+}
+
+/* ---- element decoders ------------------------------------------------------------- */
+
+static double bf16_bits_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16; /* bf16 is the top half of an IEEE binary32 */
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+static double f32_bits_to_double(const unsigned char* p)
+{
+    float f;
+    memcpy(&f, p, 4);
+    return (double)f;
+}
+
+/* OCP 8-bit float E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits;
+ * exponent 0 is subnormal (m * 2^-9); no infinities; S.1111.111 is NaN; max 448. */
+double oracle_e4m3_to_double(uint8_t c)
+{
+    int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp((double)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */
+    return s ? -v : v;
+}
+
+/* Round a binary32 value to E4M3 with round-to-nearest-even, saturating finite
+ * magnitudes above the largest finite value (448) to +-448; NaN keeps its sign bit and
+ * maps to S.1111.111.  Found by comparing |y| against the sorted table of the 127
+ * non-negative finite magnitudes (codes 0..126 are increasing in value). */
+uint8_t oracle_e4m3_encode(float y)
+{
+    uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    if (isnan(y)) return sign | 0x7f;
+    double a = fabs((double)y);
+    if (a >= 448.0) return sign | 0x7e;
+    /* largest code lo in [0, 125] with value(lo) <= a (binary search over codes) */
+    int lo = 0, hi = 126; /* invariant: value(lo) <= a < value(hi) */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (oracle_e4m3_to_double((uint8_t)mid) <= a)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    double dlo = a - oracle_e4m3_to_double((uint8_t)lo); /* exact: both have few bits */
+    double dhi = oracle_e4m3_to_double((uint8_t)hi) - a;
+    int code;
+    if (dlo < dhi)
+        code = lo;
+    else if (dhi < dlo)
+        code = hi;
+    else
+        code = (lo % 2 == 0) ? lo : hi; /* tie: even mantissa (code parity = mantissa LSB) */
+    return sign | (uint8_t)code;
+}
+
+static double load_elem(const unsigned char* base, int64_t idx, int dtype)
+{
+    switch (dtype) {
+    case OR_F32: return f32_bits_to_double(base + idx * 4);
+    case OR_BF16: {
+        uint16_t b;
+        memcpy(&b, base + idx * 2, 2);
+        return bf16_bits_to_double(b);
+    }
+    case OR_FP8_E4M3: return oracle_e4m3_to_double(base[idx]);
+    default: return NAN;
+    }
+}
+
+/* ---- paged KV append --------------------------------------------------------------- */
+
+/* For every token i with slot_mapping[i] >= 0 the token goes to physical block
+ * slot / block_size at offset slot % block_size, for every kv head and channel.  Same
+ * source and cache dtype: the element's bits are copied.  fp32/bf16 source into an E4M3
+ * cache: the stored code is e4m3(fl32(x / scale[h])) -- one IEEE binary32 division by that
+ * head's scale, then the rounding above. */
+int oracle_kv_cache_write(const void* key, const void* value, int src_dtype,
+                          void* k_pool, void* v_pool, int cache_dtype, int64_t num_blocks,
+                          const int64_t* slot_mapping, int64_t num_tokens,
+                          int num_kv_heads, int head_dim, int block_size,
+                          const float* k_scale, const float* v_scale)
+{
+    int es = elem_bytes(src_dtype), ec = elem_bytes(cache_dtype);
+    if (!es || !ec) return OR_ERR_DTYPE;
+    if (src_dtype == OR_FP8_E4M3) return OR_ERR_DTYPE;
+    if (src_dtype != cache_dtype && cache_dtype != OR_FP8_E4M3) return OR_ERR_DTYPE;
+    if (cache_dtype == OR_FP8_E4M3 && (!k_scale || !v_scale)) return OR_ERR_ARG;
+    if (!layout_ok(head_dim, block_size, cache_dtype)) return OR_ERR_ARG;
+    const unsigned char* src[2] = {(const unsigned char*)key, (const unsigned char*)value};
+    unsigned char* dst[2] = {(unsigned char*)k_pool, (unsigned char*)v_pool};
+    const float* scl[2] = {k_scale, v_scale};
+    for (int64_t i = 0; i < num_tokens; i++) {
+        int64_t slot = slot_mapping[i];
+        if (slot < 0) continue;
+        int64_t b = slot / block_size;
+        int o = (int)(slot % block_size);
+        if (b >= num_blocks) return OR_ERR_BOUNDS;
+        for (int kv = 0; kv < 2; kv++) {
+            for (int h = 0; h < num_kv_heads; h++) {
+                for (int d = 0; d < head_dim; d++) {
+                    int64_t si = ((int64_t)i * num_kv_heads + h) * head_dim + d;
+                    int64_t di = kv == 0
+                        ? oracle_k_elem_index(b, h, o, d, num_kv_heads, head_dim, block_size, cache_dtype)
+                        : oracle_v_elem_index(b, h, o, d, num_kv_heads, head_dim, block_size, cache_dtype);
+                    if (src_dtype == cache_dtype) {
+                        memcpy(dst[kv] + di * ec, src[kv] + si * es, (size_t)es);
+                    } else {
+                        float x;
+                        if (src_dtype == OR_F32) {
+                            memcpy(&x, src[kv] + si * 4, 4);
+                        } else {
+                            uint16_t bb;
+                            memcpy(&bb, src[kv] + si * 2, 2);
+                            x = (float)bf16_bits_to_double(bb);
+                        }
+                        float y = x / scl[kv][h]; /* binary32 division, round to nearest */
+                        dst[kv][di] = oracle_e4m3_encode(y);
+                    }
+                }
+            }
+        }
+    }
+    return OR_OK;
+}
+
+/* ---- paged attention ---------------------------------------------------------------- */
+
+typedef struct {
+    double* out;
+    const unsigned char* q;
+    int q_dtype;
+    const unsigned char* kp;
+    const unsigned char* vp;
+    int cache_dtype;
+    int64_t num_blocks;
+    const int32_t* tables;
+    int mbps;
+    const int32_t* ctx;
+    const int32_t* cu_q;
+    int num_seqs, hq, hkv, d, bs;
+    double scale;
+    const float* k_scale;
+    const float* v_scale;
+    int64_t total_rows;
+    int nthreads, tid;
+    int status;
+} job_t;
+
+/* One query row (sequence s, row i of its q_len rows, query head h). */
+static int attend_row(const job_t* J, int s, int64_t row, int i, int q_len, int h)
+{
+    const int G = J->hq / J->hkv;
+    const int g = h / G; /* query head h reads kv head floor(h / G) */
+    const int D = J->d, B = J->bs;
+    double* out = J->out + (row * J->hq + h) * (int64_t)D;
+    int pos = J->ctx[s] - q_len + i; /* the chunk is the last q_len positions of ctx */
+    int n = pos + 1;                 /* visible positions 0..pos */
+    for (int dd = 0; dd < D; dd++) out[dd] = 0.0;
+    if (n <= 0) return OR_OK;
+    if ((n + B - 1) / B > J->mbps) return OR_ERR_BOUNDS;
+    double ks = 1.0, vs = 1.0;
+    if (J->cache_dtype == OR_FP8_E4M3) {
+        ks = (double)J->k_scale[g];
+        vs = (double)J->v_scale[g];
+    }
+    double* qv = (double*)malloc(sizeof(double) * D);
+    double* z = (double*)malloc(sizeof(double) * (size_t)n);
+    if (!qv || !z) {
+        free(qv);
+        free(z);
+        return OR_ERR_NOMEM;
+    }
+    for (int dd = 0; dd < D; dd++)
+        qv[dd] = load_elem(J->q, (row * J->hq + h) * (int64_t)D + dd, J->q_dtype);
+    /* scores, token by token through the block table */
+    for (int t = 0; t < n; t++) {
+        int64_t b = J->tables[(int64_t)s * J->mbps + t / B];
+        int o = t % B;
+        if (b < 0 || b >= J->num_blocks) {
+            free(qv);
+            free(z);
+            return OR_ERR_BOUNDS;
+        }
+        double dot = 0.0;
+        for (int dd = 0; dd < D; dd++) {
+            int64_t ki = oracle_k_elem_index(b, g, o, dd, J->hkv, D, B, J->cache_dtype);
+            dot += qv[dd] * (ks * load_elem(J->kp, ki, J->cache_dtype));
+        }
+        z[t] = J->scale * dot;
+    }
+    /* two-pass softmax */
+    double m = -INFINITY;
+    for (int t = 0; t < n; t++)
+        if (z[t] > m) m = z[t];
+    double den = 0.0;
+    for (int t = 0; t < n; t++) {
+        z[t] = exp(z[t] - m);
+        den += z[t];
+    }
+    for (int t = 0; t < n; t++) {
+        int64_t b = J->tables[(int64_t)s * J->mbps + t / B];
+        int o = t % B;
+        for (int dd = 0; dd < D; dd++) {
+            int64_t vi = oracle_v_elem_index(b, g, o, dd, J->hkv, D, B, J->cache_dtype);
+            out[dd] += z[t] * (vs * load_elem(J->vp, vi, J->cache_dtype));
+        }
+    }
+    for (int dd = 0; dd < D; dd++) out[dd] /= den;
+    free(qv);
+    free(z);
+    return OR_OK;
+}
+
+static void* worker(void* arg)
+{
+    job_t* J = (job_t*)arg;
+    int64_t items = J->total_rows * J->hq;
+    for (int64_t it = J->tid; it < items; it += J->nthreads) {
+        int64_t row = it / J->hq;
+        int h = (int)(it % J->hq);
+        /* sequence owning this row: cu_q is a non-decreasing prefix sum */
+        int s = 0;
+        while (s + 1 < J->num_seqs && J->cu_q[s + 1] <= row) s++;
+        int q_len = J->cu_q[s + 1] - J->cu_q[s];
+        int i = (int)(row - J->cu_q[s]);
+        int st = attend_row(J, s, row, i, q_len, h);
+        if (st != OR_OK) {
+            J->status = st;
+            return NULL;
+        }
+    }
+    return NULL;
+}
+
+/* out: float64 [total_rows][num_heads][head_dim], total_rows = cu_q[num_seqs].
+ * query: [total_rows][num_heads][head_dim] in q_dtype.  context_lens[s] counts every
+ * position of sequence s including its q_len new rows.  Decode is cu_q = 0,1,2,...,S. */
+int oracle_paged_attention(double* out, const void* query, int q_dtype,
+                           const void* k_pool, const void* v_pool, int cache_dtype,
+                           int64_t num_blocks, const int32_t* block_tables, int max_blocks_per_seq,
+                           const int32_t* context_lens, const int32_t* cu_q, int num_seqs,
+                           int num_heads, int num_kv_heads, int head_dim, int block_size,
+                           double scale, const float* k_scale, const float* v_scale, int nthreads)
+{
+    if (!elem_bytes(q_dtype) || q_dtype == OR_FP8_E4M3 || !elem_bytes(cache_dtype)) return OR_ERR_DTYPE;
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads) return OR_ERR_ARG;
+    if (!layout_ok(head_dim, block_size, cache_dtype)) return OR_ERR_ARG;
+    if (cache_dtype == OR_FP8_E4M3 && (!k_scale || !v_scale)) return OR_ERR_ARG;
+    if (num_seqs == 0) return OR_OK;
+    for (int s = 0; s < num_seqs; s++)
+        if (cu_q[s + 1] < cu_q[s]) return OR_ERR_ARG;
+    if (nthreads < 1) nthreads = 1;
+    job_t base = {out, (const unsigned char*)query, q_dtype, (const unsigned char*)k_pool,
+                  (const unsigned char*)v_pool, cache_dtype, num_blocks, block_tables,
+                  max_blocks_per_seq, context_lens, cu_q, num_seqs, num_heads, num_kv_heads,
+                  head_dim, block_size, scale, k_scale, v_scale, cu_q[num_seqs], nthreads, 0, OR_OK};
+    job_t* jobs = (job_t*)malloc(sizeof(job_t) * (size_t)nthreads);
+    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    if (!jobs || !th) {
+        free(jobs);
+        free(th);
+        return OR_ERR_NOMEM;
+    }
+    char* running = (char*)calloc((size_t)nthreads, 1);
+    if (!running) {
+        free(jobs);
+        free(th);
+        return OR_ERR_NOMEM;
+    }
+    for (int k = 0; k < nthreads; k++) {
+        jobs[k] = base;
+        jobs[k].tid = k;
+    }
+    for (int k = 1; k < nthreads; k++)
+        running[k] = pthread_create(&th[k], NULL, worker, &jobs[k]) == 0;
+    worker(&jobs[0]);
+    for (int k = 1; k < nthreads; k++) {
+        if (running[k])
+            pthread_join(th[k], NULL);
+        else
+            worker(&jobs[k]); /* thread could not be started: do its share here */
+    }
+    free(running);
+    int st = OR_OK;
+    for (int k = 0; k < nthreads; k++)
+        if (jobs[k].status != OR_OK) st = jobs[k].status;
+    free(jobs);
+    free(th);
+    return st;
+}
+
+/* Closed form for the KV footprint per token: layers x kv_heads x head_dim x 2 (K and V)
+ * x bytes per element (page 1, section 2.1; page 3, section 2.1). */
+int64_t oracle_kv_bytes_per_token(int num_layers, int num_kv_heads, int head_dim, int dtype)
+{
+    return (int64_t)num_layers * num_kv_heads * head_dim * 2 * elem_bytes(dtype);
+}
+
+/* Array forms of the E4M3 codec, for exhaustive tests. */
+void oracle_e4m3_encode_array(const float* y, uint8_t* codes, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) codes[i] = oracle_e4m3_encode(y[i]);
+}
+
+void oracle_e4m3_decode_array(const uint8_t* codes, double* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = oracle_e4m3_to_double(codes[i]);
+}

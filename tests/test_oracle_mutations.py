@@ -1,0 +1,72 @@
+"""Planted mistakes in the oracle must fail a pin.
+
+Each case copies oracle/pa_oracle.c, plants one plausible mistake (a wrong index, a dropped
+term, an off-by-one, a wrong rounding rule), compiles it with gcc into a temporary library,
+swaps it in for the real oracle and runs the pins that should catch it.  The real oracle is
+restored afterwards.  CPU only.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_cache_461_amd import workloads as W
+from tests import test_oracle_pins as pins
+
+SRC = open(os.path.join(os.path.dirname(oracle.__file__), "pa_oracle.c")).read()
+
+MUTANTS = {
+    "gqa_map_modulo": ("const int g = h / G;", "const int g = h % J->hkv;"),
+    "scale_dropped": ("z[t] = J->scale * dot;", "z[t] = dot;"),
+    "causal_off_by_one": ("int n = pos + 1;", "int n = pos;"),
+    "token_in_block_shift": ("        int o = t % B;\n        if (b < 0",
+                             "        int o = (t + 1) % B;\n        if (b < 0"),
+    "v_scale_dropped": ("(vs * load_elem(J->vp", "(1.0 * load_elem(J->vp"),
+    "k_scale_dropped": ("(ks * load_elem(J->kp", "(1.0 * load_elem(J->kp"),
+    "write_slot_offset": ("int o = (int)(slot % block_size);", "int o = (int)(slot % block_size) ^ 1;"),
+    "e4m3_tie_away": ("code = (lo % 2 == 0) ? lo : hi;", "code = hi;"),
+    "e4m3_subnormal_scale": ("v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
+    "e4m3_no_saturation": ("if (a >= 448.0) return sign | 0x7e;", "if (a >= 464.0) return sign | 0x7f;"),
+    "fp8_multiply_not_divide": ("float y = x / scl[kv][h];", "float y = x * scl[kv][h];"),
+    "softmax_denominator_dropped": ("for (int dd = 0; dd < D; dd++) out[dd] /= den;", ""),
+    "kv_bytes_missing_factor_2": ("head_dim * 2 * elem_bytes(dtype)", "head_dim * elem_bytes(dtype)"),
+}
+
+
+def _checks():
+    """The pins, as plain callables; a mutant must make at least one raise."""
+    yield lambda: pins.test_decode_equals_sdpa(pins.CASES[0])
+    yield lambda: pins.test_decode_equals_sdpa(pins.CASES[2])
+    yield lambda: pins.test_decode_equals_sdpa(pins.CASES[5])
+    yield lambda: pins.test_chunked_prefill_equals_sdpa_causal(W.BF16)
+    yield lambda: pins.test_e4m3_decode_table_matches_torch()
+    yield lambda: pins.test_e4m3_encode_matches_torch_rne(0.0103125)
+    yield lambda: pins.test_e4m3_round_trip_and_ties()
+    yield lambda: pins.test_kv_size_closed_forms()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    assert SRC.count(old) == 1, "mutation anchor not unique: %s" % name
+    src = tmp_path / "mutant.c"
+    src.write_text(SRC.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread", "-o", str(so), str(src), "-lm"],
+                   check=True)
+    real = oracle._load()
+    oracle._lib = oracle._bind(ctypes.CDLL(str(so)))
+    caught = []
+    try:
+        for check in _checks():
+            try:
+                check()
+            except (AssertionError, RuntimeError) as e:  # a failed pin or an oracle error
+                caught.append(type(e).__name__)
+                break
+    finally:
+        oracle._lib = real
+    assert caught, "mutant %s passed every pin" % name
