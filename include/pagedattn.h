@@ -1,0 +1,181 @@
+/*
+ * pagedattn.h -- C ABI of libpagedattn.so: paged KV append and PagedAttention for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (from the four pages on paged KV caches):
+ *   - attention of a query over its sequence's cached keys and values is
+ *     softmax(q K^T * scale) V with scale = 1/sqrt(head_dim)   (page 1, section 2, the
+ *     Attention(Q,K,V) formula);
+ *   - the KV cache of every sequence is cut into fixed-size physical blocks (16 tokens by
+ *     default) held in one pool; a per-sequence block table maps logical block i to a
+ *     physical block, and the attention reads the cache block by block through that table
+ *     rather than assuming contiguous storage (page 1, section 4 and its worked mapping
+ *     0->7, 1->2, 2->19, 3->4; page 3, section 2.1);
+ *   - several query heads share one KV head (grouped-query attention; page 1, section 10);
+ *   - each decode step writes the new token's K and V into its block slot before attending
+ *     (page 1, section 1, the prefill/decode diagram);
+ *   - the cache may be stored as 8-bit E4M3 floats with per-head scales (page 1, section 15;
+ *     page 2, quantisation; page 3, section 2.4);
+ *   - a long prompt may be processed in chunks that run alongside decode rows (page 1,
+ *     section 12; page 3, section 2.3).
+ *
+ * Conventions for every entry point
+ *   - Pointers named "device" point to GPU memory (hipMalloc / torch CUDA tensors) that the
+ *     caller owns; the library keeps no reference after the call returns and allocates
+ *     nothing on these paths.  Host scalars are passed by value.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  All work is enqueued
+ *     asynchronously on it; nothing synchronises.
+ *   - The return value is a pa_status.  Argument errors are detected on the host before any
+ *     GPU work is enqueued, so they leave every buffer untouched.  PA_ERR_HIP means a launch
+ *     failed (the HIP error is in pa_last_error()).  Errors raised by earlier asynchronous
+ *     work are not reported here.
+ *   - Device-resident data is the caller's contract and is not validated: block ids in
+ *     [0, num_blocks), context_lens[s] <= max_context_len and
+ *     ceil(context_lens[s] / block_size) <= max_blocks_per_seq, distinct write slots.  The
+ *     kernels still bounds-check every block id and slot they dereference: an out-of-range
+ *     block is treated as holding no valid token and an out-of-range slot is skipped, so bad
+ *     data gives wrong numbers, never an out-of-bounds access.
+ *   - Functions are stateless and may be called from several host threads at once.
+ *
+ * Element types (pa_dtype):  PA_F32 IEEE binary32; PA_BF16 bfloat16; PA_FP8_E4M3 the OCP
+ * 8-bit float E4M3 (bias 7, no infinities, S.1111.111 = NaN, largest finite 448).
+ *
+ * Pool layout.  k_pool and v_pool are each [num_blocks][num_kv_heads][block_size*head_dim]
+ * elements of cache_dtype.  With e = element bytes and W = 64/e, token o of a block and
+ * channel d sit inside their (block, kv head) tile at
+ *     K:  (d / W) * (block_size * W) + o * W + (d % W)
+ *     V:  (d / W) * (block_size * W) + (o / 2) * (2 * W) + (d % W) * 2 + (o % 2)
+ * K is stored as 64-byte channel slices, token-major; V the same with the two tokens of
+ * each even/odd pair interleaved element by element.  One (block, kv head) tile of a 16-token
+ * bf16 block with head_dim 128 is 4 KiB, and one 64-lane 16-byte-per-lane load reads a whole
+ * 1 KiB slice of it.
+ *
+ * Supported shapes: head_dim 64 or 128; block_size 16; num_heads / num_kv_heads in
+ * {1, 2, 4, 8}; (q dtype, cache dtype) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)}.
+ * Anything else returns PA_ERR_UNSUPPORTED.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent sizes          */
+    PA_ERR_UNSUPPORTED = 2, /* valid request outside the support matrix above            */
+    PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the required size       */
+    PA_ERR_HIP = 4          /* a HIP launch failed                                       */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype;
+
+/*
+ * Paged KV append (the step that stores each new token's K and V in its block slot).
+ *   key, value     device, [num_tokens][num_kv_heads][head_dim] of src_dtype, contiguous.
+ *   k_pool, v_pool device, pools of cache_dtype in the layout above, num_blocks blocks.
+ *   slot_mapping   device int64 [num_tokens]; token i goes to physical block
+ *                  slot / block_size at offset slot % block_size.  A negative slot skips the
+ *                  token; a slot >= num_blocks*block_size is also skipped.
+ *   k_scale, v_scale  device fp32 [num_kv_heads] for an FP8_E4M3 cache, else NULL.
+ * src_dtype == cache_dtype copies the bits.  A BF16 or F32 source into an FP8_E4M3 cache
+ * stores e4m3(fl32(x / scale[h])): one binary32 division (round to nearest even), then
+ * round-to-nearest-even to E4M3 saturating at +-448, NaN kept as NaN with its sign.  Only
+ * the addressed slots are written; every other byte of the pools is left unchanged.  Slots
+ * must be distinct within one call.
+ */
+int32_t pa_kv_cache_write(const void* key, const void* value, int32_t src_dtype,
+                          void* k_pool, void* v_pool, int64_t num_blocks, int32_t cache_dtype,
+                          const int64_t* slot_mapping, int32_t num_tokens,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                          const float* k_scale, const float* v_scale, void* stream);
+
+/*
+ * Partition size (context tokens per split-K work item) that the decode path uses when
+ * called with partition_size 0.  A multiple of block_size.
+ */
+int32_t pa_decode_auto_partition_size(int32_t num_seqs, int32_t num_kv_heads,
+                                      int32_t max_context_len, int32_t block_size);
+
+/*
+ * Bytes of device workspace that pa_paged_attention_decode needs for these arguments
+ * (partition_size 0 = auto).  0 when no sequence can span more than one partition.
+ * Returns -1 for arguments the decode call would reject.
+ */
+int64_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                 int32_t partition_size);
+
+/*
+ * PagedAttention decode: one query row per sequence attends over all context_lens[s]
+ * cached positions of its sequence (the token appended this step included).
+ *   out            device [num_seqs][num_heads][head_dim] of q_dtype (written).
+ *   query          device [num_seqs][num_heads][head_dim] of q_dtype.
+ *   k_pool, v_pool device pools (layout above).
+ *   block_tables   device int32 [num_seqs][max_blocks_per_seq]; entries past
+ *                  ceil(context_lens[s] / block_size) are never read.
+ *   context_lens   device int32 [num_seqs]; a sequence with 0 positions gets zeros.
+ *   max_context_len  host bound on context_lens (sizes the launch and the workspace).
+ *   scale          softmax scale applied to q.k (1/sqrt(head_dim) for standard attention).
+ *   k_scale, v_scale device fp32 [num_kv_heads] for an FP8_E4M3 cache (the stored code times
+ *                  the scale is the cached value), else NULL.
+ *   partition_size 0 = auto, else a multiple of block_size: each sequence's context is cut
+ *                  into partitions of this many tokens that are attended independently and
+ *                  merged (split-K).  A value >= max_context_len means no split.
+ *   workspace      device scratch of at least pa_decode_workspace_size(...) bytes (may be
+ *                  NULL when that is 0), 256-byte aligned.  Contents need no initialisation
+ *                  and are undefined afterwards.
+ * query head h reads kv head h / (num_heads / num_kv_heads).
+ */
+int32_t pa_paged_attention_decode(void* out, const void* query, int32_t q_dtype,
+                                  const void* k_pool, const void* v_pool, int64_t num_blocks,
+                                  int32_t cache_dtype, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                  int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  float scale, const float* k_scale, const float* v_scale,
+                                  int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/*
+ * The same decode as two separately enqueued phases, for callers that time or overlap
+ * them: phase 1 runs the per-partition attention (it writes the final rows of sequences
+ * that fit in one partition and the partial results of the others into the workspace);
+ * phase 2 merges the partial results.  Calling phase 1 then phase 2 with identical
+ * arguments on one stream equals pa_paged_attention_decode.  phase 3 runs both.
+ */
+int32_t pa_paged_attention_decode_phase(int32_t phase, void* out, const void* query,
+                                        int32_t q_dtype, const void* k_pool, const void* v_pool,
+                                        int64_t num_blocks, int32_t cache_dtype,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t max_context_len,
+                                        int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size, float scale,
+                                        const float* k_scale, const float* v_scale,
+                                        int32_t partition_size, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/* KV bytes one token occupies over num_layers layers: layers x kv_heads x head_dim x 2 (K and
+ * V) x element bytes (page 1, section 2.1: 131072 for 32 x 8 x 128 bf16).  -1 on bad input. */
+int64_t pa_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t cache_dtype);
+
+/* Bytes of one pool (K or V) of num_blocks blocks.  -1 on bad input. */
+int64_t pa_pool_bytes(int64_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t cache_dtype);
+
+/* Static name of a status code. */
+const char* pa_status_string(int32_t status);
+
+/* Detail of the most recent failing call on this host thread ("" if none). */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

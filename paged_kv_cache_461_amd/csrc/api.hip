@@ -1,0 +1,281 @@
+// api.hip -- C ABI entry points of libpagedattn.so (declared in include/pagedattn.h).
+//
+// Host-side validation, workspace sizing and kernel dispatch.  Every argument check
+// happens before anything is enqueued; the library allocates nothing and keeps no state
+// beyond a per-thread error message.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/pagedattn.h"
+#include "pa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t status, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int32_t ok()
+{
+    g_last_error.clear();
+    return PA_OK;
+}
+
+int elem_bytes(int32_t dt)
+{
+    switch (dt) {
+    case PA_F32: return 4;
+    case PA_BF16: return 2;
+    case PA_FP8_E4M3: return 1;
+    default: return 0;
+    }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kWorkspaceAlign = 256;
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+struct DecodePlan {
+    int32_t partition;
+    int32_t max_partitions;
+    int64_t o_bytes, m_bytes;  // workspace regions (o, then m, then l)
+    int64_t total;
+};
+
+int32_t auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len, int32_t block_size)
+{
+    // 512 tokens (32 blocks, 8 per wave) per work item keeps the merge traffic below 1% of
+    // the KV bytes; shorter contexts run unsplit.
+    const int32_t p = 512;
+    if (max_context_len <= p) return max_context_len > 0 ? (max_context_len + block_size - 1) / block_size * block_size : block_size;
+    (void)num_seqs;
+    (void)num_kv_heads;
+    return p;
+}
+
+DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t max_context_len, int32_t partition_size)
+{
+    DecodePlan pl{};
+    pl.partition = partition_size > 0 ? partition_size
+                                      : auto_partition(num_seqs, num_kv_heads, max_context_len, block_size);
+    pl.max_partitions = max_context_len > 0 ? (max_context_len + pl.partition - 1) / pl.partition : 1;
+    if (pl.max_partitions <= 1) {
+        pl.max_partitions = 1;
+        return pl;  // nothing to merge: no workspace
+    }
+    const int64_t rows = (int64_t)num_seqs * num_heads * pl.max_partitions;
+    pl.o_bytes = align_up(rows * head_dim * 4, kWorkspaceAlign);
+    pl.m_bytes = align_up(rows * 4, kWorkspaceAlign);
+    pl.total = pl.o_bytes + 2 * pl.m_bytes;
+    return pl;
+}
+
+int32_t check_decode_shape(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t max_context_len, int32_t partition_size, int32_t q_dtype,
+                           int32_t cache_dtype)
+{
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        max_context_len < 0 || partition_size < 0)
+        return fail(PA_ERR_INVALID_ARG, "negative or zero size (num_seqs=%d num_heads=%d num_kv_heads=%d "
+                    "head_dim=%d block_size=%d max_context_len=%d partition_size=%d)", num_seqs, num_heads,
+                    num_kv_heads, head_dim, block_size, max_context_len, partition_size);
+    if (num_heads % num_kv_heads)
+        return fail(PA_ERR_INVALID_ARG, "num_heads %d is not a multiple of num_kv_heads %d", num_heads, num_kv_heads);
+    if (!elem_bytes(q_dtype) || !elem_bytes(cache_dtype) || q_dtype == PA_FP8_E4M3)
+        return fail(PA_ERR_INVALID_ARG, "unknown dtype (q %d, cache %d)", q_dtype, cache_dtype);
+    const int32_t g = num_heads / num_kv_heads;
+    if (g != 1 && g != 2 && g != 4 && g != 8)
+        return fail(PA_ERR_UNSUPPORTED, "GQA group %d (supported: 1, 2, 4, 8)", g);
+    if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
+    if (block_size != pa::kBlockSize) return fail(PA_ERR_UNSUPPORTED, "block_size %d (supported: 16)", block_size);
+    const bool combo = (q_dtype == PA_F32 && cache_dtype == PA_F32) || (q_dtype == PA_BF16 && cache_dtype == PA_BF16) ||
+                       (q_dtype == PA_BF16 && cache_dtype == PA_FP8_E4M3);
+    if (!combo) return fail(PA_ERR_UNSUPPORTED, "(q dtype %d, cache dtype %d) not supported", q_dtype, cache_dtype);
+    if (partition_size > 0 && partition_size % block_size)
+        return fail(PA_ERR_INVALID_ARG, "partition_size %d is not a multiple of block_size %d", partition_size, block_size);
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int32_t status)
+{
+    switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int64_t pa_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim, int32_t cache_dtype)
+{
+    const int e = elem_bytes(cache_dtype);
+    if (!e || num_layers < 0 || num_kv_heads < 0 || head_dim < 0) return -1;
+    return (int64_t)num_layers * num_kv_heads * head_dim * 2 * e;
+}
+
+int64_t pa_pool_bytes(int64_t num_blocks, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t cache_dtype)
+{
+    const int e = elem_bytes(cache_dtype);
+    if (!e || num_blocks < 0 || num_kv_heads < 0 || head_dim < 0 || block_size < 0) return -1;
+    return num_blocks * num_kv_heads * (int64_t)block_size * head_dim * e;
+}
+
+int32_t pa_kv_cache_write(const void* key, const void* value, int32_t src_dtype, void* k_pool, void* v_pool,
+                          int64_t num_blocks, int32_t cache_dtype, const int64_t* slot_mapping, int32_t num_tokens,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size, const float* k_scale,
+                          const float* v_scale, void* stream)
+{
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks < 0)
+        return fail(PA_ERR_INVALID_ARG, "negative or zero size (num_tokens=%d num_kv_heads=%d head_dim=%d "
+                    "block_size=%d num_blocks=%lld)", num_tokens, num_kv_heads, head_dim, block_size,
+                    (long long)num_blocks);
+    if (!elem_bytes(src_dtype) || !elem_bytes(cache_dtype) || src_dtype == PA_FP8_E4M3)
+        return fail(PA_ERR_INVALID_ARG, "unknown dtype (src %d, cache %d)", src_dtype, cache_dtype);
+    if (!(src_dtype == cache_dtype || cache_dtype == PA_FP8_E4M3))
+        return fail(PA_ERR_UNSUPPORTED, "append from dtype %d into a dtype %d cache", src_dtype, cache_dtype);
+    if (head_dim % (64 / elem_bytes(cache_dtype)) || head_dim % (16 / elem_bytes(src_dtype)))
+        return fail(PA_ERR_UNSUPPORTED, "head_dim %d is not a whole number of 64-byte cache slices", head_dim);
+    if (block_size % 2) return fail(PA_ERR_UNSUPPORTED, "block_size %d must be even", block_size);
+    if (num_tokens == 0) return ok();
+    if (!key || !value || !k_pool || !v_pool || !slot_mapping)
+        return fail(PA_ERR_INVALID_ARG, "null pointer (key %p value %p k_pool %p v_pool %p slot_mapping %p)", key,
+                    value, k_pool, v_pool, (const void*)slot_mapping);
+    if (!aligned16(key) || !aligned16(value) || !aligned16(k_pool) || !aligned16(v_pool))
+        return fail(PA_ERR_INVALID_ARG, "key, value and pools must be 16-byte aligned");
+    if (cache_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale))
+        return fail(PA_ERR_INVALID_ARG, "an fp8 cache needs k_scale and v_scale");
+    pa::KvWriteArgs a{key, value, k_pool, v_pool, num_blocks, slot_mapping, num_tokens, num_kv_heads, head_dim,
+                      block_size, cache_dtype == PA_FP8_E4M3 ? k_scale : nullptr,
+                      cache_dtype == PA_FP8_E4M3 ? v_scale : nullptr};
+    hipError_t e = pa::launch_kv_write(src_dtype, cache_dtype, a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "kv_cache_write launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int32_t pa_decode_auto_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                                      int32_t block_size)
+{
+    if (block_size <= 0 || max_context_len < 0) return -1;
+    return auto_partition(num_seqs, num_kv_heads, max_context_len, block_size);
+}
+
+int64_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t max_context_len, int32_t partition_size)
+{
+    if (check_decode_shape(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                           partition_size, PA_BF16, PA_BF16) != PA_OK)
+        return -1;
+    return plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len, partition_size)
+        .total;
+}
+
+int32_t pa_paged_attention_decode_phase(int32_t phase, void* out, const void* query, int32_t q_dtype,
+                                        const void* k_pool, const void* v_pool, int64_t num_blocks,
+                                        int32_t cache_dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
+                                        int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t block_size, float scale, const float* k_scale,
+                                        const float* v_scale, int32_t partition_size, void* workspace,
+                                        size_t workspace_bytes, void* stream)
+{
+    if (phase < 1 || phase > 3) return fail(PA_ERR_INVALID_ARG, "phase %d (1, 2 or 3)", phase);
+    int32_t st = check_decode_shape(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                                    partition_size, q_dtype, cache_dtype);
+    if (st != PA_OK) return st;
+    if (num_blocks < 0 || max_blocks_per_seq < 0)
+        return fail(PA_ERR_INVALID_ARG, "num_blocks %lld / max_blocks_per_seq %d negative", (long long)num_blocks,
+                    max_blocks_per_seq);
+    if ((int64_t)max_blocks_per_seq * block_size < max_context_len)
+        return fail(PA_ERR_INVALID_ARG, "max_context_len %d exceeds the table capacity %d x %d", max_context_len,
+                    max_blocks_per_seq, block_size);
+    if (num_seqs == 0) return ok();
+    if (!out || !query || !k_pool || !v_pool || !block_tables || !context_lens)
+        return fail(PA_ERR_INVALID_ARG, "null pointer (out %p query %p k_pool %p v_pool %p block_tables %p "
+                    "context_lens %p)", out, query, k_pool, v_pool, (const void*)block_tables,
+                    (const void*)context_lens);
+    if (!aligned16(query) || !aligned16(k_pool) || !aligned16(v_pool))
+        return fail(PA_ERR_INVALID_ARG, "query and pools must be 16-byte aligned");
+    if (cache_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale))
+        return fail(PA_ERR_INVALID_ARG, "an fp8 cache needs k_scale and v_scale");
+    if (!(scale == scale)) return fail(PA_ERR_INVALID_ARG, "scale is NaN");
+    const DecodePlan pl =
+        plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len, partition_size);
+    if (pl.total > 0) {
+        if (!workspace || (int64_t)workspace_bytes < pl.total)
+            return fail(PA_ERR_WORKSPACE, "workspace %zu bytes at %p, need %lld", workspace_bytes, workspace,
+                        (long long)pl.total);
+        if (reinterpret_cast<uintptr_t>(workspace) % kWorkspaceAlign)
+            return fail(PA_ERR_WORKSPACE, "workspace must be %d-byte aligned", (int)kWorkspaceAlign);
+    }
+    const bool fp8 = cache_dtype == PA_FP8_E4M3;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    pa::DecodeArgs a{};
+    a.out = out;
+    a.query = query;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.num_blocks = num_blocks;
+    a.block_tables = block_tables;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.context_lens = context_lens;
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.k_scale = fp8 ? k_scale : nullptr;
+    a.v_scale = fp8 ? v_scale : nullptr;
+    a.partition_size = pl.partition;
+    a.max_partitions = pl.max_partitions;
+    a.o_part = pl.total ? reinterpret_cast<float*>(ws) : nullptr;
+    a.m_part = pl.total ? reinterpret_cast<float*>(ws + pl.o_bytes) : nullptr;
+    a.l_part = pl.total ? reinterpret_cast<float*>(ws + pl.o_bytes + pl.m_bytes) : nullptr;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (phase & 1) {
+        hipError_t e = pa::launch_decode_partitions(q_dtype, cache_dtype, head_dim, num_heads / num_kv_heads, a, s);
+        if (e != hipSuccess) return fail(PA_ERR_HIP, "decode partition launch: %s", hipGetErrorString(e));
+    }
+    if (phase & 2) {
+        hipError_t e = pa::launch_decode_reduce(q_dtype, head_dim, a, s);
+        if (e != hipSuccess) return fail(PA_ERR_HIP, "decode reduce launch: %s", hipGetErrorString(e));
+    }
+    return ok();
+}
+
+int32_t pa_paged_attention_decode(void* out, const void* query, int32_t q_dtype, const void* k_pool,
+                                  const void* v_pool, int64_t num_blocks, int32_t cache_dtype,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                  int32_t max_context_len, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, float scale, const float* k_scale,
+                                  const float* v_scale, int32_t partition_size, void* workspace,
+                                  size_t workspace_bytes, void* stream)
+{
+    return pa_paged_attention_decode_phase(3, out, query, q_dtype, k_pool, v_pool, num_blocks, cache_dtype,
+                                           block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                                           num_heads, num_kv_heads, head_dim, block_size, scale, k_scale, v_scale,
+                                           partition_size, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

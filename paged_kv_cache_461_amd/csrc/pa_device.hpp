@@ -1,0 +1,124 @@
+// pa_device.hpp -- gfx950 device helpers shared by the paged-KV kernels.
+//
+// Element conversions and cross-lane primitives, written directly against CDNA4
+// instructions through clang builtins: v_dot2c_f32_bf16, DPP row/quad moves, ds_swizzle,
+// v_exp_f32, v_cvt_scalef32_pk_bf16_fp8 (OCP E4M3 -> bf16 pair), v_cvt_pk_fp8_f32
+// (f32 -> OCP E4M3) and the gfx950 f32 -> bf16 pack.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum Dtype : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+
+template <int DT>
+struct DtypeBytes;
+template <>
+struct DtypeBytes<kF32> {
+    static constexpr int value = 4;
+};
+template <>
+struct DtypeBytes<kBF16> {
+    static constexpr int value = 2;
+};
+template <>
+struct DtypeBytes<kFP8> {
+    static constexpr int value = 1;
+};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr uint32_t kBf16OnePair = 0x3F803F80u;  // (1.0, 1.0) as two bf16
+
+__device__ __forceinline__ float as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t as_uint(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// c + a.lo*b.lo + a.hi*b.hi with a, b holding two bf16 each; products and sum in fp32.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Two fp32 -> two bf16 (round to nearest even), lo in bits 0..15.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x)
+{
+    return (uint16_t)(pack_bf16x2(x, 0.0f) & 0xFFFFu);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return as_float(b << 16); }
+
+// Two OCP E4M3 bytes (bits 0..15 if !hi, 16..31 if hi) -> two bf16, exact.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// fp32 -> OCP E4M3 code: round to nearest even, finite overflow saturates to +-448, NaN
+// keeps its sign and becomes S.1111.111.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y)
+{
+    if (__builtin_isnan(y)) return (as_uint(y) >> 24 & 0x80u) | 0x7Fu;
+    float c = __builtin_fminf(__builtin_fmaxf(y, -448.0f), 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
+}
+
+// v_exp_f32: 2^x.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// DPP move inside a row of 16 lanes; lanes whose source is outside the row read 0.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x)
+{
+    return as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_uint(x), CTRL, 0xF, 0xF, true));
+}
+
+constexpr int kDppQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+
+// Sum over the 4 lanes of a quad (every lane gets the sum).
+__device__ __forceinline__ float quad_sum(float x)
+{
+    x += dpp_f32<kDppQuadSwap1>(x);
+    x += dpp_f32<kDppQuadSwap2>(x);
+    return x;
+}
+
+// Value held by lane ^ 4 (within 32-lane halves; ds_swizzle bitmask mode, xor 4).
+__device__ __forceinline__ float swizzle_xor4(float x)
+{
+    return as_float((uint32_t)__builtin_amdgcn_ds_swizzle((int)as_uint(x), 0x101F));
+}
+
+// Maximum over all 64 lanes of a wave (every lane gets it).
+__device__ __forceinline__ float wave_max(float x)
+{
+    x = __builtin_fmaxf(x, dpp_f32<kDppQuadSwap1>(x));
+    x = __builtin_fmaxf(x, dpp_f32<kDppQuadSwap2>(x));
+    x = __builtin_fmaxf(x, dpp_f32<kDppRowRor4>(x));
+    x = __builtin_fmaxf(x, dpp_f32<kDppRowRor8>(x));
+    x = __builtin_fmaxf(x, __shfl_xor(x, 16, 64));
+    x = __builtin_fmaxf(x, __shfl_xor(x, 32, 64));
+    return x;
+}
+
+__device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ uint32_t u4_get(const uint4& v, int i)
+{
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+}  // namespace pa
