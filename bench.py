@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of one paged decode step on one MI355X (gfx950).
+
+A step is the whole hot path over one batch: the paged KV append of every sequence's new
+token (pa_kv_cache_write) followed by PagedAttention decode of every sequence's query row
+over its paged context (pa_paged_attention_decode: the per-partition attention kernel, then
+the split-K merge kernel).  Inputs are seeded synthetic data of the Llama-3-8B-shaped decode
+layer (64 sequences, contexts uniform in [512, 4096], 32 query / 8 KV heads, head dim 128,
+bf16, 16-token blocks, pool = used blocks + 10%); they are resident in HBM before timing.
+Several layers' pools (same block tables, different values) are cycled through so that no
+step finds the previous step's KV in the 256 MB last-level cache.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--layers L] [--partition-size P]
+
+Prints one JSON line.  `value` is algorithmic bytes of the step (KV read + query/output +
+tables + append traffic) over the measured step time, in TB/s; `roofline` reports the decode
+attention kernel alone, timed with HIP events on its stream; `cpu_baseline` times the CPU
+float64 oracle on the same batch (one layer) on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import dataclasses
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged-attn decode achieved HBM TB/s (% of peak) + decode seqs/s per layer"
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="llama3_8b_decode",
+                   choices=["llama3_8b_decode", "long_context", "mixed_continuous_batch"])
+    p.add_argument("--layers", type=int, default=2, help="layer pools cycled through (>= 2)")
+    p.add_argument("--partition-size", type=int, default=0, help="split-K partition (0 = library's choice)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="only run a plain 1 GiB device copy (HBM counter calibration) and exit")
+    return p.parse_args()
+
+
+def copy_probe():
+    """A plain copy of known size: 1 GiB read + 1 GiB written per launch, 10 launches."""
+    import torch
+
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read_per_launch": src.numel() * 4,
+                      "copy_probe_bytes_written_per_launch": dst.numel() * 4, "launches": 10}))
+
+
+def make_batch(name):
+    from paged_kv_cache_461_amd import workloads as W
+
+    return W.WORKLOADS[name]()
+
+
+def source_digest():
+    """Hash of the kernel sources, to tell whether stored counter readings still apply."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_461_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload, digest):
+    """HBM bytes per decode launch from the committed counter runs, if they were taken on
+    the current kernel sources for this workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def fill_pools(batch, layers, dev):
+    """Device K/V pools for each layer (same tables, per-layer values), history written by
+    the library's append; returns the pools and, for layer 0, the raw history chunks'
+    generator arguments (regenerated on demand for the CPU baseline)."""
+    import torch
+
+    from paged_kv_cache_461_amd import ops
+    from paged_kv_cache_461_amd import workloads as W
+
+    tdt = {W.BF16: torch.bfloat16, W.F32: torch.float32, W.FP8_E4M3: torch.uint8}[batch.cache_dtype]
+    sdt = {W.BF16: torch.bfloat16, W.F32: torch.float32}[batch.src_dtype]
+    pools = []
+    for layer in range(layers):
+        lb = dataclasses.replace(batch, layer=layer)
+        kp = torch.zeros(batch.pool_elems, dtype=tdt, device=dev)
+        vp = torch.zeros(batch.pool_elems, dtype=tdt, device=dev)
+        for k, v, slots in lb.history_chunks():
+            kt = torch.from_numpy(k.view(np.int16) if k.dtype == np.uint16 else k).to(dev).view(sdt)
+            vt = torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).to(dev).view(sdt)
+            ops.kv_cache_write(kt, vt, kp, vp, torch.from_numpy(slots).to(dev), num_kv_heads=batch.num_kv_heads,
+                               head_dim=batch.head_dim, block_size=batch.block_size)
+        k, v, slots = lb.new_tokens()
+        new = (torch.from_numpy(k.view(np.int16) if k.dtype == np.uint16 else k).to(dev).view(sdt),
+               torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).to(dev).view(sdt),
+               torch.from_numpy(slots).to(dev))
+        q = lb.query_raw()
+        qt = torch.from_numpy(q.view(np.int16) if q.dtype == np.uint16 else q).to(dev).view(sdt)
+        pools.append((kp, vp, new, qt))
+    torch.cuda.synchronize()
+    return pools
+
+
+def cpu_baseline(batch, min_seconds=1.5):
+    """The CPU float64 oracle on the same step (one layer): append of the new tokens, then
+    decode of every sequence's query row.  Host pool built by the oracle's own append."""
+    import oracle
+
+    kp, vp = batch.empty_pool(poison=False)
+    for k, v, slots in batch.history_chunks():
+        oracle.kv_cache_write(k, v, batch.src_dtype, kp, vp, batch.cache_dtype, slots, batch.num_kv_heads,
+                              batch.head_dim, batch.block_size)
+    k, v, slots = batch.new_tokens()
+    q = batch.query_raw()
+    cores = len(os.sched_getaffinity(0))
+    runs, t0 = 0, time.perf_counter()
+    while runs == 0 or time.perf_counter() - t0 < min_seconds:  # repeat to >= min_seconds of wall time
+        oracle.kv_cache_write(k, v, batch.src_dtype, kp, vp, batch.cache_dtype, slots, batch.num_kv_heads,
+                              batch.head_dim, batch.block_size)
+        oracle.paged_attention(q, batch.q_dtype, kp, vp, batch.cache_dtype, batch.block_tables,
+                               batch.context_lens, batch.num_heads, batch.num_kv_heads, batch.head_dim,
+                               batch.block_size, batch.scale, nthreads=cores)
+        runs += 1
+    dt = (time.perf_counter() - t0) / runs
+    step_bytes = batch.decode_bytes() + batch.write_bytes()
+    return {"value": step_bytes / dt / 1e12, "unit": "TB/s", "cores": cores, "kind": "oracle",
+            "sample": "the whole %s step for one layer (%d appends + %d decode rows x %d heads), %d runs"
+                      % (batch.name, batch.num_rows, batch.num_seqs, batch.num_heads, runs),
+            "seconds_per_step": dt, "seqs_per_s_per_layer": batch.num_seqs / dt}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU: this build has no multi-GPU path (--gpus %d requested); "
+              "sequences and KV heads shard across GPUs with no exchange inside attention, so the "
+              "one-GPU figure is the per-GPU figure." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if args.layers < 1 or args.steps < 1 or args.warmup < 0:
+        sys.exit("--layers and --steps must be >= 1, --warmup >= 0")
+
+    import torch
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    from paged_kv_cache_461_amd import ops
+
+    ops.library()  # fails loudly if the HIP library is missing
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    batch = make_batch(args.workload)
+    S, Hq, Hkv, D, B = batch.num_seqs, batch.num_heads, batch.num_kv_heads, batch.head_dim, batch.block_size
+    print("# workload %s: %d seqs, ctx %d..%d, pool %.1f MB x2 per layer, %d layers" % (
+        batch.name, S, batch.context_lens.min(), batch.context_lens.max(), batch.pool_bytes / 1e6, args.layers),
+        file=sys.stderr, flush=True)
+    t0 = time.time()
+    pools = fill_pools(batch, args.layers, dev)
+    print("# pools filled in %.1f s" % (time.time() - t0), file=sys.stderr, flush=True)
+
+    tables = torch.from_numpy(batch.block_tables).to(dev)
+    ctx = torch.from_numpy(batch.context_lens).to(dev)
+    P = args.partition_size
+    ws = ops.decode_workspace(S, Hq, Hkv, D, batch.max_context_len, B, P, device=dev)
+    outs = [torch.empty_like(p[3]) for p in pools]
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        kp, vp, (nk, nv, nslots), q = pools[i % len(pools)]
+        if ev is not None:
+            ev[0].record(stream)
+        ops.kv_cache_write(nk, nv, kp, vp, nslots, num_kv_heads=Hkv, head_dim=D, block_size=B, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        common = dict(max_context_len=batch.max_context_len, num_kv_heads=Hkv, scale=batch.scale, block_size=B,
+                      partition_size=P, workspace=ws, stream=stream)
+        ops.paged_attention_decode(outs[i % len(pools)], q, kp, vp, tables, ctx, phase=1, **common)
+        if ev is not None:
+            ev[2].record(stream)
+        ops.paged_attention_decode(outs[i % len(pools)], q, kp, vp, tables, ctx, phase=2, **common)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    t_write = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3  # us
+    t_part = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+    t_red = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e3
+
+    step_bytes = batch.decode_bytes() + batch.write_bytes()
+    from paged_kv_cache_461_amd import workloads as W
+
+    out_bytes = batch.num_rows * Hq * D * W.ELEM_BYTES[batch.q_dtype]
+    part_bytes = batch.decode_bytes() - out_bytes  # KV + query + tables + lengths
+    part_us = float(t_part.mean())
+    achieved = part_bytes / (part_us * 1e-6) / 1e9
+    value = step_bytes / (ms_per_step * 1e-3) / 1e12
+    digest = source_digest()
+    traffic = stored_traffic(batch.name, digest)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": batch.name, "num_seqs": S, "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+            "block_size": B, "context_lens": "seeded, %d..%d, sum %d" % (
+                batch.context_lens.min(), batch.context_lens.max(), int(batch.context_lens.sum())),
+            "num_blocks": batch.num_blocks, "layers_cycled": args.layers,
+            "partition_size": ops.decode_auto_partition_size(S, Hkv, batch.max_context_len, B) if P == 0 else P,
+        },
+        "frac_of_hbm_peak": round(value * 1e3 / HBM_PEAK_GBS, 4),
+        "seqs_per_s_per_layer": round(S / (ms_per_step * 1e-3), 1),
+        "step_bytes": int(step_bytes),
+        "kernels_us": {"kv_write": round(float(t_write.mean()), 2), "decode_partition": round(part_us, 2),
+                       "decode_reduce": round(float(t_red.mean()), 2),
+                       "decode_partition_p10_p90": [round(float(np.percentile(t_part, 10)), 2),
+                                                    round(float(np.percentile(t_part, 90)), 2)]},
+        "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": int(part_bytes),
+                     "source_digest": digest},
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(batch)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

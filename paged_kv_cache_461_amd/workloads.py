@@ -39,8 +39,9 @@ FP8_E4M3_MAX = 448.0  # largest finite OCP E4M3 value, used only to size calibra
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bf16 bit patterns (round to nearest, ties to even)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    # uint32 arithmetic cannot wrap for a non-NaN input (the largest is 0xFF800000)
+    r = ((u + (np.uint32(0x7FFF) + ((u >> 16) & np.uint32(1)))) >> 16).astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         r[nan] = ((x.view(np.uint32)[nan] >> 16) | 0x0040).astype(np.uint16)
@@ -196,6 +197,12 @@ class PagedBatch:
     def token_values(self, s: int, t0: int = 0, t1: int | None = None):
         """float32 K and V values of positions [t0, t1) of sequence s, rounded to the source
         dtype, each [n][Hkv][D]."""
+        kv = self._token_f32(s, t0, t1)
+        kv = raw_to_f32(to_raw(kv, self.src_dtype), self.src_dtype)
+        return np.ascontiguousarray(kv[:, 0]), np.ascontiguousarray(kv[:, 1])
+
+    def _token_f32(self, s: int, t0: int, t1: int | None) -> np.ndarray:
+        """Unrounded float32 draws [n][2][Hkv][D] of positions [t0, t1) of sequence s."""
         ctx = int(self.context_lens[s])
         t1 = ctx if t1 is None else t1
         start = self._own_start(s)
@@ -205,14 +212,16 @@ class PagedBatch:
         if t1 > start:
             own = self._own_values(s, ctx - start)
             parts.append(own[max(t0, start) - start:t1 - start])
-        kv = np.concatenate(parts, axis=0) if parts else np.zeros(
+        if len(parts) == 1:
+            return parts[0]
+        return np.concatenate(parts, axis=0) if parts else np.zeros(
             (0, 2, self.num_kv_heads, self.head_dim), np.float32)
-        kv = raw_to_f32(to_raw(kv, self.src_dtype), self.src_dtype)
-        return np.ascontiguousarray(kv[:, 0]), np.ascontiguousarray(kv[:, 1])
 
     def token_raw(self, s: int, t0: int = 0, t1: int | None = None):
-        k, v = self.token_values(s, t0, t1)
-        return to_raw(k, self.src_dtype), to_raw(v, self.src_dtype)
+        """Raw bits of token_values(s, t0, t1) in the source dtype."""
+        kv = self._token_f32(s, t0, t1)
+        return (np.ascontiguousarray(to_raw(kv[:, 0], self.src_dtype)),
+                np.ascontiguousarray(to_raw(kv[:, 1], self.src_dtype)))
 
     def query_values(self) -> np.ndarray:
         rng = np.random.default_rng([self.seed, 103, self.layer])
