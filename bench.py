@@ -257,7 +257,7 @@ def main():
             "block_size": B, "context_lens": "seeded, %d..%d, sum %d" % (
                 batch.context_lens.min(), batch.context_lens.max(), int(batch.context_lens.sum())),
             "num_blocks": batch.num_blocks, "layers_cycled": args.layers,
-            "partition_size": ops.decode_auto_partition_size(S, Hkv, batch.max_context_len, B) if P == 0 else P,
+            "partition_size": "auto (equal chunks per wave)" if P == 0 else P,
         },
         "frac_of_hbm_peak": round(value * 1e3 / HBM_PEAK_GBS, 4),
         "seqs_per_s_per_layer": round(S / (ms_per_step * 1e-3), 1),

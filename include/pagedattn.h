@@ -41,14 +41,15 @@
  * 8-bit float E4M3 (bias 7, no infinities, S.1111.111 = NaN, largest finite 448).
  *
  * Pool layout.  k_pool and v_pool are each [num_blocks][num_kv_heads][block_size*head_dim]
- * elements of cache_dtype.  With e = element bytes and W = 64/e, token o of a block and
- * channel d sit inside their (block, kv head) tile at
+ * elements of cache_dtype.  With e = element bytes, W = 64/e and T = min(16/e, block_size),
+ * token o of a block and channel d sit inside their (block, kv head) tile at
  *     K:  (d / W) * (block_size * W) + o * W + (d % W)
- *     V:  (d / W) * (block_size * W) + (o / 2) * (2 * W) + (d % W) * 2 + (o % 2)
- * K is stored as 64-byte channel slices, token-major; V the same with the two tokens of
- * each even/odd pair interleaved element by element.  One (block, kv head) tile of a 16-token
- * bf16 block with head_dim 128 is 4 KiB, and one 64-lane 16-byte-per-lane load reads a whole
- * 1 KiB slice of it.
+ *     V:  ((o / T) * head_dim + d) * T + (o % T)
+ * K is stored as 64-byte channel slices, token-major; V as groups of T consecutive tokens,
+ * channel-major, so the T tokens of one channel fill one 16-byte piece.  One (block, kv head)
+ * tile of a 16-token bf16 block with head_dim 128 is 4 KiB; one 64-lane 16-byte-per-lane load
+ * reads a whole 1 KiB K slice (16 tokens x 32 channels) or a 1 KiB V piece (8 tokens x 64
+ * channels).
  *
  * Supported shapes: head_dim 64 or 128; block_size 16; num_heads / num_kv_heads in
  * {1, 2, 4, 8}; (q dtype, cache dtype) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)}.
@@ -95,16 +96,10 @@ int32_t pa_kv_cache_write(const void* key, const void* value, int32_t src_dtype,
                           const float* k_scale, const float* v_scale, void* stream);
 
 /*
- * Partition size (context tokens per split-K work item) that the decode path uses when
- * called with partition_size 0.  A multiple of block_size.
- */
-int32_t pa_decode_auto_partition_size(int32_t num_seqs, int32_t num_kv_heads,
-                                      int32_t max_context_len, int32_t block_size);
-
-/*
  * Bytes of device workspace that pa_paged_attention_decode needs for these arguments
- * (partition_size 0 = auto).  0 when no sequence can span more than one partition.
- * Returns -1 for arguments the decode call would reject.
+ * (partition_size 0 = automatic work split).  Depends only on the shapes, never on the
+ * context lengths' values; 0 only for an empty batch.  Returns -1 for arguments the decode
+ * call would reject.
  */
 int64_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size, int32_t max_context_len,
@@ -115,7 +110,7 @@ int64_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t nu
  * cached positions of its sequence (the token appended this step included).
  *   out            device [num_seqs][num_heads][head_dim] of q_dtype (written).
  *   query          device [num_seqs][num_heads][head_dim] of q_dtype.
- *   k_pool, v_pool device pools (layout above).
+ *   k_pool, v_pool device pools (layout above) of num_blocks >= 1 blocks.
  *   block_tables   device int32 [num_seqs][max_blocks_per_seq]; entries past
  *                  ceil(context_lens[s] / block_size) are never read.
  *   context_lens   device int32 [num_seqs]; a sequence with 0 positions gets zeros.
@@ -123,12 +118,16 @@ int64_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t nu
  *   scale          softmax scale applied to q.k (1/sqrt(head_dim) for standard attention).
  *   k_scale, v_scale device fp32 [num_kv_heads] for an FP8_E4M3 cache (the stored code times
  *                  the scale is the cached value), else NULL.
- *   partition_size 0 = auto, else a multiple of block_size: each sequence's context is cut
- *                  into partitions of this many tokens that are attended independently and
- *                  merged (split-K).  A value >= max_context_len means no split.
- *   workspace      device scratch of at least pa_decode_workspace_size(...) bytes (may be
- *                  NULL when that is 0), 256-byte aligned.  Contents need no initialisation
- *                  and are undefined afterwards.
+ *   partition_size 0 = automatic, else a multiple of block_size.  The work is the list of
+ *                  every (sequence, kv head) pair's blocks laid end to end; it is cut into
+ *                  chunks of partition_size / block_size blocks (automatic: equal chunks, one per
+ *                  wave of a grid sized to fill the GPU), each chunk is attended independently
+ *                  per sequence piece, and the pieces of a sequence are merged (split-K).  The
+ *                  result does not depend on the split beyond rounding.
+ *   workspace      device scratch of at least pa_decode_workspace_size(...) bytes, 256-byte
+ *                  aligned.  Contents need no initialisation and are undefined afterwards.
+ *                  Two calls that run concurrently need separate workspaces.
+ * Context lengths above max_context_len are treated as max_context_len.
  * query head h reads kv head h / (num_heads / num_kv_heads).
  */
 int32_t pa_paged_attention_decode(void* out, const void* query, int32_t q_dtype,
@@ -143,9 +142,10 @@ int32_t pa_paged_attention_decode(void* out, const void* query, int32_t q_dtype,
 
 /*
  * The same decode as two separately enqueued phases, for callers that time or overlap
- * them: phase 1 runs the per-partition attention (it writes the final rows of sequences
- * that fit in one partition and the partial results of the others into the workspace);
- * phase 2 merges the partial results.  Calling phase 1 then phase 2 with identical
+ * them: phase 1 runs the attention over the work chunks (it writes the final rows of
+ * sequences that one chunk covers whole and the partial results of the others into the
+ * workspace); phase 2 merges the partial results and writes the zero rows of empty
+ * sequences.  Calling phase 1 then phase 2 with identical
  * arguments on one stream equals pa_paged_attention_decode.  phase 3 runs both.
  */
 int32_t pa_paged_attention_decode_phase(int32_t phase, void* out, const void* query,

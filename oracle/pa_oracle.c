@@ -28,13 +28,14 @@
  * There is no online-softmax trick, no blocking and no reordering.
  *
  * Pool layout (a format both sides must agree on; the pages give none).  Let e be the
- * element size in bytes (4 fp32, 2 bf16, 1 fp8), W = 64 / e, and B the block size.  The
- * K pool and the V pool are each [num_blocks][num_kv_heads][B * D] elements; inside one
- * (block, kv head) tile of B*D elements, token o (0 <= o < B) and channel d are at
+ * element size in bytes (4 fp32, 2 bf16, 1 fp8), W = 64 / e, T = min(16 / e, B) and B the
+ * block size.  The K pool and the V pool are each [num_blocks][num_kv_heads][B * D]
+ * elements; inside one (block, kv head) tile of B*D elements, token o (0 <= o < B) and
+ * channel d are at
  *     K:  (d / W) * (B * W) + o * W + (d % W)
- *     V:  (d / W) * (B * W) + (o / 2) * (2 * W) + (d % W) * 2 + (o % 2)
- * i.e. K is split into 64-byte channel slices stored token-major, and V the same but with
- * the two tokens of each even/odd pair interleaved element by element.
+ *     V:  ((o / T) * D + d) * T + (o % T)
+ * i.e. K is split into 64-byte channel slices stored token-major, and V into groups of T
+ * consecutive tokens stored channel-major, the T tokens of one channel side by side.
  */
 #include <math.h>
 #include <pthread.h>
@@ -79,18 +80,18 @@ int64_t oracle_v_elem_index(int64_t block, int kv_head, int token, int d,
 {
     int e = elem_bytes(dtype);
     if (e == 0) return -1;
-    int64_t W = 64 / e;
+    int64_t T = 16 / e < block_size ? 16 / e : block_size;
     int64_t tile = ((int64_t)block * num_kv_heads + kv_head) * (int64_t)block_size * head_dim;
-    return tile + (d / W) * ((int64_t)block_size * W) + (int64_t)(token / 2) * (2 * W)
-           + (d % W) * 2 + (token % 2);
+    return tile + ((int64_t)(token / T) * head_dim + d) * T + (token % T);
 }
 
-/* The layout needs whole 64-byte channel slices and whole token pairs. */
+/* The layout needs whole 64-byte channel slices (K) and whole token groups (V). */
 static int layout_ok(int head_dim, int block_size, int dtype)
 {
     int e = elem_bytes(dtype);
     if (e == 0 || head_dim <= 0 || block_size <= 0) return 0;
-    return (head_dim % (64 / e)) == 0 && (block_size % 2) == 0;
+    int T = 16 / e < block_size ? 16 / e : block_size;
+    return (head_dim % (64 / e)) == 0 && (block_size % T) == 0;
 }
 
 /* ---- element decoders ------------------------------------------------------------- */

@@ -49,38 +49,45 @@ constexpr int64_t kWorkspaceAlign = 256;
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 struct DecodePlan {
-    int32_t partition;
-    int32_t max_partitions;
-    int64_t o_bytes, m_bytes;  // workspace regions (o, then m, then l)
+    int32_t chunk_blocks;  // 0 = balanced over the grid
+    int32_t grid_workgroups;
+    int64_t max_chunks, max_pieces;
+    int64_t o_bytes, ml_bytes, info_bytes;  // workspace regions, in this order
     int64_t total;
 };
 
-int32_t auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len, int32_t block_size)
+// Work units (16-token blocks of one kv head) of the largest batch these arguments allow.
+int64_t max_units(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size, int32_t max_context_len)
 {
-    // 512 tokens (32 blocks, 8 per wave) per work item keeps the merge traffic below 1% of
-    // the KV bytes; shorter contexts run unsplit.
-    const int32_t p = 512;
-    if (max_context_len <= p) return max_context_len > 0 ? (max_context_len + block_size - 1) / block_size * block_size : block_size;
-    (void)num_seqs;
-    (void)num_kv_heads;
-    return p;
+    return (int64_t)num_seqs * num_kv_heads * ((max_context_len + block_size - 1) / block_size);
 }
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t block_size, int32_t max_context_len, int32_t partition_size)
 {
     DecodePlan pl{};
-    pl.partition = partition_size > 0 ? partition_size
-                                      : auto_partition(num_seqs, num_kv_heads, max_context_len, block_size);
-    pl.max_partitions = max_context_len > 0 ? (max_context_len + pl.partition - 1) / pl.partition : 1;
-    if (pl.max_partitions <= 1) {
-        pl.max_partitions = 1;
-        return pl;  // nothing to merge: no workspace
+    const int64_t umax = max_units(num_seqs, num_kv_heads, block_size, max_context_len);
+    int64_t waves;
+    if (partition_size > 0) {
+        pl.chunk_blocks = partition_size / block_size;
+        pl.max_chunks = (umax + pl.chunk_blocks - 1) / pl.chunk_blocks;
+        waves = pl.max_chunks < pa::kStreamWaves ? pl.max_chunks : pa::kStreamWaves;
+    } else {
+        pl.chunk_blocks = 0;
+        const int64_t need = (umax + pa::kMinChunkBlocks - 1) / pa::kMinChunkBlocks;
+        waves = need < pa::kStreamWaves ? need : pa::kStreamWaves;
     }
-    const int64_t rows = (int64_t)num_seqs * num_heads * pl.max_partitions;
-    pl.o_bytes = align_up(rows * head_dim * 4, kWorkspaceAlign);
-    pl.m_bytes = align_up(rows * 4, kWorkspaceAlign);
-    pl.total = pl.o_bytes + 2 * pl.m_bytes;
+    pl.grid_workgroups = (int32_t)((waves + pa::kDecodeWaves - 1) / pa::kDecodeWaves);
+    // automatic chunks: C >= ceil(U / NW) gives at most NW chunks
+    if (partition_size <= 0) pl.max_chunks = (int64_t)pl.grid_workgroups * pa::kDecodeWaves;
+    if (num_seqs == 0) return pl;
+    const int64_t runs = (int64_t)num_seqs * num_kv_heads;
+    const int64_t gqa = num_heads / num_kv_heads;
+    pl.max_pieces = runs + pl.max_chunks;
+    pl.o_bytes = align_up(pl.max_pieces * gqa * head_dim * 4, kWorkspaceAlign);
+    pl.ml_bytes = align_up(pl.max_pieces * gqa * 2 * 4, kWorkspaceAlign);
+    pl.info_bytes = align_up(runs * 2 * 4, kWorkspaceAlign);
+    pl.total = pl.o_bytes + pl.ml_bytes + pl.info_bytes;
     return pl;
 }
 
@@ -158,7 +165,11 @@ int32_t pa_kv_cache_write(const void* key, const void* value, int32_t src_dtype,
         return fail(PA_ERR_UNSUPPORTED, "append from dtype %d into a dtype %d cache", src_dtype, cache_dtype);
     if (head_dim % (64 / elem_bytes(cache_dtype)) || head_dim % (16 / elem_bytes(src_dtype)))
         return fail(PA_ERR_UNSUPPORTED, "head_dim %d is not a whole number of 64-byte cache slices", head_dim);
-    if (block_size % 2) return fail(PA_ERR_UNSUPPORTED, "block_size %d must be even", block_size);
+    {
+        const int t = 16 / elem_bytes(cache_dtype) < block_size ? 16 / elem_bytes(cache_dtype) : block_size;
+        if (block_size % t)
+            return fail(PA_ERR_UNSUPPORTED, "block_size %d is not a whole number of %d-token V groups", block_size, t);
+    }
     if (num_tokens == 0) return ok();
     if (!key || !value || !k_pool || !v_pool || !slot_mapping)
         return fail(PA_ERR_INVALID_ARG, "null pointer (key %p value %p k_pool %p v_pool %p slot_mapping %p)", key,
@@ -173,13 +184,6 @@ int32_t pa_kv_cache_write(const void* key, const void* value, int32_t src_dtype,
     hipError_t e = pa::launch_kv_write(src_dtype, cache_dtype, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(PA_ERR_HIP, "kv_cache_write launch: %s", hipGetErrorString(e));
     return ok();
-}
-
-int32_t pa_decode_auto_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
-                                      int32_t block_size)
-{
-    if (block_size <= 0 || max_context_len < 0) return -1;
-    return auto_partition(num_seqs, num_kv_heads, max_context_len, block_size);
 }
 
 int64_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -212,6 +216,7 @@ int32_t pa_paged_attention_decode_phase(int32_t phase, void* out, const void* qu
         return fail(PA_ERR_INVALID_ARG, "max_context_len %d exceeds the table capacity %d x %d", max_context_len,
                     max_blocks_per_seq, block_size);
     if (num_seqs == 0) return ok();
+    if (num_blocks < 1) return fail(PA_ERR_INVALID_ARG, "the pool has no blocks (num_blocks %lld)", (long long)num_blocks);
     if (!out || !query || !k_pool || !v_pool || !block_tables || !context_lens)
         return fail(PA_ERR_INVALID_ARG, "null pointer (out %p query %p k_pool %p v_pool %p block_tables %p "
                     "context_lens %p)", out, query, k_pool, v_pool, (const void*)block_tables,
@@ -241,26 +246,23 @@ int32_t pa_paged_attention_decode_phase(int32_t phase, void* out, const void* qu
     a.block_tables = block_tables;
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.context_lens = context_lens;
+    a.max_context_len = max_context_len;
     a.num_seqs = num_seqs;
     a.num_heads = num_heads;
     a.num_kv_heads = num_kv_heads;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.k_scale = fp8 ? k_scale : nullptr;
     a.v_scale = fp8 ? v_scale : nullptr;
-    a.partition_size = pl.partition;
-    a.max_partitions = pl.max_partitions;
-    a.o_part = pl.total ? reinterpret_cast<float*>(ws) : nullptr;
-    a.m_part = pl.total ? reinterpret_cast<float*>(ws + pl.o_bytes) : nullptr;
-    a.l_part = pl.total ? reinterpret_cast<float*>(ws + pl.o_bytes + pl.m_bytes) : nullptr;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (phase & 1) {
-        hipError_t e = pa::launch_decode_partitions(q_dtype, cache_dtype, head_dim, num_heads / num_kv_heads, a, s);
-        if (e != hipSuccess) return fail(PA_ERR_HIP, "decode partition launch: %s", hipGetErrorString(e));
-    }
-    if (phase & 2) {
-        hipError_t e = pa::launch_decode_reduce(q_dtype, head_dim, a, s);
-        if (e != hipSuccess) return fail(PA_ERR_HIP, "decode reduce launch: %s", hipGetErrorString(e));
-    }
+    a.chunk_blocks = pl.chunk_blocks;
+    a.grid_workgroups = pl.grid_workgroups;
+    a.max_chunks = pl.max_chunks;
+    a.max_pieces = pl.max_pieces;
+    a.o_part = reinterpret_cast<float*>(ws);
+    a.ml_part = reinterpret_cast<float*>(ws + pl.o_bytes);
+    a.run_info = reinterpret_cast<int32_t*>(ws + pl.o_bytes + pl.ml_bytes);
+    hipError_t e = pa::launch_decode(phase, q_dtype, cache_dtype, head_dim, num_heads / num_kv_heads, a,
+                                     static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "decode launch (phase %d): %s", phase, hipGetErrorString(e));
     return ok();
 }
 

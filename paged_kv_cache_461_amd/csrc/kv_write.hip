@@ -6,11 +6,10 @@
 //
 // One thread moves one 16-byte piece of one source row (token, kv head, K or V).  A K piece
 // lands contiguously inside one 64-byte channel slice of the tile; a V piece is spread over
-// every other element because the two tokens of a pair are interleaved (layout in
-// include/pagedattn.h), so V is written with element-sized stores that touch only this
-// token's bytes.  Same-dtype append copies bits.  bf16/fp32 -> OCP E4M3 divides by the
-// head's scale in binary32 (round to nearest even) and converts with v_cvt_pk_fp8_f32 after
-// clamping to +-448 (saturation), NaN handled explicitly.
+// its channels' token groups (layout in include/pagedattn.h), so V is written with
+// element-sized stores that touch only this token's bytes.  Same-dtype append copies bits.
+// bf16/fp32 -> OCP E4M3 divides by the head's scale in binary32 (round to nearest even) and
+// converts with v_cvt_pk_fp8_f32 after clamping to +-448 (saturation), NaN handled explicitly.
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
@@ -52,14 +51,16 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const KvWriteArgs a)
     unsigned char* pool = static_cast<unsigned char*>(kv ? a.v_pool : a.k_pool);
 
     uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
+    // V: token group (o / T), channel d, position o % T inside the channel's 16-byte piece
+    const int T = (16 / EC) < B ? (16 / EC) : B;
+    const int64_t vbase = tile + ((int64_t)(o / T) * D + d0) * T + (o % T);
     if constexpr (ST == CT) {
         if (kv == 0) {
             *reinterpret_cast<uint4*>(pool + (slice + (int64_t)o * W + d0 % W) * EC) = raw;
         } else {
-            const int64_t base = slice + (int64_t)(o / 2) * 2 * W + (o % 2);
 #pragma unroll
             for (int i = 0; i < N; i++) {
-                const int64_t e = base + (int64_t)((d0 % W) + i) * 2;
+                const int64_t e = vbase + (int64_t)i * T;
                 if constexpr (EC == 4)
                     reinterpret_cast<uint32_t*>(pool)[e] = words[i];
                 else
@@ -90,9 +91,8 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const KvWriteArgs a)
                 *reinterpret_cast<uint32_t*>(dst) = codes[0] | codes[1] << 8 | codes[2] << 16 | codes[3] << 24;
             }
         } else {
-            const int64_t base = slice + (int64_t)(o / 2) * 2 * W + (o % 2);
 #pragma unroll
-            for (int i = 0; i < N; i++) pool[base + (int64_t)((d0 % W) + i) * 2] = (unsigned char)codes[i];
+            for (int i = 0; i < N; i++) pool[vbase + (int64_t)i * T] = (unsigned char)codes[i];
         }
     }
 }

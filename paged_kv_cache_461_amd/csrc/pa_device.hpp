@@ -30,6 +30,7 @@ struct DtypeBytes<kFP8> {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kBf16OnePair = 0x3F803F80u;  // (1.0, 1.0) as two bf16
 
@@ -100,6 +101,12 @@ __device__ __forceinline__ float quad_sum(float x)
 __device__ __forceinline__ float swizzle_xor4(float x)
 {
     return as_float((uint32_t)__builtin_amdgcn_ds_swizzle((int)as_uint(x), 0x101F));
+}
+
+// Value held by lane ^ 16 (within 32-lane halves; ds_swizzle bitmask mode, xor 16).
+__device__ __forceinline__ float swizzle_xor16(float x)
+{
+    return as_float((uint32_t)__builtin_amdgcn_ds_swizzle((int)as_uint(x), 0x401F));
 }
 
 // Maximum over all 64 lanes of a wave (every lane gets it).

@@ -25,6 +25,10 @@ struct KvWriteArgs {
     const float* v_scale;
 };
 
+// Decode: the streaming kernel (phase 1) and the merge kernel (phase 2).
+constexpr int kStreamWaves = 2048;   // waves of the persistent grid (8 per CU on 256 CUs)
+constexpr int kMinChunkBlocks = 8;   // smallest automatic chunk, in (block, kv head) units
+
 struct DecodeArgs {
     void* out;
     const void* query;
@@ -34,24 +38,27 @@ struct DecodeArgs {
     const int32_t* block_tables;
     int32_t max_blocks_per_seq;
     const int32_t* context_lens;
+    int32_t max_context_len;  // context lengths are clamped to this bound
     int32_t num_seqs;
     int32_t num_heads;
     int32_t num_kv_heads;
     float scale_log2;  // softmax scale times log2(e): scores are kept in base 2
     const float* k_scale;
     const float* v_scale;
-    int32_t partition_size;  // tokens per partition (multiple of kBlockSize)
-    int32_t max_partitions;  // partitions of the longest sequence
-    float* o_part;           // [S][Hq][max_partitions][D]  normalised partial rows
-    float* m_part;           // [S][Hq][max_partitions]     running max (base 2)
-    float* l_part;           // [S][Hq][max_partitions]     softmax denominator
+    int32_t chunk_blocks;     // units per chunk; 0 = ceil(U / waves), at least kMinChunkBlocks
+    int32_t grid_workgroups;  // workgroups of the streaming grid (4 waves each)
+    int64_t max_chunks;       // chunks the workspace has room for
+    int64_t max_pieces;       // pieces the workspace has room for (runs + max_chunks)
+    float* o_part;            // [max_pieces][G][D]  normalised partial rows
+    float* ml_part;           // [max_pieces][G][2]  (running max in base 2, softmax sum)
+    int32_t* run_info;        // [S * Hkv][2]        (first chunk, number of pieces)
 };
 
 hipError_t launch_kv_write(int src_dtype, int cache_dtype, const KvWriteArgs& a, hipStream_t stream);
 
-// Returns hipErrorInvalidValue when no kernel exists for the combination.
-hipError_t launch_decode_partitions(int q_dtype, int cache_dtype, int head_dim, int gqa,
-                                    const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_decode_reduce(int q_dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
+// phase 1 = streaming kernel, 2 = merge kernel, 3 = both.  Returns hipErrorInvalidValue when
+// no kernel exists for the combination.
+hipError_t launch_decode(int phase, int q_dtype, int cache_dtype, int head_dim, int gqa,
+                         const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace pa

@@ -24,7 +24,7 @@ PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = ra
 
 # Every symbol include/pagedattn.h declares.
 EXPORTS = (
-    "pa_kv_cache_write", "pa_decode_auto_partition_size", "pa_decode_workspace_size",
+    "pa_kv_cache_write", "pa_decode_workspace_size",
     "pa_paged_attention_decode", "pa_paged_attention_decode_phase", "pa_kv_bytes_per_token",
     "pa_pool_bytes", "pa_status_string", "pa_last_error",
 )
@@ -49,8 +49,6 @@ def library():
         P, I32, I64, F, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
         lib.pa_kv_cache_write.restype = I32
         lib.pa_kv_cache_write.argtypes = [P, P, I32, P, P, I64, I32, P, I32, I32, I32, I32, P, P, P]
-        lib.pa_decode_auto_partition_size.restype = I32
-        lib.pa_decode_auto_partition_size.argtypes = [I32, I32, I32, I32]
         lib.pa_decode_workspace_size.restype = I64
         lib.pa_decode_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32]
         dec = [P, P, I32, P, P, I64, I32, P, I32, P, I32, I32, I32, I32, I32, I32, F, P, P, I32, P, SZ, P]
@@ -129,10 +127,6 @@ def kv_cache_write(key, value, k_pool, v_pool, slot_mapping, *, num_kv_heads, he
     _check(library().pa_kv_cache_write(_ptr(key), _ptr(value), dtype_code(key), _ptr(k_pool), _ptr(v_pool), nb,
                                        dtype_code(k_pool), _ptr(slot_mapping), T, num_kv_heads, head_dim,
                                        block_size, _ptr(k_scale), _ptr(v_scale), _stream(stream)))
-
-
-def decode_auto_partition_size(num_seqs, num_kv_heads, max_context_len, block_size=16) -> int:
-    return int(library().pa_decode_auto_partition_size(num_seqs, num_kv_heads, max_context_len, block_size))
 
 
 def decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, block_size=16,

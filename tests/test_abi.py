@@ -83,6 +83,7 @@ def _decode(lib, **kw):
     (dict(phase=4), ops.PA_ERR_INVALID_ARG),
     (dict(query=FAKE + 8), ops.PA_ERR_INVALID_ARG),          # misaligned
     (dict(scale=float("nan")), ops.PA_ERR_INVALID_ARG),
+    (dict(num_blocks=0), ops.PA_ERR_INVALID_ARG),            # empty pool
     (dict(ws=None, ws_bytes=0), ops.PA_ERR_WORKSPACE),       # split-K needs workspace
     (dict(ws=FAKE, ws_bytes=1024), ops.PA_ERR_WORKSPACE),
     (dict(ws=FAKE + 16, ws_bytes=1 << 30), ops.PA_ERR_WORKSPACE),  # misaligned workspace
@@ -97,17 +98,28 @@ def test_decode_empty_batch_is_ok_without_launch(lib):
 
 
 def test_workspace_size(lib):
-    # 64 seqs x 32 heads x ceil(4096/512)=8 partitions x (128 + 2) floats, regions 256-aligned
-    n = lib.pa_decode_workspace_size(64, 32, 8, 128, 16, 4096, 512)
-    rows = 64 * 32 * 8
-    assert n == rows * 128 * 4 + 2 * rows * 4
-    assert lib.pa_decode_workspace_size(64, 32, 8, 128, 16, 512, 512) == 0     # one partition
-    assert lib.pa_decode_workspace_size(64, 32, 8, 128, 16, 4096, 4096) == 0   # no split
+    """Workspace = partial rows and (max, sum) for runs + chunks pieces, and 2 ints per run
+    (regions 256-byte aligned); it depends on shapes only."""
+    def expect(S, Hq, Hkv, D, maxctx, P):
+        runs = S * Hkv
+        G = Hq // Hkv
+        units = S * Hkv * ((maxctx + 15) // 16)
+        if P:
+            chunks = -(-units // (P // 16))
+        else:
+            waves = min(2048, -(-units // 8))
+            chunks = -(-waves // 4) * 4
+        pieces = runs + chunks
+        al = lambda x: -(-x // 256) * 256
+        return al(pieces * G * D * 4) + al(pieces * G * 2 * 4) + al(runs * 2 * 4)
+
+    for args in [(64, 32, 8, 128, 4096, 0), (64, 32, 8, 128, 4096, 512), (4, 8, 2, 64, 100, 0),
+                 (3, 32, 8, 128, 2000, 16), (1, 4, 1, 128, 1, 0)]:
+        S, Hq, Hkv, D, maxctx, P = args
+        assert lib.pa_decode_workspace_size(S, Hq, Hkv, D, 16, maxctx, P) == expect(*args), args
+    assert lib.pa_decode_workspace_size(0, 32, 8, 128, 16, 4096, 0) == 0
     assert lib.pa_decode_workspace_size(64, 30, 8, 128, 16, 4096, 512) == -1
-    p = lib.pa_decode_auto_partition_size(64, 8, 4096, 16)
-    assert p > 0 and p % 16 == 0
-    assert lib.pa_decode_workspace_size(64, 32, 8, 128, 16, 4096, 0) == \
-        lib.pa_decode_workspace_size(64, 32, 8, 128, 16, 4096, p)
+    assert lib.pa_decode_workspace_size(64, 32, 8, 128, 16, 4096, 24) == -1   # not a multiple of 16
 
 
 def _write(lib, **kw):
