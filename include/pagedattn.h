@@ -52,7 +52,8 @@
  * channels).
  *
  * Supported shapes: head_dim 64 or 128; block_size 16; num_heads / num_kv_heads in
- * {1, 2, 4, 8}; (q dtype, cache dtype) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)}.
+ * {1, 2, 4, 8}; (q dtype, cache dtype) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)};
+ * up to 16384 sequences per decode call.
  * Anything else returns PA_ERR_UNSUPPORTED.
  */
 #ifndef PAGEDATTN_H

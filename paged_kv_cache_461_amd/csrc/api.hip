@@ -212,6 +212,9 @@ int32_t pa_paged_attention_decode_phase(int32_t phase, void* out, const void* qu
     if (num_blocks < 0 || max_blocks_per_seq < 0)
         return fail(PA_ERR_INVALID_ARG, "num_blocks %lld / max_blocks_per_seq %d negative", (long long)num_blocks,
                     max_blocks_per_seq);
+    if (num_seqs > pa::kMaxDecodeSeqs)
+        return fail(PA_ERR_UNSUPPORTED, "num_seqs %d above %d (context lengths are staged in LDS)", num_seqs,
+                    pa::kMaxDecodeSeqs);
     if ((int64_t)max_blocks_per_seq * block_size < max_context_len)
         return fail(PA_ERR_INVALID_ARG, "max_context_len %d exceeds the table capacity %d x %d", max_context_len,
                     max_blocks_per_seq, block_size);

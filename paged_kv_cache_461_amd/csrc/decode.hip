@@ -20,7 +20,7 @@
 // Inside a wave, per 16-token block (pool layout in include/pagedattn.h) NCH K loads and NCH V
 // loads of 16 bytes per lane each read one contiguous 1 KiB slice:
 //   QK^T: lane l holds channels of token l/4; bf16/fp8 K is multiplied with bf16 query pairs
-//         (staged per wave in LDS) by v_dot2c_f32_bf16 (fp8 first widened exactly to bf16
+//         (held in VGPRs for the piece) by v_dot2c_f32_bf16 (fp8 first widened exactly to bf16
 //         pairs), fp32 K with FMAs; the 4 lanes of a token finish the dot product with two DPP
 //         quad moves.
 //   softmax: online, in base 2.  The running max is wave-uniform and only moved when a score
@@ -42,10 +42,6 @@ namespace pa {
 namespace {
 
 constexpr float kRescaleMargin = 8.0f;  // log2 units: weights are kept <= 2^8
-#ifndef PA_PIPELINE_DEPTH
-#define PA_PIPELINE_DEPTH 3
-#endif
-constexpr int kPipelineDepth = PA_PIPELINE_DEPTH;  // blocks per wave in the register ring
 
 template <int QT, int KT, int D, int G>
 struct Shape {
@@ -73,51 +69,101 @@ struct Acc {
     float m[G];
 };
 
-// Four dwords of this wave's query copy in LDS.
-__device__ __forceinline__ u32x4_t lds_q16(const unsigned char* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+// The lane's query channels for every slice: the 16 (fp8 cache: 32) bytes of each (slice c,
+// head h) that meet this lane's K elements.  Held in VGPRs for the whole piece.
+template <int QT, int KT, int D, int G>
+struct QRegs {
+    using S = Shape<QT, KT, D, G>;
+    static constexpr int NQW = (KT == kFP8) ? 8 : 4;  // dwords per (slice, head)
+    uint32_t w[S::NCH][G][NQW];
+};
 
-// The query copy's LDS offset, made opaque to the compiler once per block: otherwise the
-// loop-invariant query reads are hoisted out of the block loop and the query occupies 64 more
-// VGPRs per lane (half the waves per SIMD).  An empty asm on a scalar register costs nothing
-// and, unlike a volatile access, adds no memory wait that would drain the K/V ring.
+template <int QT, int KT, int D, int G>
+__device__ __forceinline__ void load_q(QRegs<QT, KT, D, G>& q, const unsigned char* qrow, int kp)
+{
+    using S = Shape<QT, KT, D, G>;
+#pragma unroll
+    for (int c = 0; c < S::NCH; c++)
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            const unsigned char* src = qrow + (h * D + c * S::W + kp * S::KE) * S::QB;
+#pragma unroll
+            for (int i = 0; i < QRegs<QT, KT, D, G>::NQW; i += 4) {
+                const uint4 v = load16(src + i * 4);
+                q.w[c][h][i] = v.x;
+                q.w[c][h][i + 1] = v.y;
+                q.w[c][h][i + 2] = v.z;
+                q.w[c][h][i + 3] = v.w;
+            }
+        }
+}
+
+// The query kept in the wave's LDS copy instead: the same dwords are read per slice as
+// they are needed.  The copy's LDS offset is made opaque to the compiler once per block --
+// otherwise the loop-invariant reads are hoisted back into VGPRs -- with an empty asm on a
+// scalar register, which (unlike a volatile access) adds no memory wait that would drain the
+// K/V ring.
+struct QLds {
+    const unsigned char* base;
+    int off;
+};
+
 __device__ __forceinline__ int opaque(int x)
 {
     asm volatile("" : "+s"(x));
     return x;
 }
 
-// Partial dot products of this lane's K channels with the G query rows (query in LDS).
 template <int QT, int KT, int D, int G>
-__device__ __forceinline__ void qk_slice(const unsigned char* q_lds, int kp, int c, const uint4& kv,
-                                         float (&acc)[G])
+__device__ __forceinline__ void q_dwords(const QRegs<QT, KT, D, G>& q, int c, int h, int kp, uint32_t (&qw)[QRegs<QT, KT, D, G>::NQW])
+{
+#pragma unroll
+    for (int i = 0; i < QRegs<QT, KT, D, G>::NQW; i++) qw[i] = q.w[c][h][i];
+    (void)kp;
+}
+
+template <int QT, int KT, int D, int G>
+__device__ __forceinline__ void q_dwords(const QLds& q, int c, int h, int kp, uint32_t (&qw)[QRegs<QT, KT, D, G>::NQW])
 {
     using S = Shape<QT, KT, D, G>;
+    const unsigned char* p = q.base + q.off + (h * D + c * S::W + kp * S::KE) * S::QB;
+#pragma unroll
+    for (int i = 0; i < QRegs<QT, KT, D, G>::NQW; i += 4) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p + i * 4);
+        qw[i] = v.x;
+        qw[i + 1] = v.y;
+        qw[i + 2] = v.z;
+        qw[i + 3] = v.w;
+    }
+}
+
+// Partial dot products of this lane's K channels with the G query rows.
+template <int QT, int KT, int D, int G, class QSrc>
+__device__ __forceinline__ void qk_slice(const QSrc& q, int kp, int c, const uint4& kv, float (&acc)[G])
+{
 #pragma unroll
     for (int h = 0; h < G; h++) {
-        const unsigned char* qp = q_lds + (h * D + c * S::W + kp * S::KE) * S::QB;
+        uint32_t qw[QRegs<QT, KT, D, G>::NQW];
+        q_dwords<QT, KT, D, G>(q, c, h, kp, qw);
         if constexpr (KT == kBF16) {
-            const u32x4_t q = lds_q16(qp);
-            acc[h] = dot2_bf16(kv.x, q.x, acc[h]);
-            acc[h] = dot2_bf16(kv.y, q.y, acc[h]);
-            acc[h] = dot2_bf16(kv.z, q.z, acc[h]);
-            acc[h] = dot2_bf16(kv.w, q.w, acc[h]);
+            acc[h] = dot2_bf16(kv.x, qw[0], acc[h]);
+            acc[h] = dot2_bf16(kv.y, qw[1], acc[h]);
+            acc[h] = dot2_bf16(kv.z, qw[2], acc[h]);
+            acc[h] = dot2_bf16(kv.w, qw[3], acc[h]);
         } else if constexpr (KT == kFP8) {
-            const u32x4_t q0 = lds_q16(qp);
-            const u32x4_t q1 = lds_q16(qp + 16);
-            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<false>(kv.x), q0.x, acc[h]);
-            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<true>(kv.x), q0.y, acc[h]);
-            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<false>(kv.y), q0.z, acc[h]);
-            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<true>(kv.y), q0.w, acc[h]);
-            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<false>(kv.z), q1.x, acc[h]);
-            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<true>(kv.z), q1.y, acc[h]);
-            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<false>(kv.w), q1.z, acc[h]);
-            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<true>(kv.w), q1.w, acc[h]);
+            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<false>(kv.x), qw[0], acc[h]);
+            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<true>(kv.x), qw[1], acc[h]);
+            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<false>(kv.y), qw[2], acc[h]);
+            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<true>(kv.y), qw[3], acc[h]);
+            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<false>(kv.z), qw[4], acc[h]);
+            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<true>(kv.z), qw[5], acc[h]);
+            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<false>(kv.w), qw[6], acc[h]);
+            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<true>(kv.w), qw[7], acc[h]);
         } else {
-            const u32x4_t q = lds_q16(qp);
-            acc[h] = __builtin_fmaf(as_float(kv.x), as_float(q.x), acc[h]);
-            acc[h] = __builtin_fmaf(as_float(kv.y), as_float(q.y), acc[h]);
-            acc[h] = __builtin_fmaf(as_float(kv.z), as_float(q.z), acc[h]);
-            acc[h] = __builtin_fmaf(as_float(kv.w), as_float(q.w), acc[h]);
+            acc[h] = __builtin_fmaf(as_float(kv.x), as_float(qw[0]), acc[h]);
+            acc[h] = __builtin_fmaf(as_float(kv.y), as_float(qw[1]), acc[h]);
+            acc[h] = __builtin_fmaf(as_float(kv.z), as_float(qw[2]), acc[h]);
+            acc[h] = __builtin_fmaf(as_float(kv.w), as_float(qw[3]), acc[h]);
         }
     }
 }
@@ -183,19 +229,18 @@ __device__ __forceinline__ uint4 mask_tail(uint4 v, int c, int n_valid)
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-template <int QT, int KT, int D, int G>
-__device__ __forceinline__ void attend_block(Acc<QT, KT, D, G>& st, const unsigned char* q_lds_base, int q_off,
+template <int QT, int KT, int D, int G, class QSrc>
+__device__ __forceinline__ void attend_block(Acc<QT, KT, D, G>& st, const QSrc& q,
                                              const uint4 (&kb)[Shape<QT, KT, D, G>::NCH],
                                              const uint4 (&vb)[Shape<QT, KT, D, G>::NCH], int n_valid, float c2,
                                              int lane)
 {
     using S = Shape<QT, KT, D, G>;
-    const unsigned char* q_lds = q_lds_base + opaque(q_off);
     float acc[G];
 #pragma unroll
     for (int h = 0; h < G; h++) acc[h] = 0.0f;
 #pragma unroll
-    for (int c = 0; c < S::NCH; c++) qk_slice<QT, KT, D, G>(q_lds, lane & 3, c, kb[c], acc);
+    for (int c = 0; c < S::NCH; c++) qk_slice<QT, KT, D, G>(q, lane & 3, c, kb[c], acc);
 
     const int tok = lane >> 2;  // this lane's token within the block
     float s2[G];
@@ -255,16 +300,14 @@ __device__ __forceinline__ void attend_block(Acc<QT, KT, D, G>& st, const unsign
 // Context length the kernels use for sequence s: clamped to [0, max_context_len], so a
 // length beyond the caller's bound can never send a table read or a workspace write out of
 // range (the caller's contract is context_lens[s] <= max_context_len).
-__device__ __forceinline__ int seq_ctx(const DecodeArgs& a, int s)
+__device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int c)
 {
-    const int c = a.context_lens[s];
     return c < 0 ? 0 : (c > a.max_context_len ? a.max_context_len : c);
 }
 
-__device__ __forceinline__ int seq_blocks(const DecodeArgs& a, int s)
-{
-    return (seq_ctx(a, s) + kBlockSize - 1) / kBlockSize;
-}
+__device__ __forceinline__ int seq_ctx(const DecodeArgs& a, int s) { return clamp_ctx(a, a.context_lens[s]); }
+
+__device__ __forceinline__ int nblocks(int ctx) { return (ctx + kBlockSize - 1) / kBlockSize; }
 
 __device__ __forceinline__ int wave_incl_scan(int x, int lane)
 {
@@ -276,45 +319,53 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane)
     return x;
 }
 
-constexpr int kScanPerLane = 16;  // sequences per lane in one pass over context_lens
+constexpr int kScanPerLane = 16;  // sequences per lane in one pass over the context lengths
 constexpr int kScanWindow = 64 * kScanPerLane;
-
-// Total units U = num_kv_heads * sum_s ceil(ctx_s / B).
-__device__ int64_t total_units(const DecodeArgs& a, int lane)
-{
-    int64_t total = 0;
-    for (int base = 0; base < a.num_seqs; base += kScanWindow) {
-        int part = 0;
-#pragma unroll
-        for (int i = 0; i < kScanPerLane; i++) {
-            // unconditional (clamped) loads: all of them are in flight before the first wait
-            const int s = base + i * 64 + lane;
-            const int n = seq_blocks(a, min(s, a.num_seqs - 1));
-            part += s < a.num_seqs ? n : 0;
-        }
-        total += __builtin_amdgcn_readlane(wave_incl_scan(part, lane), 63);
-    }
-    return total * a.num_kv_heads;
-}
 
 struct Pos {
     int s, g, j;        // run (sequence s, kv head g), block j of the run
     int64_t run_start;  // unit index of the run's block 0
 };
 
-// Position of unit u0 in the work list (s = num_seqs when u0 >= U).
-__device__ Pos locate(const DecodeArgs& a, int64_t u0, int lane)
+// The list's total U and the position of unit chunk_start(U), from the clamped context
+// lengths in LDS.  Lane l holds sequences base + 16 l .. base + 16 l + 15 of each
+// 1024-sequence window.
+struct Plan {
+    int64_t U;
+    Pos p;
+};
+
+template <class ChunkStart>
+__device__ __forceinline__ Plan plan_wave(const DecodeArgs& a, const int* lctx, int lane, ChunkStart chunk_start)
 {
-    const int Hkv = a.num_kv_heads;
-    int64_t before = 0;  // units of the sequences before this window
-    for (int base = 0; base < a.num_seqs; base += kScanWindow) {
+    const int Hkv = a.num_kv_heads, S = a.num_seqs;
+    // total
+    int64_t total = 0;
+    for (int base = 0; base < S; base += kScanWindow) {
+        int part = 0;
+#pragma unroll
+        for (int i = 0; i < kScanPerLane; i++) {
+            const int s = base + lane * kScanPerLane + i;
+            part += s < S ? nblocks(lctx[s]) : 0;
+        }
+        total += __builtin_amdgcn_readlane(wave_incl_scan(part, lane), 63);
+    }
+    Plan pl;
+    pl.U = total * Hkv;
+    const int64_t u0 = chunk_start(pl.U);
+    pl.p.s = S;
+    pl.p.g = pl.p.j = 0;
+    pl.p.run_start = pl.U;
+    if (u0 >= pl.U) return pl;
+    // locate u0
+    int64_t before = 0;
+    for (int base = 0; base < S; base += kScanWindow) {
         int nb[kScanPerLane];
         int part = 0;
 #pragma unroll
         for (int i = 0; i < kScanPerLane; i++) {
-            const int s = base + lane * kScanPerLane + i;  // lane holds consecutive sequences
-            const int n = seq_blocks(a, min(s, a.num_seqs - 1));
-            nb[i] = s < a.num_seqs ? n : 0;
+            const int s = base + lane * kScanPerLane + i;
+            nb[i] = s < S ? nblocks(lctx[s]) : 0;
             part += nb[i];
         }
         const int incl = wave_incl_scan(part, lane);
@@ -328,77 +379,147 @@ __device__ Pos locate(const DecodeArgs& a, int64_t u0, int lane)
                 const int64_t span = (int64_t)n * Hkv;
                 if (u0 < u + span) {
                     const int64_t off = u0 - u;
-                    Pos p;
-                    p.s = base + L * kScanPerLane + i;
-                    p.g = (int)(off / n);
-                    p.j = (int)(off % n);
-                    p.run_start = u + (int64_t)p.g * n;
-                    return p;
+                    pl.p.s = base + L * kScanPerLane + i;
+                    pl.p.g = (int)(off / n);
+                    pl.p.j = (int)(off % n);
+                    pl.p.run_start = u + (int64_t)pl.p.g * n;
+                    return pl;
                 }
                 u += span;
             }
         }
         before += (int64_t)__builtin_amdgcn_readlane(incl, 63) * Hkv;
     }
-    Pos p;
-    p.s = a.num_seqs;
-    p.g = p.j = 0;
-    p.run_start = before;
-    return p;
+    return pl;  // not reached
+}
+
+// A position in the work list that moves block by block: (sequence, kv head, block) with
+// the run's context length.  Sequences with no context are skipped.
+struct Cursor {
+    int s, g, j, ctx, nbs;
+    int64_t run_start;
+};
+
+__device__ __forceinline__ Cursor cursor_at(const Pos& p, const int* lctx)
+{
+    Cursor c;
+    c.s = p.s;
+    c.g = p.g;
+    c.j = p.j;
+    c.ctx = lctx[p.s];
+    c.nbs = nblocks(c.ctx);
+    c.run_start = p.run_start;
+    return c;
+}
+
+__device__ __forceinline__ void cursor_next(Cursor& c, const int* lctx, int num_seqs, int num_kv_heads)
+{
+    if (++c.j < c.nbs) return;
+    c.run_start += c.nbs;
+    c.j = 0;
+    if (++c.g < num_kv_heads) return;
+    c.g = 0;
+    do {
+        ++c.s;
+        c.ctx = c.s < num_seqs ? lctx[c.s] : 0;
+    } while (c.ctx == 0 && c.s < num_seqs);
+    c.nbs = nblocks(c.ctx);
 }
 
 // ---- the streaming kernel ---------------------------------------------------------------
 
-template <int QT, int KT, int D, int G, int NST>
+// Per (cache dtype): where the query lives and how deep the K/V ring is.  Measured on the
+// Llama-3-8B-shaped bf16 batch: query in VGPRs with a 2-deep ring beats query in LDS with a
+// 3-deep ring (118 vs 121 us); an fp32 query does not fit in VGPRs beside the ring.
+template <int KT>
+struct Variant {
+    static constexpr bool kQueryInLds = KT == kF32;
+    static constexpr int kDepth = kQueryInLds ? 3 : 2;
+};
+
+template <int QT, int KT, int D, int G>
 __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(const DecodeArgs a)
 {
     using S = Shape<QT, KT, D, G>;
+    constexpr bool QL = Variant<KT>::kQueryInLds;
+    constexpr int NST = Variant<KT>::kDepth;
     const int lane = threadIdx.x & 63;
     const int wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t NW = (int64_t)gridDim.x * kDecodeWaves;
     const int64_t w = (int64_t)blockIdx.x * kDecodeWaves + wave_in_wg;
-    const int Hkv = a.num_kv_heads;
+    const int Hkv = a.num_kv_heads, NS = a.num_seqs;
 
-    __shared__ __align__(16) unsigned char q_lds_all[kDecodeWaves * S::QBYTES];
-    const int q_off = wave_in_wg * S::QBYTES;
-    unsigned char* q_lds = q_lds_all + q_off;
+    __shared__ __align__(16) unsigned char q_lds[QL ? kDecodeWaves * S::QBYTES : 16];
+    extern __shared__ int lctx[];  // clamped context length of every sequence
 
-    const int64_t U = total_units(a, lane);
-    const int64_t C = a.chunk_blocks > 0 ? a.chunk_blocks : max((U + NW - 1) / NW, (int64_t)kMinChunkBlocks);
+    // All cursor moves read context lengths from LDS, so inside the stream the only global
+    // loads are the ring's K/V loads and one block-table entry per step, a fixed count per
+    // step that keeps every wait on the ring exact.
+    for (int i = threadIdx.x; i < NS; i += kDecodeThreads) lctx[i] = seq_ctx(a, i);
+    __syncthreads();
+
+    // Chunk size: one chunk of ceil(U / NW) units per wave (at least kMinChunkBlocks), or the
+    // caller's chunk size with chunks dealt round-robin to the waves.
+    int64_t C = 0;
+    const Plan pl = plan_wave(a, lctx, lane, [&](int64_t U) {
+        C = a.chunk_blocks > 0 ? (int64_t)a.chunk_blocks : max((U + NW - 1) / NW, (int64_t)kMinChunkBlocks);
+        return w * C;
+    });
+    const int64_t U = pl.U;
     const int64_t nchunks = min((U + C - 1) / C, a.max_chunks);
 
     const unsigned char* kpool = static_cast<const unsigned char*>(a.k_pool) + lane * 16;
     const unsigned char* vpool = static_cast<const unsigned char*>(a.v_pool) + lane * 16;
     const int64_t block_stride = (int64_t)Hkv * S::TILE;
+    const int32_t* tables = a.block_tables;
+    const int mbps = a.max_blocks_per_seq;
 
     for (int64_t k = w; k < nchunks; k += NW) {
-        const int64_t u0 = k * C;
-        const int64_t uend = min(u0 + C, U);
-        Pos p = locate(a, u0, lane);
-        int64_t u = u0;
-        while (u < uend && p.s < a.num_seqs) {
-            // ---- one piece: blocks j0 .. j0+len-1 of run (s, g) ----
-            const int s = p.s, g = p.g, j0 = p.j;
-            const int ctx = seq_ctx(a, s);
-            const int nbs = (ctx + kBlockSize - 1) / kBlockSize;
-            const int len = (int)min((int64_t)(nbs - j0), uend - u);
-            const int64_t run = (int64_t)s * Hkv + g;
-            const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+        const int n = (int)min(C, U - k * C);  // blocks of this chunk (>= 1)
+        const Pos p0 = k == w ? pl.p : plan_wave(a, lctx, lane, [&](int64_t) { return k * C; }).p;
 
-            // the group's query rows into this wave's LDS copy
-            {
-                const unsigned char* qsrc = static_cast<const unsigned char*>(a.query) +
-                                            ((int64_t)s * a.num_heads + (int64_t)g * G) * D * S::QB;
+        // table cursor: the block whose table entry is fetched next (it stops at the chunk's
+        // last block, whose entry then feeds the fill-in loads past the end)
+        Cursor tc = cursor_at(p0, lctx);
+        int tcount = 0;
+        auto fetch_entry = [&](int& e, int& nv, int& g) {
+            e = tables[(int64_t)tc.s * mbps + tc.j];
+            nv = min(kBlockSize, tc.ctx - tc.j * kBlockSize);
+            g = tc.g;
+            if (tcount + 1 < n) {
+                cursor_next(tc, lctx, NS, Hkv);
+                ++tcount;
+            }
+        };
+        // compute cursor: the block attended next, with its piece's bookkeeping
+        Cursor cc = cursor_at(p0, lctx);
+        int piece_j0 = cc.j;
+
+        // entry ring: physical id, valid tokens and kv head of blocks t .. t+NST-1
+        int ent[NST], ent_nv[NST], ent_g[NST];
+#pragma unroll
+        for (int i = 0; i < NST; i++) fetch_entry(ent[i], ent_nv[i], ent_g[i]);
+
+        auto query_row = [&](const Cursor& c) {
+            return static_cast<const unsigned char*>(a.query) + ((int64_t)c.s * a.num_heads + (int64_t)c.g * G) * D * S::QB;
+        };
+        QRegs<QT, KT, D, G> qr;
+        const int q_off = wave_in_wg * S::QBYTES;
+        auto load_query = [&](const Cursor& c) {
+            if constexpr (QL) {
 #pragma unroll
                 for (int off = 0; off < S::QBYTES; off += 1024)
                     if (off + lane * 16 < S::QBYTES)
-                        *reinterpret_cast<uint4*>(q_lds + off + lane * 16) = load16(qsrc + off + lane * 16);
+                        *reinterpret_cast<uint4*>(q_lds + q_off + off + lane * 16) = load16(query_row(c) + off + lane * 16);
+            } else {
+                load_q<QT, KT, D, G>(qr, query_row(c), lane & 3);
             }
-            const float c2 = a.scale_log2 * (KT == kFP8 ? a.k_scale[g] : 1.0f);
-            const unsigned char* kbase = kpool + (int64_t)g * S::TILE;
-            const unsigned char* vbase = vpool + (int64_t)g * S::TILE;
+        };
+        load_query(cc);
+        float c2 = a.scale_log2 * (KT == kFP8 ? a.k_scale[cc.g] : 1.0f);
 
-            Acc<QT, KT, D, G> st;
+        Acc<QT, KT, D, G> st;
+        auto reset = [&]() {
 #pragma unroll
             for (int h = 0; h < G; h++) {
                 st.m[h] = -FLT_MAX;
@@ -406,50 +527,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(const Dec
 #pragma unroll
                 for (int cg = 0; cg < S::CG; cg++) st.o[cg][h] = 0.0f;
             }
+        };
+        reset();
 
-            // Segments of up to 64 blocks: lane i of `entry` holds the physical id of the
-            // segment's block i.  Every ring refill is issued, also past the end of the segment
-            // (then it re-reads the last block, which is in cache, and is never attended), so the
-            // number of loads between a block's issue and its use is fixed and the compiler
-            // waits for exactly that block.
-            for (int sj = 0; sj < len; sj += 64) {
-                const int slen = min(64, len - sj);
-                const int jb = j0 + sj;
-                int entry = table[jb + min(lane, slen - 1)];
-                entry = lane < slen ? entry : -1;
-
-                uint4 kb[NST][S::NCH], vb[NST][S::NCH];
-                int nv[NST];  // valid tokens of the block in each ring slot (0 = unusable block)
-                auto issue = [&](int t, uint4 (&kd)[S::NCH], uint4 (&vd)[S::NCH]) -> int {
-                    t = min(t, slen - 1);
-                    int phys = __builtin_amdgcn_readlane(entry, t);
-                    const bool bad = phys < 0 || (int64_t)phys >= a.num_blocks;
-                    phys = bad ? 0 : phys;
-                    const unsigned char* kp = kbase + (int64_t)phys * block_stride;
-                    const unsigned char* vp = vbase + (int64_t)phys * block_stride;
-#pragma unroll
-                    for (int c = 0; c < S::NCH; c++) kd[c] = load16(kp + c * 1024);
-#pragma unroll
-                    for (int c = 0; c < S::NCH; c++) vd[c] = load16(vp + c * 1024);
-                    return bad ? 0 : min(kBlockSize, ctx - (jb + t) * kBlockSize);
-                };
-
-#pragma unroll
-                for (int i = 0; i < NST - 1; i++) nv[i] = issue(i, kb[i], vb[i]);
-                for (int t0 = 0; t0 < slen; t0 += NST) {
-#pragma unroll
-                    for (int i = 0; i < NST; i++) {
-                        const int nx = (i + NST - 1) % NST;  // the slot freed by the previous step
-                        nv[nx] = issue(t0 + i + NST - 1, kb[nx], vb[nx]);
-                        if (t0 + i < slen)
-                            attend_block<QT, KT, D, G>(st, q_lds_all, q_off, kb[i], vb[i], nv[i], c2, lane);
-                    }
-                }
-            }
-
-            // ---- finish the piece ----
-            // every lane of a token pair's 8 lanes added that pair's weights to l: add the 8
-            // pairs once each (lanes differing in bits 3, 4, 5)
+        // ---- end of a piece: fold the 8 token-pair lane groups of l, then write the row (a
+        // run covered whole) or the partial result ----
+        auto finish_piece = [&]() {
 #pragma unroll
             for (int h = 0; h < G; h++) {
                 float x = st.l[h];
@@ -458,21 +541,22 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(const Dec
                 x += __shfl_xor(x, 32, 64);
                 st.l[h] = x;
             }
-            const bool first = j0 == 0, whole = first && len == nbs;
+            const int64_t run = (int64_t)cc.s * Hkv + cc.g;
+            const bool first = piece_j0 == 0, whole = first && cc.j == cc.nbs - 1;
             if (first && lane == 0) {
                 // every run with blocks is entered at its block 0 by exactly one wave, which
                 // records the chunk range covering it for the merge
-                const int64_t k_last = (p.run_start + nbs - 1) / C;
+                const int64_t k_last = (cc.run_start + cc.nbs - 1) / C;
                 a.run_info[2 * run] = (int32_t)k;
                 a.run_info[2 * run + 1] = (int32_t)(k_last - k + 1);
             }
             const int64_t piece = run + k;
             if (whole) {
-                const float vs = KT == kFP8 ? a.v_scale[g] : 1.0f;
+                const float vs = KT == kFP8 ? a.v_scale[cc.g] : 1.0f;
 #pragma unroll
                 for (int h = 0; h < G; h++) {
                     const float f = st.l[h] > 0.0f ? vs / st.l[h] : 0.0f;
-                    const int64_t row = (int64_t)s * a.num_heads + (int64_t)g * G + h;
+                    const int64_t row = (int64_t)cc.s * a.num_heads + (int64_t)cc.g * G + h;
 #pragma unroll
                     for (int cg = 0; cg < S::CG; cg++) {
                         const float v = st.o[cg][h] * f;
@@ -495,16 +579,48 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(const Dec
                     }
                 }
             }
+        };
 
-            // ---- next run ----
-            u += len;
-            p.run_start = u;
-            p.j = 0;
-            if (++p.g == Hkv) {
-                p.g = 0;
-                do {
-                    ++p.s;
-                } while (p.s < a.num_seqs && seq_ctx(a, p.s) == 0);
+        // ---- the stream: step t issues block t into ring slot t % NST (blocks past the end
+        // re-read the chunk's last block and are never attended), refills the entry ring with
+        // block t + NST, and attends block t - (NST - 1) ----
+        uint4 kb[NST][S::NCH], vb[NST][S::NCH];
+        int kv_nv[NST];
+        for (int t0 = 0; t0 < n + NST - 1; t0 += NST) {
+#pragma unroll
+            for (int i = 0; i < NST; i++) {
+                const int t = t0 + i;
+                {
+                    int phys = ent[i];
+                    const bool bad = phys < 0 || (int64_t)phys >= a.num_blocks;
+                    phys = bad ? 0 : phys;
+                    kv_nv[i] = bad ? 0 : ent_nv[i];
+                    const int64_t off = (int64_t)phys * block_stride + (int64_t)ent_g[i] * S::TILE;
+#pragma unroll
+                    for (int c = 0; c < S::NCH; c++) kb[i][c] = load16(kpool + off + c * 1024);
+#pragma unroll
+                    for (int c = 0; c < S::NCH; c++) vb[i][c] = load16(vpool + off + c * 1024);
+                }
+                fetch_entry(ent[i], ent_nv[i], ent_g[i]);
+
+                const int ta = t - (NST - 1);
+                if (ta >= 0 && ta < n) {
+                    const int j = (i + 1) % NST;  // the slot issued NST-1 steps ago
+                    if (ta > 0 && cc.j == 0) {       // a new run: start its piece
+                        load_query(cc);
+                        c2 = a.scale_log2 * (KT == kFP8 ? a.k_scale[cc.g] : 1.0f);
+                        reset();
+                        piece_j0 = 0;
+                    }
+                    if constexpr (QL) {
+                        const QLds qo{q_lds, opaque(q_off)};
+                        attend_block<QT, KT, D, G>(st, qo, kb[j], vb[j], kv_nv[j], c2, lane);
+                    } else {
+                        attend_block<QT, KT, D, G>(st, qr, kb[j], vb[j], kv_nv[j], c2, lane);
+                    }
+                    if (cc.j == cc.nbs - 1 || ta == n - 1) finish_piece();
+                    if (ta < n - 1) cursor_next(cc, lctx, NS, Hkv);
+                }
             }
         }
     }
@@ -559,8 +675,8 @@ template <int QT, int KT, int D, int G>
 hipError_t launch_phase_t(int phase, const DecodeArgs& a, hipStream_t stream)
 {
     if ((phase & 1) && a.grid_workgroups > 0) {
-        hipLaunchKernelGGL((decode_stream_kernel<QT, KT, D, G, kPipelineDepth>), dim3((unsigned)a.grid_workgroups),
-                           dim3(kDecodeThreads), 0, stream, a);
+        hipLaunchKernelGGL((decode_stream_kernel<QT, KT, D, G>), dim3((unsigned)a.grid_workgroups),
+                           dim3(kDecodeThreads), (size_t)a.num_seqs * sizeof(int), stream, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

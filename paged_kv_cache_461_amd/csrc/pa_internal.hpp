@@ -28,6 +28,7 @@ struct KvWriteArgs {
 // Decode: the streaming kernel (phase 1) and the merge kernel (phase 2).
 constexpr int kStreamWaves = 2048;   // waves of the persistent grid (8 per CU on 256 CUs)
 constexpr int kMinChunkBlocks = 8;   // smallest automatic chunk, in (block, kv head) units
+constexpr int kMaxDecodeSeqs = 16384;  // context lengths of a call are staged in 64 KiB of LDS
 
 struct DecodeArgs {
     void* out;

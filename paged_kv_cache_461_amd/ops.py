@@ -140,7 +140,7 @@ def decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, max_conte
 
 def decode_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, block_size=16,
                      partition_size=0, device="cuda"):
-    """A workspace tensor of the required size (None when none is needed)."""
+    """A workspace tensor of the required size (None for an empty batch)."""
     n = decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, block_size,
                               partition_size)
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None

@@ -84,6 +84,7 @@ def _decode(lib, **kw):
     (dict(query=FAKE + 8), ops.PA_ERR_INVALID_ARG),          # misaligned
     (dict(scale=float("nan")), ops.PA_ERR_INVALID_ARG),
     (dict(num_blocks=0), ops.PA_ERR_INVALID_ARG),            # empty pool
+    (dict(S=16385), ops.PA_ERR_UNSUPPORTED),                 # more sequences than LDS holds
     (dict(ws=None, ws_bytes=0), ops.PA_ERR_WORKSPACE),       # split-K needs workspace
     (dict(ws=FAKE, ws_bytes=1024), ops.PA_ERR_WORKSPACE),
     (dict(ws=FAKE + 16, ws_bytes=1 << 30), ops.PA_ERR_WORKSPACE),  # misaligned workspace
