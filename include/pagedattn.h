@@ -169,6 +169,19 @@ int64_t pa_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t 
 int64_t pa_pool_bytes(int64_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
                       int32_t block_size, int32_t cache_dtype);
 
+/*
+ * Measurement helper (not part of the attention path): read num_reads 4 KiB tiles of buf, tile
+ * order[i] for i = 0 .. num_reads-1, with grid_workgroups x 256 threads (two tiles per wave and
+ * iteration, 16-byte loads, each wave load one contiguous 1 KiB).  Timing it with a random
+ * order gives the HBM read bandwidth this GPU delivers for the scattered 4 KiB (block, kv head)
+ * tiles of a paged pool, the practical ceiling the decode kernel is compared with.
+ *   buf    device, buf_bytes bytes (16-byte aligned; whole tiles are used).
+ *   order  device int32 [num_reads]; an entry outside [0, buf_bytes / 4096) reads tile 0.
+ *   sink   device, at least 4 * grid_workgroups bytes; written only in a case that does not occur.
+ */
+int32_t pa_probe_tile_read(const void* buf, int64_t buf_bytes, const int32_t* order, int64_t num_reads,
+                           int32_t grid_workgroups, void* sink, void* stream);
+
 /* Static name of a status code. */
 const char* pa_status_string(int32_t status);
 

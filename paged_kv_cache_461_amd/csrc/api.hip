@@ -283,4 +283,19 @@ int32_t pa_paged_attention_decode(void* out, const void* query, int32_t q_dtype,
                                            partition_size, workspace, workspace_bytes, stream);
 }
 
+int32_t pa_probe_tile_read(const void* buf, int64_t buf_bytes, const int32_t* order, int64_t num_reads,
+                           int32_t grid_workgroups, void* sink, void* stream)
+{
+    if (!buf || !order || !sink) return fail(PA_ERR_INVALID_ARG, "null pointer");
+    if (!aligned16(buf)) return fail(PA_ERR_INVALID_ARG, "buf must be 16-byte aligned");
+    if (buf_bytes < 4096 || num_reads < 0 || grid_workgroups < 1 || grid_workgroups > 65535)
+        return fail(PA_ERR_INVALID_ARG, "buf_bytes %lld, num_reads %lld, grid %d", (long long)buf_bytes,
+                    (long long)num_reads, grid_workgroups);
+    if (num_reads == 0) return ok();
+    hipError_t e = pa::launch_tile_read(buf, buf_bytes / 4096, num_reads, order, grid_workgroups,
+                                        static_cast<uint32_t*>(sink), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "probe launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

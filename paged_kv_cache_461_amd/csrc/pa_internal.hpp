@@ -62,4 +62,8 @@ hipError_t launch_kv_write(int src_dtype, int cache_dtype, const KvWriteArgs& a,
 hipError_t launch_decode(int phase, int q_dtype, int cache_dtype, int head_dim, int gqa,
                          const DecodeArgs& a, hipStream_t stream);
 
+// Measurement helper: num_reads 4 KiB tiles of buf in the order given, grid x 256 threads.
+hipError_t launch_tile_read(const void* buf, int64_t buf_tiles, int64_t num_reads, const int32_t* order, int grid,
+                            uint32_t* sink, hipStream_t stream);
+
 }  // namespace pa

@@ -26,7 +26,7 @@ PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = ra
 EXPORTS = (
     "pa_kv_cache_write", "pa_decode_workspace_size",
     "pa_paged_attention_decode", "pa_paged_attention_decode_phase", "pa_kv_bytes_per_token",
-    "pa_pool_bytes", "pa_status_string", "pa_last_error",
+    "pa_pool_bytes", "pa_probe_tile_read", "pa_status_string", "pa_last_error",
 )
 
 
@@ -60,6 +60,8 @@ def library():
         lib.pa_kv_bytes_per_token.argtypes = [I32, I32, I32, I32]
         lib.pa_pool_bytes.restype = I64
         lib.pa_pool_bytes.argtypes = [I64, I32, I32, I32, I32]
+        lib.pa_probe_tile_read.restype = I32
+        lib.pa_probe_tile_read.argtypes = [P, I64, P, I64, I32, P, P]
         lib.pa_status_string.restype = ctypes.c_char_p
         lib.pa_status_string.argtypes = [I32]
         lib.pa_last_error.restype = ctypes.c_char_p
@@ -179,3 +181,12 @@ def kv_bytes_per_token(num_layers, num_kv_heads, head_dim, cache_dtype) -> int:
 
 def pool_bytes(num_blocks, num_kv_heads, head_dim, block_size, cache_dtype) -> int:
     return int(library().pa_pool_bytes(num_blocks, num_kv_heads, head_dim, block_size, cache_dtype))
+
+
+def probe_tile_read(buf, order, sink, grid_workgroups=2048, stream=None):
+    """Read order.numel() 4 KiB tiles of buf in the given order (pa_probe_tile_read)."""
+    _dev("buf", buf)
+    _dev("order", order, torch.int32)
+    _dev("sink", sink)
+    _check(library().pa_probe_tile_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(order), order.numel(),
+                                        int(grid_workgroups), _ptr(sink), _stream(stream)))
