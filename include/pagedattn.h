@@ -53,7 +53,7 @@
  *
  * Supported shapes: head_dim 64 or 128; block_size 16; num_heads / num_kv_heads in
  * {1, 2, 4, 8}; (q dtype, cache dtype) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)};
- * up to 16384 sequences per decode call.
+ * up to 16384 sequences per decode call; chunked prefill with BF16 queries only.
  * Anything else returns PA_ERR_UNSUPPORTED.
  */
 #ifndef PAGEDATTN_H
@@ -159,6 +159,55 @@ int32_t pa_paged_attention_decode_phase(int32_t phase, void* out, const void* qu
                                         const float* k_scale, const float* v_scale,
                                         int32_t partition_size, void* workspace,
                                         size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace that pa_paged_attention_chunked_prefill needs for these arguments
+ * (0 when the keys are not split; partition_size as there).  Depends only on the shapes.
+ * Returns -1 for shapes the prefill call would reject.
+ */
+int64_t pa_chunked_prefill_workspace_size(int32_t num_query_rows, int32_t num_seqs, int32_t max_query_len,
+                                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t block_size, int32_t max_context_len,
+                                          int32_t partition_size);
+
+/*
+ * Chunked-prefill PagedAttention (page 1, section 12: a long prompt is processed as chunks
+ * scheduled alongside decode rows; page 3, section 2.3).  Sequence s contributes
+ * q_len = cu_query_lens[s+1] - cu_query_lens[s] query rows, rows cu_query_lens[s] .. +q_len-1
+ * of query/out; they are the LAST q_len positions of its context_lens[s] cached positions
+ * (their K and V are already in the cache), so row i sits at position
+ * p = context_lens[s] - q_len + i and attends causally to positions 0..p.  A sequence with
+ * q_len 1 is a decode row; q_len 0 contributes nothing.  A row whose position would be
+ * negative (q_len > context_lens[s]) gets zeros.
+ *   out            device [num_query_rows][num_heads][head_dim] bf16 (written).
+ *   query          device [num_query_rows][num_heads][head_dim] bf16.
+ *   q_dtype        PA_BF16 (the products run on bf16 matrix cores with fp32 accumulation; an
+ *                  fp8 cache is widened to bf16 exactly).  Other types: PA_ERR_UNSUPPORTED.
+ *   cu_query_lens  device int32 [num_seqs + 1], non-decreasing, cu_query_lens[0] = 0 and
+ *                  cu_query_lens[num_seqs] = num_query_rows.  A sequence whose rows fall
+ *                  outside [0, num_query_rows) is skipped.
+ *   max_query_len  host bound on q_len (sizes the launch).
+ *   k_pool .. v_scale, scale  as for pa_paged_attention_decode.
+ *   partition_size 0 = automatic, else a multiple of block_size: the visible keys of each group
+ *                  of rows are cut into ranges of partition_size keys that run on separate
+ *                  workgroups and are merged (split-K).  Automatic splits only when the rows
+ *                  alone do not fill the GPU.
+ *   workspace      device scratch of pa_chunked_prefill_workspace_size(...) bytes, 256-byte
+ *                  aligned (NULL when that size is 0).  Contents need no initialisation.
+ * Rows not owned by any sequence are left unchanged when the keys are not split and are
+ * undefined otherwise.
+ */
+int32_t pa_paged_attention_chunked_prefill(void* out, const void* query, int32_t q_dtype,
+                                           const int32_t* cu_query_lens, int32_t num_query_rows,
+                                           int32_t max_query_len, const void* k_pool, const void* v_pool,
+                                           int64_t num_blocks, int32_t cache_dtype,
+                                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                           const int32_t* context_lens, int32_t max_context_len,
+                                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size, float scale,
+                                           const float* k_scale, const float* v_scale,
+                                           int32_t partition_size, void* workspace,
+                                           size_t workspace_bytes, void* stream);
 
 /* KV bytes one token occupies over num_layers layers: layers x kv_heads x head_dim x 2 (K and
  * V) x element bytes (page 1, section 2.1: 131072 for 32 x 8 x 128 bf16).  -1 on bad input. */

@@ -117,6 +117,66 @@ int32_t check_decode_shape(int32_t num_seqs, int32_t num_heads, int32_t num_kv_h
     return PA_OK;
 }
 
+struct PrefillPlan {
+    int32_t row_blocks, num_splits, split_keys;
+    int64_t grid;
+    int64_t o_bytes, ml_bytes;  // workspace regions, in this order
+    int64_t total;
+};
+
+// Workgroups the prefill grid should reach before splitting keys: 2 per CU of 256 CUs.
+constexpr int64_t kPrefillTargetWorkgroups = 512;
+// Automatic splits keep at least this many keys per split.
+constexpr int32_t kPrefillMinSplitKeys = 256;
+
+PrefillPlan plan_prefill(int32_t num_query_rows, int32_t num_seqs, int32_t max_query_len, int32_t num_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len, int32_t partition_size)
+{
+    PrefillPlan pl{};
+    const int32_t gqa = num_heads / num_kv_heads;
+    const int32_t rows_per_wg = pa::kPrefillThreads / 64 * pa::kPrefillRowTiles * 16;
+    pl.row_blocks = (int32_t)(((int64_t)max_query_len * gqa + rows_per_wg - 1) / rows_per_wg);
+    const int64_t base = (int64_t)num_seqs * num_kv_heads * pl.row_blocks;
+    if (partition_size > 0) {
+        pl.split_keys = partition_size;
+        pl.num_splits = max_context_len > 0 ? (max_context_len + partition_size - 1) / partition_size : 1;
+    } else {
+        pl.split_keys = 0;
+        int64_t ns = base > 0 ? (kPrefillTargetWorkgroups + base - 1) / base : 1;
+        const int64_t cap = max_context_len / kPrefillMinSplitKeys;
+        if (ns > cap) ns = cap;
+        pl.num_splits = ns < 1 ? 1 : (int32_t)ns;
+    }
+    pl.grid = base * pl.num_splits;
+    if (pl.num_splits > 1 && num_query_rows > 0) {
+        const int64_t rh = (int64_t)num_query_rows * num_heads;
+        pl.o_bytes = align_up(pl.num_splits * rh * head_dim * 4, kWorkspaceAlign);
+        pl.ml_bytes = align_up(pl.num_splits * rh * 2 * 4, kWorkspaceAlign);
+    }
+    pl.total = pl.o_bytes + pl.ml_bytes;
+    return pl;
+}
+
+int32_t check_prefill_shape(int32_t num_query_rows, int32_t num_seqs, int32_t max_query_len, int32_t num_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                            int32_t partition_size, int32_t q_dtype, int32_t cache_dtype)
+{
+    int32_t st = check_decode_shape(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                                    partition_size, q_dtype, cache_dtype);
+    if (st != PA_OK) return st;
+    if (num_query_rows < 0 || max_query_len < 0)
+        return fail(PA_ERR_INVALID_ARG, "num_query_rows %d / max_query_len %d negative", num_query_rows,
+                    max_query_len);
+    if (num_query_rows > 0 && max_query_len < 1)
+        return fail(PA_ERR_INVALID_ARG, "max_query_len %d with %d query rows", max_query_len, num_query_rows);
+    if (max_query_len > num_query_rows)
+        return fail(PA_ERR_INVALID_ARG, "max_query_len %d exceeds num_query_rows %d", max_query_len, num_query_rows);
+    if (q_dtype != PA_BF16)
+        return fail(PA_ERR_UNSUPPORTED, "chunked prefill runs on bf16 matrix cores: q dtype must be BF16 (got %d)",
+                    q_dtype);
+    return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -281,6 +341,91 @@ int32_t pa_paged_attention_decode(void* out, const void* query, int32_t q_dtype,
                                            block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
                                            num_heads, num_kv_heads, head_dim, block_size, scale, k_scale, v_scale,
                                            partition_size, workspace, workspace_bytes, stream);
+}
+
+int64_t pa_chunked_prefill_workspace_size(int32_t num_query_rows, int32_t num_seqs, int32_t max_query_len,
+                                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t block_size, int32_t max_context_len, int32_t partition_size)
+{
+    if (check_prefill_shape(num_query_rows, num_seqs, max_query_len, num_heads, num_kv_heads, head_dim, block_size,
+                            max_context_len, partition_size, PA_BF16, PA_BF16) != PA_OK)
+        return -1;
+    return plan_prefill(num_query_rows, num_seqs, max_query_len, num_heads, num_kv_heads, head_dim, max_context_len,
+                        partition_size)
+        .total;
+}
+
+int32_t pa_paged_attention_chunked_prefill(void* out, const void* query, int32_t q_dtype,
+                                           const int32_t* cu_query_lens, int32_t num_query_rows,
+                                           int32_t max_query_len, const void* k_pool, const void* v_pool,
+                                           int64_t num_blocks, int32_t cache_dtype, const int32_t* block_tables,
+                                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                           int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+                                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                                           const float* k_scale, const float* v_scale, int32_t partition_size,
+                                           void* workspace, size_t workspace_bytes, void* stream)
+{
+    int32_t st = check_prefill_shape(num_query_rows, num_seqs, max_query_len, num_heads, num_kv_heads, head_dim,
+                                     block_size, max_context_len, partition_size, q_dtype, cache_dtype);
+    if (st != PA_OK) return st;
+    if (num_blocks < 0 || max_blocks_per_seq < 0)
+        return fail(PA_ERR_INVALID_ARG, "num_blocks %lld / max_blocks_per_seq %d negative", (long long)num_blocks,
+                    max_blocks_per_seq);
+    if ((int64_t)max_blocks_per_seq * block_size < max_context_len)
+        return fail(PA_ERR_INVALID_ARG, "max_context_len %d exceeds the table capacity %d x %d", max_context_len,
+                    max_blocks_per_seq, block_size);
+    if (num_seqs == 0 || num_query_rows == 0) return ok();
+    if (num_blocks < 1) return fail(PA_ERR_INVALID_ARG, "the pool has no blocks (num_blocks %lld)", (long long)num_blocks);
+    if (!out || !query || !cu_query_lens || !k_pool || !v_pool || !block_tables || !context_lens)
+        return fail(PA_ERR_INVALID_ARG, "null pointer (out %p query %p cu_query_lens %p k_pool %p v_pool %p "
+                    "block_tables %p context_lens %p)", out, query, (const void*)cu_query_lens, k_pool, v_pool,
+                    (const void*)block_tables, (const void*)context_lens);
+    if (!aligned16(query) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool))
+        return fail(PA_ERR_INVALID_ARG, "query, out and pools must be 16-byte aligned");
+    if (cache_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale))
+        return fail(PA_ERR_INVALID_ARG, "an fp8 cache needs k_scale and v_scale");
+    if (!(scale == scale)) return fail(PA_ERR_INVALID_ARG, "scale is NaN");
+    const PrefillPlan pl = plan_prefill(num_query_rows, num_seqs, max_query_len, num_heads, num_kv_heads, head_dim,
+                                        max_context_len, partition_size);
+    if (pl.grid > 0x7FFFFFFF)
+        return fail(PA_ERR_UNSUPPORTED, "prefill grid of %lld workgroups", (long long)pl.grid);
+    if (pl.total > 0) {
+        if (!workspace || (int64_t)workspace_bytes < pl.total)
+            return fail(PA_ERR_WORKSPACE, "workspace %zu bytes at %p, need %lld", workspace_bytes, workspace,
+                        (long long)pl.total);
+        if (reinterpret_cast<uintptr_t>(workspace) % kWorkspaceAlign)
+            return fail(PA_ERR_WORKSPACE, "workspace must be %d-byte aligned", (int)kWorkspaceAlign);
+    }
+    if (pl.grid == 0) return ok();
+    const bool fp8 = cache_dtype == PA_FP8_E4M3;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    pa::PrefillArgs a{};
+    a.out = out;
+    a.query = query;
+    a.cu_query_lens = cu_query_lens;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.num_blocks = num_blocks;
+    a.block_tables = block_tables;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.context_lens = context_lens;
+    a.max_context_len = max_context_len;
+    a.num_seqs = num_seqs;
+    a.num_query_rows = num_query_rows;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.row_blocks = pl.row_blocks;
+    a.num_splits = pl.num_splits;
+    a.split_keys = pl.split_keys;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.k_scale = fp8 ? k_scale : nullptr;
+    a.v_scale = fp8 ? v_scale : nullptr;
+    a.o_part = pl.total > 0 ? reinterpret_cast<float*>(ws) : nullptr;
+    a.ml_part = pl.total > 0 ? reinterpret_cast<float*>(ws + pl.o_bytes) : nullptr;
+    hipError_t e = pa::launch_prefill(cache_dtype, head_dim, num_heads / num_kv_heads, a, pl.grid,
+                                      static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "chunked prefill launch: %s", hipGetErrorString(e));
+    return ok();
 }
 
 int32_t pa_probe_tile_read(const void* buf, int64_t buf_bytes, const int32_t* order, int64_t num_reads,

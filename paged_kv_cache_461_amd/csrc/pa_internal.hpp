@@ -55,12 +55,45 @@ struct DecodeArgs {
     int32_t* run_info;        // [S * Hkv][2]        (first chunk, number of pieces)
 };
 
+// Chunked prefill: MFMA attention kernel (+ merge kernel when the keys are split).
+constexpr int kPrefillThreads = 256;  // 4 waves per workgroup
+constexpr int kPrefillRowTiles = 2;   // 16-row MFMA tiles per wave: 128 stacked rows per workgroup
+
+struct PrefillArgs {
+    void* out;                     // [num_query_rows][Hq][D], bf16
+    const void* query;             // [num_query_rows][Hq][D], bf16
+    const int32_t* cu_query_lens;  // [num_seqs + 1]
+    const void* k_pool;
+    const void* v_pool;
+    int64_t num_blocks;
+    const int32_t* block_tables;
+    int32_t max_blocks_per_seq;
+    const int32_t* context_lens;
+    int32_t max_context_len;  // context lengths are clamped to this bound
+    int32_t num_seqs;
+    int32_t num_query_rows;
+    int32_t num_heads;
+    int32_t num_kv_heads;
+    int32_t row_blocks;  // workgroup row blocks per (sequence, kv head)
+    int32_t num_splits;  // key ranges per row block
+    int32_t split_keys;  // keys per range; 0 = each row block's keys cut into num_splits parts
+    float scale_log2;
+    const float* k_scale;
+    const float* v_scale;
+    float* o_part;   // [num_splits][num_query_rows][Hq][D]  unnormalised rows times v_scale
+    float* ml_part;  // [num_splits][num_query_rows][Hq][2]  (running max in base 2, softmax sum)
+};
+
 hipError_t launch_kv_write(int src_dtype, int cache_dtype, const KvWriteArgs& a, hipStream_t stream);
 
 // phase 1 = streaming kernel, 2 = merge kernel, 3 = both.  Returns hipErrorInvalidValue when
 // no kernel exists for the combination.
 hipError_t launch_decode(int phase, int q_dtype, int cache_dtype, int head_dim, int gqa,
                          const DecodeArgs& a, hipStream_t stream);
+
+// grid = num_seqs * num_kv_heads * row_blocks * num_splits workgroups.
+hipError_t launch_prefill(int cache_dtype, int head_dim, int gqa, const PrefillArgs& a, int64_t grid,
+                          hipStream_t stream);
 
 // Measurement helper: num_reads 4 KiB tiles of buf in the order given, grid x 256 threads.
 hipError_t launch_tile_read(const void* buf, int64_t buf_tiles, int64_t num_reads, const int32_t* order, int grid,

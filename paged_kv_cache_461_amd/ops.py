@@ -27,6 +27,7 @@ EXPORTS = (
     "pa_kv_cache_write", "pa_decode_workspace_size",
     "pa_paged_attention_decode", "pa_paged_attention_decode_phase", "pa_kv_bytes_per_token",
     "pa_pool_bytes", "pa_probe_tile_read", "pa_status_string", "pa_last_error",
+    "pa_chunked_prefill_workspace_size", "pa_paged_attention_chunked_prefill",
 )
 
 
@@ -56,6 +57,11 @@ def library():
         lib.pa_paged_attention_decode.argtypes = dec
         lib.pa_paged_attention_decode_phase.restype = I32
         lib.pa_paged_attention_decode_phase.argtypes = [I32] + dec
+        lib.pa_chunked_prefill_workspace_size.restype = I64
+        lib.pa_chunked_prefill_workspace_size.argtypes = [I32] * 9
+        lib.pa_paged_attention_chunked_prefill.restype = I32
+        lib.pa_paged_attention_chunked_prefill.argtypes = [P, P, I32, P, I32, I32, P, P, I64, I32, P, I32, P, I32, I32,
+                                                           I32, I32, I32, I32, F, P, P, I32, P, SZ, P]
         lib.pa_kv_bytes_per_token.restype = I64
         lib.pa_kv_bytes_per_token.argtypes = [I32, I32, I32, I32]
         lib.pa_pool_bytes.restype = I64
@@ -172,6 +178,54 @@ def paged_attention_decode(out, query, k_pool, v_pool, block_tables, context_len
         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), int(max_context_len), S, Hq, num_kv_heads, D,
         block_size, float(scale), _ptr(k_scale), _ptr(v_scale), int(partition_size), _ptr(workspace), ws_bytes,
         _stream(stream)))
+    return out
+
+
+def chunked_prefill_workspace_size(num_query_rows, num_seqs, max_query_len, num_heads, num_kv_heads, head_dim,
+                                   max_context_len, block_size=16, partition_size=0) -> int:
+    n = int(library().pa_chunked_prefill_workspace_size(num_query_rows, num_seqs, max_query_len, num_heads,
+                                                        num_kv_heads, head_dim, block_size, max_context_len,
+                                                        partition_size))
+    if n < 0:
+        raise ValueError("invalid chunked-prefill shape")
+    return n
+
+
+def chunked_prefill_workspace(num_query_rows, num_seqs, max_query_len, num_heads, num_kv_heads, head_dim,
+                              max_context_len, block_size=16, partition_size=0, device="cuda"):
+    """A workspace tensor of the required size (None when the call needs none)."""
+    n = chunked_prefill_workspace_size(num_query_rows, num_seqs, max_query_len, num_heads, num_kv_heads, head_dim,
+                                       max_context_len, block_size, partition_size)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def paged_attention_chunked_prefill(out, query, cu_query_lens, k_pool, v_pool, block_tables, context_lens, *,
+                                    max_query_len, max_context_len, num_kv_heads, scale, block_size=16,
+                                    k_scale=None, v_scale=None, partition_size=0, workspace=None, stream=None):
+    """Causal attention of each sequence's last q_len positions over its paged context
+    (pa_paged_attention_chunked_prefill).  query/out: [rows][Hq][D] bf16; cu_query_lens:
+    int32 [S+1]; block_tables: int32 [S][max_blocks]; context_lens: int32 [S]."""
+    for n, t in (("out", out), ("query", query), ("k_pool", k_pool), ("v_pool", v_pool)):
+        _dev(n, t)
+    _dev("cu_query_lens", cu_query_lens, torch.int32)
+    _dev("block_tables", block_tables, torch.int32)
+    _dev("context_lens", context_lens, torch.int32)
+    _dev("k_scale", k_scale, torch.float32)
+    _dev("v_scale", v_scale, torch.float32)
+    _dev("workspace", workspace)
+    if query.dim() != 3 or out.shape != query.shape or out.dtype != query.dtype:
+        raise ValueError("query and out must both be [num_query_rows][num_heads][head_dim] of one dtype")
+    rows, Hq, D = query.shape
+    S = context_lens.numel()
+    if cu_query_lens.numel() != S + 1 or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("cu_query_lens must be [S+1], block_tables [S][max_blocks], context_lens [S]")
+    nb = num_pool_blocks(k_pool, num_kv_heads, D, block_size)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().pa_paged_attention_chunked_prefill(
+        _ptr(out), _ptr(query), dtype_code(query), _ptr(cu_query_lens), rows, int(max_query_len), _ptr(k_pool),
+        _ptr(v_pool), nb, dtype_code(k_pool), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        int(max_context_len), S, Hq, num_kv_heads, D, block_size, float(scale), _ptr(k_scale), _ptr(v_scale),
+        int(partition_size), _ptr(workspace), ws_bytes, _stream(stream)))
     return out
 
 

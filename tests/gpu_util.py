@@ -73,6 +73,7 @@ class DeviceBatch:
         self.query = to_dev(batch.query_raw(), batch.q_dtype)
         self.k_scale = None if batch.k_scale is None else torch.from_numpy(batch.k_scale).to(DEV)
         self.v_scale = None if batch.v_scale is None else torch.from_numpy(batch.v_scale).to(DEV)
+        self.cu = torch.from_numpy(batch.cu_query_lens).to(DEV)
 
     def write(self, k_pool, v_pool, key_raw, value_raw, slots):
         b = self.b
@@ -103,6 +104,21 @@ class DeviceBatch:
                                    max_context_len=b.max_context_len, num_kv_heads=b.num_kv_heads, scale=b.scale,
                                    block_size=b.block_size, k_scale=self.k_scale, v_scale=self.v_scale,
                                    partition_size=partition_size, workspace=workspace, phase=phase)
+        return out
+
+    def prefill(self, k_pool, v_pool, partition_size=0, out=None, workspace="auto"):
+        b = self.b
+        if out is None:
+            out = torch.empty_like(self.query)
+        if isinstance(workspace, str):
+            workspace = ops.chunked_prefill_workspace(b.num_rows, b.num_seqs, b.max_query_len, b.num_heads,
+                                                      b.num_kv_heads, b.head_dim, b.max_context_len, b.block_size,
+                                                      partition_size)
+        ops.paged_attention_chunked_prefill(out, self.query, self.cu, k_pool, v_pool, self.tables, self.ctx,
+                                            max_query_len=b.max_query_len, max_context_len=b.max_context_len,
+                                            num_kv_heads=b.num_kv_heads, scale=b.scale, block_size=b.block_size,
+                                            k_scale=self.k_scale, v_scale=self.v_scale,
+                                            partition_size=partition_size, workspace=workspace)
         return out
 
 

@@ -155,3 +155,70 @@ def test_binding_without_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(ops, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         ops.library()
+
+
+def _prefill(lib, **kw):
+    a = dict(out=FAKE, query=FAKE, q_dtype=BF16, cu=FAKE, rows=512, max_q=512, k_pool=FAKE, v_pool=FAKE,
+             num_blocks=600, cache_dtype=FP8, block_tables=FAKE, mbps=512, context_lens=FAKE, max_ctx=8192, S=1,
+             Hq=32, Hkv=8, D=128, B=16, scale=0.088, k_scale=FAKE, v_scale=FAKE, P=0, ws=None, ws_bytes=0,
+             stream=None)
+    a.update(kw)
+    return lib.pa_paged_attention_chunked_prefill(
+        a["out"], a["query"], a["q_dtype"], a["cu"], a["rows"], a["max_q"], a["k_pool"], a["v_pool"],
+        a["num_blocks"], a["cache_dtype"], a["block_tables"], a["mbps"], a["context_lens"], a["max_ctx"], a["S"],
+        a["Hq"], a["Hkv"], a["D"], a["B"], a["scale"], a["k_scale"], a["v_scale"], a["P"], a["ws"], a["ws_bytes"],
+        a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=None), ops.PA_ERR_INVALID_ARG),
+    (dict(cu=None), ops.PA_ERR_INVALID_ARG),
+    (dict(q_dtype=F32, cache_dtype=F32), ops.PA_ERR_UNSUPPORTED),   # prefill runs on bf16 matrix cores
+    (dict(max_q=513), ops.PA_ERR_INVALID_ARG),                      # longer than all rows
+    (dict(max_q=0), ops.PA_ERR_INVALID_ARG),                        # rows but no row per sequence
+    (dict(rows=-1), ops.PA_ERR_INVALID_ARG),
+    (dict(k_scale=None), ops.PA_ERR_INVALID_ARG),                   # fp8 without scales
+    (dict(Hq=24, Hkv=2), ops.PA_ERR_UNSUPPORTED),
+    (dict(D=96), ops.PA_ERR_UNSUPPORTED),
+    (dict(P=40), ops.PA_ERR_INVALID_ARG),                           # not a multiple of 16
+    (dict(mbps=100), ops.PA_ERR_INVALID_ARG),                       # table shorter than max_ctx
+    (dict(num_blocks=0), ops.PA_ERR_INVALID_ARG),
+    (dict(out=FAKE + 2), ops.PA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), ops.PA_ERR_INVALID_ARG),
+    (dict(ws=None, ws_bytes=0), ops.PA_ERR_WORKSPACE),              # 128 row blocks -> split keys
+    (dict(ws=FAKE + 64, ws_bytes=1 << 30), ops.PA_ERR_WORKSPACE),
+])
+def test_prefill_rejects_before_launch(lib, kw, status):
+    assert _prefill(lib, **kw) == status
+    assert lib.pa_last_error() != b""
+
+
+def test_prefill_empty_is_ok_without_launch(lib):
+    assert _prefill(lib, S=0, out=None, query=None) == ops.PA_OK
+    assert _prefill(lib, rows=0, max_q=0, out=None, query=None) == ops.PA_OK
+
+
+def test_prefill_workspace_size(lib):
+    """Splits: partition_size given -> ceil(max_ctx / P); automatic -> enough workgroups of 128
+    stacked rows to reach 512, at most max_ctx / 256.  Workspace = fp32 partial rows plus
+    (max, sum) per split, row and head (256-byte aligned regions), none without a split."""
+    def expect(rows, S, max_q, Hq, Hkv, D, max_ctx, P):
+        G = Hq // Hkv
+        rb = -(-max_q * G // 128)
+        base = S * Hkv * rb
+        if P:
+            ns = -(-max_ctx // P) if max_ctx else 1
+        else:
+            ns = max(1, min(-(-512 // base) if base else 1, max_ctx // 256))
+        if ns == 1 or rows == 0:
+            return 0
+        al = lambda x: -(-x // 256) * 256
+        return al(ns * rows * Hq * D * 4) + al(ns * rows * Hq * 2 * 4)
+
+    for args in [(512, 1, 512, 32, 8, 128, 8192, 0), (512, 1, 512, 32, 8, 128, 8192, 1024),
+                 (640, 129, 512, 32, 8, 128, 8192, 0), (40, 3, 30, 8, 2, 64, 300, 0), (7, 7, 1, 4, 1, 128, 100, 0),
+                 (100, 2, 60, 16, 2, 128, 5000, 48)]:
+        rows, S, max_q, Hq, Hkv, D, max_ctx, P = args
+        got = lib.pa_chunked_prefill_workspace_size(rows, S, max_q, Hq, Hkv, D, 16, max_ctx, P)
+        assert got == expect(*args), args
+    assert lib.pa_chunked_prefill_workspace_size(10, 1, 11, 32, 8, 128, 16, 100, 0) == -1
