@@ -10,6 +10,11 @@ bf16, 16-token blocks, pool = used blocks + 10%); they are resident in HBM befor
 Several layers' pools (same block tables, different values) are cycled through so that no
 step finds the previous step's KV in the 256 MB last-level cache.
 
+With --workload fp8_chunked_prefill the step is the mixed one: append of the 512 chunk rows
+and the 128 decode tokens into an fp8 cache, chunked prefill of the chunk
+(pa_paged_attention_chunked_prefill, bf16 matrix cores) and decode of the 128 sequences;
+`roofline_prefill` then reports the chunk kernel against the bf16 MFMA peak.
+
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--layers L] [--partition-size P]
 
 Prints one JSON line.  `value` is algorithmic bytes of the step (KV read + query/output +
@@ -35,6 +40,7 @@ if ROOT not in sys.path:
 
 METRIC = "paged-attn decode achieved HBM TB/s (% of peak) + decode seqs/s per layer"
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -44,7 +50,7 @@ def parse_args():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="llama3_8b_decode",
-                   choices=["llama3_8b_decode", "long_context", "mixed_continuous_batch"])
+                   choices=["llama3_8b_decode", "long_context", "mixed_continuous_batch", "fp8_chunked_prefill"])
     p.add_argument("--layers", type=int, default=2, help="layer pools cycled through (>= 2)")
     p.add_argument("--partition-size", type=int, default=0, help="split-K partition (0 = library's choice)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -103,7 +109,7 @@ def source_digest():
     """Hash of the decode kernel's sources, to tell whether stored counter readings still apply."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_461_amd", "csrc")
-    for f in ("decode.hip", "pa_device.hpp", "pa_internal.hpp"):
+    for f in ("decode.hip", "prefill.hip", "pa_device.hpp", "pa_internal.hpp"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
@@ -136,20 +142,25 @@ def fill_pools(batch, layers, dev):
     pools = []
     for layer in range(layers):
         lb = dataclasses.replace(batch, layer=layer)
+        if batch.cache_dtype == W.FP8_E4M3:
+            lb.k_scale, lb.v_scale = W.fp8_calibration_scales(batch.num_kv_heads, batch.head_dim, batch.seed, layer,
+                                                              batch.src_dtype)
+        ks = None if lb.k_scale is None else torch.from_numpy(lb.k_scale).to(dev)
+        vs = None if lb.v_scale is None else torch.from_numpy(lb.v_scale).to(dev)
         kp = torch.zeros(batch.pool_elems, dtype=tdt, device=dev)
         vp = torch.zeros(batch.pool_elems, dtype=tdt, device=dev)
         for k, v, slots in lb.history_chunks():
             kt = torch.from_numpy(k.view(np.int16) if k.dtype == np.uint16 else k).to(dev).view(sdt)
             vt = torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).to(dev).view(sdt)
             ops.kv_cache_write(kt, vt, kp, vp, torch.from_numpy(slots).to(dev), num_kv_heads=batch.num_kv_heads,
-                               head_dim=batch.head_dim, block_size=batch.block_size)
+                               head_dim=batch.head_dim, block_size=batch.block_size, k_scale=ks, v_scale=vs)
         k, v, slots = lb.new_tokens()
         new = (torch.from_numpy(k.view(np.int16) if k.dtype == np.uint16 else k).to(dev).view(sdt),
                torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).to(dev).view(sdt),
                torch.from_numpy(slots).to(dev))
         q = lb.query_raw()
         qt = torch.from_numpy(q.view(np.int16) if q.dtype == np.uint16 else q).to(dev).view(sdt)
-        pools.append((kp, vp, new, qt))
+        pools.append((kp, vp, new, qt, ks, vs))
     torch.cuda.synchronize()
     return pools
 
@@ -160,25 +171,31 @@ def cpu_baseline(batch, min_seconds=1.5):
     import oracle
 
     kp, vp = batch.empty_pool(poison=False)
-    for k, v, slots in batch.history_chunks():
+
+    def append(k, v, slots):
         oracle.kv_cache_write(k, v, batch.src_dtype, kp, vp, batch.cache_dtype, slots, batch.num_kv_heads,
-                              batch.head_dim, batch.block_size)
+                              batch.head_dim, batch.block_size, batch.k_scale, batch.v_scale)
+
+    for k, v, slots in batch.history_chunks():
+        append(k, v, slots)
     k, v, slots = batch.new_tokens()
     q = batch.query_raw()
+    cu = None if batch.is_decode else batch.cu_query_lens
     cores = len(os.sched_getaffinity(0))
     runs, t0 = 0, time.perf_counter()
     while runs == 0 or time.perf_counter() - t0 < min_seconds:  # repeat to >= min_seconds of wall time
-        oracle.kv_cache_write(k, v, batch.src_dtype, kp, vp, batch.cache_dtype, slots, batch.num_kv_heads,
-                              batch.head_dim, batch.block_size)
+        append(k, v, slots)
         oracle.paged_attention(q, batch.q_dtype, kp, vp, batch.cache_dtype, batch.block_tables,
                                batch.context_lens, batch.num_heads, batch.num_kv_heads, batch.head_dim,
-                               batch.block_size, batch.scale, nthreads=cores)
+                               batch.block_size, batch.scale, cu_query_lens=cu, k_scale=batch.k_scale,
+                               v_scale=batch.v_scale, nthreads=cores)
         runs += 1
     dt = (time.perf_counter() - t0) / runs
     step_bytes = batch.decode_bytes() + batch.write_bytes()
     return {"value": step_bytes / dt / 1e12, "unit": "TB/s", "cores": cores, "kind": "oracle",
-            "sample": "the whole %s step for one layer (%d appends + %d decode rows x %d heads), %d runs"
-                      % (batch.name, batch.num_rows, batch.num_seqs, batch.num_heads, runs),
+            "sample": "the whole %s step for one layer (%d appended rows, %d query rows x %d heads over %d "
+                      "sequences), %d runs" % (batch.name, batch.num_rows, batch.num_rows, batch.num_heads,
+                                               batch.num_seqs, runs),
             "seconds_per_step": dt, "seqs_per_s_per_layer": batch.num_seqs / dt}
 
 
@@ -214,19 +231,50 @@ def main():
     pools = fill_pools(batch, args.layers, dev)
     print("# pools filled in %.1f s" % (time.time() - t0), file=sys.stderr, flush=True)
 
+    # Rows of sequences with more than one query row go to the chunked-prefill call; the
+    # decode sequences (one row each) follow them and go to the decode call.
+    ql = batch.query_lens
+    Sp = int(np.argmax(ql == 1)) if (ql == 1).any() else len(ql)
+    assert (ql[:Sp] > 1).all() and (ql[Sp:] == 1).all(), "prefill sequences must precede decode sequences"
+    Rp = int(ql[:Sp].sum())
     tables = torch.from_numpy(batch.block_tables).to(dev)
     ctx = torch.from_numpy(batch.context_lens).to(dev)
+    cu = torch.from_numpy(batch.cu_query_lens).to(dev)
     P = args.partition_size
-    ws = ops.decode_workspace(S, Hq, Hkv, D, batch.max_context_len, B, P, device=dev)
+    Sd = S - Sp
+    dec_max_ctx = int(batch.context_lens[Sp:].max()) if Sd else 0
+    ws = ops.decode_workspace(Sd, Hq, Hkv, D, dec_max_ctx, B, P, device=dev) if Sd else None
+    pf_max_q = int(ql[:Sp].max()) if Sp else 0
+    pf_max_ctx = int(batch.context_lens[:Sp].max()) if Sp else 0
+    pf_ws = ops.chunked_prefill_workspace(Rp, Sp, pf_max_q, Hq, Hkv, D, pf_max_ctx, B, 0, device=dev) if Sp else None
     outs = [torch.empty_like(p[3]) for p in pools]
     stream = torch.cuda.current_stream()
 
+    def write(r):
+        kp, vp, (nk, nv, nslots), q, ks, vs = pools[r % len(pools)]
+        ops.kv_cache_write(nk, nv, kp, vp, nslots, num_kv_heads=Hkv, head_dim=D, block_size=B, k_scale=ks,
+                           v_scale=vs, stream=stream)
+
+    def prefill(r):
+        kp, vp, _, q, ks, vs = pools[r % len(pools)]
+        ops.paged_attention_chunked_prefill(outs[r % len(pools)][:Rp], q[:Rp], cu[:Sp + 1], kp, vp, tables[:Sp],
+                                            ctx[:Sp], max_query_len=pf_max_q, max_context_len=pf_max_ctx,
+                                            num_kv_heads=Hkv, scale=batch.scale, block_size=B, k_scale=ks,
+                                            v_scale=vs, workspace=pf_ws, stream=stream)
+
+    def decode(r, phase=3):
+        kp, vp, _, q, ks, vs = pools[r % len(pools)]
+        ops.paged_attention_decode(outs[r % len(pools)][Rp:], q[Rp:], kp, vp, tables[Sp:], ctx[Sp:],
+                                   max_context_len=dec_max_ctx, num_kv_heads=Hkv, scale=batch.scale, block_size=B,
+                                   k_scale=ks, v_scale=vs, partition_size=P, workspace=ws, phase=phase,
+                                   stream=stream)
+
     def step(i):
-        kp, vp, (nk, nv, nslots), q = pools[i % len(pools)]
-        ops.kv_cache_write(nk, nv, kp, vp, nslots, num_kv_heads=Hkv, head_dim=D, block_size=B, stream=stream)
-        common = dict(max_context_len=batch.max_context_len, num_kv_heads=Hkv, scale=batch.scale, block_size=B,
-                      partition_size=P, workspace=ws, stream=stream)
-        ops.paged_attention_decode(outs[i % len(pools)], q, kp, vp, tables, ctx, phase=3, **common)
+        write(i)
+        if Sp:
+            prefill(i)
+        if Sd:
+            decode(i)
 
     for i in range(args.warmup):
         step(i)
@@ -256,36 +304,21 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / reps  # us
 
-    common = dict(max_context_len=batch.max_context_len, num_kv_heads=Hkv, scale=batch.scale, block_size=B,
-                  partition_size=P, workspace=ws, stream=stream)
-
-    def write_only(r):
-        kp, vp, (nk, nv, nslots), q = pools[r % len(pools)]
-        ops.kv_cache_write(nk, nv, kp, vp, nslots, num_kv_heads=Hkv, head_dim=D, block_size=B, stream=stream)
-
-    def stream_only(r):
-        kp, vp, _, q = pools[r % len(pools)]
-        ops.paged_attention_decode(outs[r % len(pools)], q, kp, vp, tables, ctx, phase=1, **common)
-
-    def merge_only(r):
-        kp, vp, _, q = pools[(args.steps - 1) % len(pools)]
-        ops.paged_attention_decode(outs[0], q, kp, vp, tables, ctx, phase=2, **common)
-
-    t_write = np.array([launches(write_only, args.steps)])
-    t_part = np.array([launches(stream_only, args.steps)])
-    t_red = np.array([launches(merge_only, args.steps)])
-
-    step_bytes = batch.decode_bytes() + batch.write_bytes()
     from paged_kv_cache_461_amd import workloads as W
 
-    out_bytes = batch.num_rows * Hq * D * W.ELEM_BYTES[batch.q_dtype]
-    part_bytes = batch.decode_bytes() - out_bytes  # KV + query + tables + lengths
-    part_us = float(t_part.mean())
-    achieved = part_bytes / (part_us * 1e-6) / 1e9
+    kernels = {"kv_write": round(launches(write, args.steps), 2)}
+    if Sp:
+        kernels["chunked_prefill"] = round(launches(prefill, args.steps), 2)
+    if Sd:
+        kernels["decode_stream"] = round(launches(lambda r: decode(r, 1), args.steps), 2)
+        kernels["decode_merge"] = round(launches(lambda r: decode(args.steps - 1, 2), args.steps), 2)
+    kernels["timing"] = ("K back-to-back launches of each kernel between two HIP events on the launch stream, "
+                         "after the timed region")
+
+    step_bytes = batch.decode_bytes() + batch.write_bytes()
     value = step_bytes / (ms_per_step * 1e-3) / 1e12
     digest = source_digest()
-    traffic = stored_traffic(batch.name, digest)
-
+    eq = W.ELEM_BYTES[batch.q_dtype]
     res = {
         "metric": METRIC,
         "value": round(value, 4),
@@ -301,7 +334,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": batch.name, "num_seqs": S, "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
-            "block_size": B, "context_lens": "seeded, %d..%d, sum %d" % (
+            "block_size": B, "cache_dtype": {W.BF16: "bf16", W.F32: "f32", W.FP8_E4M3: "fp8_e4m3"}[batch.cache_dtype],
+            "context_lens": "seeded, %d..%d, sum %d" % (
                 batch.context_lens.min(), batch.context_lens.max(), int(batch.context_lens.sum())),
             "num_blocks": batch.num_blocks, "layers_cycled": args.layers,
             "partition_size": "auto (equal chunks per wave)" if P == 0 else P,
@@ -309,18 +343,35 @@ def main():
         "frac_of_hbm_peak": round(value * 1e3 / HBM_PEAK_GBS, 4),
         "seqs_per_s_per_layer": round(S / (ms_per_step * 1e-3), 1),
         "step_bytes": int(step_bytes),
-        "kernels_us": {"kv_write": round(float(t_write.mean()), 2), "decode_stream": round(part_us, 2),
-                       "decode_merge": round(float(t_red.mean()), 2),
-                       "timing": "K back-to-back launches of each kernel between two HIP events on the "
-                                 "launch stream, after the timed region"},
-        "roofline": {"bound": "hbm", "kernel": "decode_stream_kernel", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": int(part_bytes),
-                     "source_digest": digest},
+        "kernels_us": kernels,
     }
+    if Sp:
+        res["config"]["prefill_rows"] = Rp
+    if Sd:
+        # decode kernel: KV of the decode sequences + their queries + tables + lengths (+ scales)
+        dec = dataclasses.replace(batch, context_lens=batch.context_lens[Sp:], query_lens=ql[Sp:],
+                                  block_tables=batch.block_tables[Sp:])
+        part_bytes = dec.decode_bytes() - dec.num_rows * Hq * D * eq
+        achieved = part_bytes / (kernels["decode_stream"] * 1e-6) / 1e9
+        res["roofline"] = {"bound": "hbm", "kernel": "decode_stream_kernel", "achieved": round(achieved, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                           "traffic": stored_traffic(batch.name, digest),
+                           "algorithmic_bytes_per_launch": int(part_bytes), "source_digest": digest}
+    if Sp:
+        pos = [np.arange(c - q, c, dtype=np.int64) for c, q in zip(batch.context_lens[:Sp], ql[:Sp])]
+        visible = int(sum(int((p + 1).sum()) for p in pos))  # (row, key) pairs of the causal chunks
+        flops = 4.0 * D * Hq * visible  # q.k and p.v: 2 flops per multiply-add, per channel
+        tflops = flops / (kernels["chunked_prefill"] * 1e-6) / 1e12
+        res["roofline_prefill"] = {"bound": "mfma", "kernel": "prefill_kernel (+ merge)",
+                                   "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                   "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                                   "algorithmic_flops_per_launch": flops}
+    if "roofline" not in res:
+        res["roofline"] = dict(res["roofline_prefill"])
     probe = read_probe(stream)
     res["hbm_read_probe"] = probe
-    res["roofline"]["frac_of_probe"] = round(achieved / probe["achieved"], 4)
+    if res["roofline"]["bound"] == "hbm":
+        res["roofline"]["frac_of_probe"] = round(res["roofline"]["achieved"] / probe["achieved"], 4)
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(batch)

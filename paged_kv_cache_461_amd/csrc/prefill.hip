@@ -24,6 +24,8 @@
 //     running max only moved when a row's max grows by more than 8 (p stays <= 256).
 //   * Keys split over several workgroups (split-K) when the grid would otherwise not fill the
 //     GPU; a merge kernel combines the partial rows.
+#include <type_traits>
+
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
@@ -54,29 +56,54 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// 16 E4M3 bytes -> 16 bf16 (two 16-byte halves), exact.
-__device__ __forceinline__ void e4m3x16_to_bf16(const uint4& v, uint4& lo, uint4& hi)
+// Keep the first n bf16 of an 8-element group (n may be <= 0 or >= 8), zero the rest.
+__device__ __forceinline__ u32x4_t keep_bf16(u32x4_t v, int n)
 {
-    lo.x = e4m3x2_to_bf16x2<false>(v.x);
-    lo.y = e4m3x2_to_bf16x2<true>(v.x);
-    lo.z = e4m3x2_to_bf16x2<false>(v.y);
-    lo.w = e4m3x2_to_bf16x2<true>(v.y);
-    hi.x = e4m3x2_to_bf16x2<false>(v.z);
-    hi.y = e4m3x2_to_bf16x2<true>(v.z);
-    hi.z = e4m3x2_to_bf16x2<false>(v.w);
-    hi.w = e4m3x2_to_bf16x2<true>(v.w);
-}
-
-// Keep the first n (0..8) bf16 of an 8-element group, zero the rest.
-__device__ __forceinline__ uint4 keep_bf16(uint4 v, int n)
-{
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const int t = 2 * i;
-        w[i] = t + 1 < n ? w[i] : t < n ? (w[i] & 0xFFFFu) : 0u;
+        v[i] = t + 1 < n ? v[i] : t < n ? (v[i] & 0xFFFFu) : 0u;
     }
-    return make_uint4(w[0], w[1], w[2], w[3]);
+    return v;
+}
+
+// Channel order inside an LDS K row, in chunks of 8 channels.  The products read chunk
+// position 4*st + grp (step st, lane group grp) and the query fragments follow the same
+// order, so any permutation is valid; for head_dim 128 it is chosen so that the 16 lanes of
+// a staging store (4 tokens x 4 pieces) hit distinct LDS banks: pieces of one token land 4
+// positions (64 bytes) apart.  fp8: lane piece = 16 channels 64*slice + 16*q .. (two chunks);
+// bf16: lane piece = 8 channels 32*slice + 8*q.
+template <int KT, int D>
+__device__ __forceinline__ int k_pos_of_chunk(int c8)
+{
+    if constexpr (D != 128) return c8;
+    else if constexpr (KT == kFP8) return 4 * ((c8 & 7) >> 1) + 2 * (c8 >> 3) + (c8 & 1);
+    else return 4 * (c8 & 3) + (c8 >> 2);
+}
+template <int KT, int D>
+__device__ __forceinline__ int k_chunk_of_pos(int p)
+{
+    if constexpr (D != 128) return p;
+    else if constexpr (KT == kFP8) return 8 * ((p & 3) >> 1) + 2 * (p >> 2) + (p & 1);
+    else return 4 * (p & 3) + (p >> 2);
+}
+
+// LDS fragments of a product loop are read kRing ahead of the MFMAs that use them.
+constexpr int kRing = 4;
+
+// Scheduling hint for such a loop over N fragments with R products each: kRing reads, then
+// (R products, one read) while reads remain, then the last kRing x R products.
+template <int N, int R>
+__device__ __forceinline__ void ring_schedule()
+{
+    __builtin_amdgcn_sched_group_barrier(0x100, kRing, 0);
+#pragma unroll
+    for (int i = 0; i < N - kRing; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, R, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kRing; i++) __builtin_amdgcn_sched_group_barrier(0x008, R, 0);
 }
 
 // LDS row of key o of block b (0..3) of an iteration: tile u = o / 4 of the S^T product reads
@@ -84,7 +111,7 @@ __device__ __forceinline__ uint4 keep_bf16(uint4 v, int n)
 __device__ __forceinline__ int k_lds_row(int b, int o) { return 16 * (o >> 2) + 4 * b + (o & 3); }
 
 template <int KT, int D, int G, int R>
-__global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
+__global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs a)
 {
     using L = PfLds<D>;
     constexpr int EB = KT == kFP8 ? 1 : 2;
@@ -112,21 +139,23 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     const int g = t % a.num_kv_heads;
     const int s = t / a.num_kv_heads;
 
-    int q0 = a.cu_query_lens[s];
-    int qlen = a.cu_query_lens[s + 1] - q0;
+    // values loaded once per workgroup: readfirstlane keeps them (and all loop control derived
+    // from them) in scalar registers
+    const int q0 = __builtin_amdgcn_readfirstlane(a.cu_query_lens[s]);
+    int qlen = __builtin_amdgcn_readfirstlane(a.cu_query_lens[s + 1]) - q0;
     if (q0 < 0 || qlen < 0 || q0 > a.num_query_rows - qlen) qlen = 0;  // rows outside the query array
     const int i_first = rb * POS;
     if (i_first >= qlen) return;  // uniform over the workgroup
     const int i_last = min(i_first + POS, qlen) - 1;
-    const int ctx = min(max(a.context_lens[s], 0), a.max_context_len);
+    const int ctx = min(max(__builtin_amdgcn_readfirstlane(a.context_lens[s]), 0), a.max_context_len);
     const int past = ctx - qlen;  // positions before the chunk
     const int kend = max(past + i_last + 1, 0);  // keys any row of the workgroup sees
 
     // key range of this split: fixed-size partitions, or kend cut into num_splits equal parts
     int per = a.split_keys;
     if (per <= 0) per = ((kend + a.num_splits - 1) / a.num_splits + kPfKeys - 1) / kPfKeys * kPfKeys;
-    const int kbeg = min(split * per, kend);
-    const int kstop = min(kbeg + per, kend);
+    const int kbeg = __builtin_amdgcn_readfirstlane(min(split * per, kend));
+    const int kstop = __builtin_amdgcn_readfirstlane(min(kbeg + per, kend));
     const int niter = (kstop - kbeg + kPfKeys - 1) / kPfKeys;
 
     const int tid = threadIdx.x;
@@ -148,10 +177,10 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         const bool valid = i <= i_last;
         prow[r] = valid ? past + i : -1;
         orow[r] = valid ? (int64_t)(q0 + i) * Hq + h : -1;
-        const __bf16* qp = static_cast<const __bf16*>(a.query) + (valid ? orow[r] : 0) * D + 8 * grp;
+        const __bf16* qp = static_cast<const __bf16*>(a.query) + (valid ? orow[r] : 0) * D;
 #pragma unroll
         for (int st = 0; st < NS; st++)
-            qb[r][st] = as_bf16x8(valid ? load16(qp + 32 * st) : make_uint4(0, 0, 0, 0));
+            qb[r][st] = as_bf16x8(valid ? load16(qp + 8 * k_chunk_of_pos<KT, D>(4 * st + grp)) : make_uint4(0, 0, 0, 0));
     }
     // wave-uniform bounds of the rows' visible keys (padding rows count as seeing nothing)
     const int wi_lo = i_first + (16 * R * w) / G, wi_hi = i_first + (16 * R * w + 16 * R - 1) / G;
@@ -184,69 +213,104 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     uint32_t okbits = 0;  // bit j: piece j comes from a block that holds tokens of this range
     __shared__ int blk_ok[2][4];  // per buffer: block b of the iteration has a valid table entry
 
+    // The block of piece j is the same for all 64 lanes of a wave (a tile is a whole number of
+    // 1 KiB wave loads), so its checks are uniform.  Each load() fetches the table entries the
+    // next load() needs, unconditionally (the index is clamped to the range's last block), so
+    // a K/V load never waits on a table read.
+    static_assert(CH_PER_TILE % 64 == 0, "wave-uniform block per piece");
+    const int last_blk = kstop > 0 ? (kstop - 1) >> 4 : 0;
+    int ent[NCH];
+    auto fetch_entries = [&](int kbase) {
+#pragma unroll
+        for (int j = 0; j < NCH; j++) {
+            const int b = __builtin_amdgcn_readfirstlane((tid + kPrefillThreads * j) / CH_PER_TILE);
+            ent[j] = table[min((kbase >> 4) + b, last_blk)];
+        }
+    };
     auto load = [&](int kbase) {
         okbits = 0;
 #pragma unroll
         for (int j = 0; j < NCH; j++) {
             const int c = tid + kPrefillThreads * j;
-            const int b = c / CH_PER_TILE;
+            const int b = __builtin_amdgcn_readfirstlane(c / CH_PER_TILE);
             const int off = (c % CH_PER_TILE) * 16;
-            bool ok = kbase + 16 * b < kstop;
-            int phys = ok ? table[(kbase >> 4) + b] : 0;
-            ok = ok && phys >= 0 && (int64_t)phys < a.num_blocks;
+            const int phys = __builtin_amdgcn_readfirstlane(ent[j]);
+            const bool ok = kbase + 16 * b < kstop && phys >= 0 && (int64_t)phys < a.num_blocks;
+            // a block with no valid entry still reads block 0 (the pool has one); store() zeroes it
             const int64_t base = ((int64_t)(ok ? phys : 0) * a.num_kv_heads + g) * TILE_BYTES + off;
-            kr[j] = ok ? load16(kpool + base) : make_uint4(0, 0, 0, 0);
-            vr[j] = ok ? load16(vpool + base) : make_uint4(0, 0, 0, 0);
+            kr[j] = load16(kpool + base);
+            vr[j] = load16(vpool + base);
             okbits |= ok ? 1u << j : 0u;
         }
+        fetch_entries(kbase + kPfKeys);  // for the next load, one compute phase away
     };
 
+    // Convert and place piece j.  MASK: zero tokens at or past nval of the piece's block (the
+    // range end, or the whole block when its table entry is invalid).
+    auto put = [&](auto mask_tag, int j, __bf16* kl, __bf16* vl, int buf, int kbase) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const int c = tid + kPrefillThreads * j;
+        const int b = c / CH_PER_TILE;
+        const int off = (c % CH_PER_TILE) * 16;
+        const bool blk = okbits >> j & 1u;
+        if (off == 0) blk_ok[buf][b] = blk;  // one piece per block starts it
+        const int nval = MASK ? (blk ? min(kstop - (kbase + 16 * b), 16) : 0) : 16;  // valid tokens
+        // K: 64-byte channel slices, token-major: a piece is 16 bytes of one token
+        const int slice = off >> 10;
+        const int tok = (off & 1023) >> 6;
+        __bf16* krow = kl + k_lds_row(b, tok) * L::KS;
+        const bool kzero = MASK && tok >= nval;
+        if constexpr (KT == kFP8) {
+            const int c8 = (64 * slice + (off & 63)) >> 3;
+            const uint4 w = kr[j];
+            u32x4_t lo = {e4m3x2_to_bf16x2<false>(w.x), e4m3x2_to_bf16x2<true>(w.x), e4m3x2_to_bf16x2<false>(w.y),
+                          e4m3x2_to_bf16x2<true>(w.y)};
+            u32x4_t hi = {e4m3x2_to_bf16x2<false>(w.z), e4m3x2_to_bf16x2<true>(w.z), e4m3x2_to_bf16x2<false>(w.w),
+                          e4m3x2_to_bf16x2<true>(w.w)};
+            if (kzero) lo = hi = u32x4_t{0, 0, 0, 0};
+            *reinterpret_cast<u32x4_t*>(krow + 8 * k_pos_of_chunk<KT, D>(c8)) = lo;
+            *reinterpret_cast<u32x4_t*>(krow + 8 * k_pos_of_chunk<KT, D>(c8 + 1)) = hi;
+            // V: 16 tokens of channel d side by side
+            const int d = off >> 4;
+            const uint4 v = vr[j];
+            u32x4_t vlo = {e4m3x2_to_bf16x2<false>(v.x), e4m3x2_to_bf16x2<true>(v.x), e4m3x2_to_bf16x2<false>(v.y),
+                           e4m3x2_to_bf16x2<true>(v.y)};
+            u32x4_t vhi = {e4m3x2_to_bf16x2<false>(v.z), e4m3x2_to_bf16x2<true>(v.z), e4m3x2_to_bf16x2<false>(v.w),
+                           e4m3x2_to_bf16x2<true>(v.w)};
+            if constexpr (MASK) {
+                vlo = keep_bf16(vlo, nval);
+                vhi = keep_bf16(vhi, nval - 8);
+            }
+            *reinterpret_cast<u32x4_t*>(vl + d * L::VS + 16 * b) = vlo;
+            *reinterpret_cast<u32x4_t*>(vl + d * L::VS + 16 * b + 8) = vhi;
+        } else {
+            const int c8 = (32 * slice + ((off & 63) >> 1)) >> 3;
+            u32x4_t k = __builtin_bit_cast(u32x4_t, kr[j]);
+            if (kzero) k = u32x4_t{0, 0, 0, 0};
+            *reinterpret_cast<u32x4_t*>(krow + 8 * k_pos_of_chunk<KT, D>(c8)) = k;
+            // V: groups of 8 tokens, channel-major
+            const int gi = off >> 4;
+            const int og = gi / D, d = gi % D;
+            u32x4_t v = __builtin_bit_cast(u32x4_t, vr[j]);
+            if constexpr (MASK) v = keep_bf16(v, nval - 8 * og);
+            *reinterpret_cast<u32x4_t*>(vl + d * L::VS + 16 * b + 8 * og) = v;
+        }
+    };
     auto store = [&](int buf, int kbase) {
         __bf16* kl = lds + buf * L::STAGE;
         __bf16* vl = kl + L::K_ELEMS;
+        // all four blocks valid and inside the range: no token to zero (wave-uniform)
+        if (kbase + kPfKeys <= kstop && okbits == (1u << NCH) - 1) {
 #pragma unroll
-        for (int j = 0; j < NCH; j++) {
-            const int c = tid + kPrefillThreads * j;
-            const int b = c / CH_PER_TILE;
-            const int off = (c % CH_PER_TILE) * 16;
-            const bool blk = okbits >> j & 1u;
-            if (off == 0) blk_ok[buf][b] = blk;  // one piece per block starts it
-            const int nval = blk ? min(kstop - (kbase + 16 * b), 16) : 0;  // valid tokens of block b
-            // K: 64-byte channel slices, token-major: a piece is 16 bytes of one token
-            const int slice = off >> 10;
-            const int ok_ = (off & 1023) >> 6;
-            const int krow = k_lds_row(b, ok_);
-            const bool kval = ok_ < nval;
-            if constexpr (KT == kFP8) {
-                const int d0 = 64 * slice + (off & 63);
-                uint4 lo, hi;
-                e4m3x16_to_bf16(kr[j], lo, hi);
-                if (!kval) lo = hi = make_uint4(0, 0, 0, 0);
-                *reinterpret_cast<uint4*>(kl + krow * L::KS + d0) = lo;
-                *reinterpret_cast<uint4*>(kl + krow * L::KS + d0 + 8) = hi;
-                // V: 16 tokens of channel d side by side
-                const int d = off >> 4;
-                e4m3x16_to_bf16(vr[j], lo, hi);
-                if (nval < 16) {
-                    lo = keep_bf16(lo, nval);
-                    hi = keep_bf16(hi, nval - 8);
-                }
-                *reinterpret_cast<uint4*>(vl + d * L::VS + 16 * b) = lo;
-                *reinterpret_cast<uint4*>(vl + d * L::VS + 16 * b + 8) = hi;
-            } else {
-                const int d0 = 32 * slice + ((off & 63) >> 1);
-                *reinterpret_cast<uint4*>(kl + krow * L::KS + d0) = kval ? kr[j] : make_uint4(0, 0, 0, 0);
-                // V: groups of 8 tokens, channel-major
-                const int gi = off >> 4;
-                const int og = gi / D, d = gi % D;
-                uint4 v = vr[j];
-                if (nval < 16) v = keep_bf16(v, nval - 8 * og);
-                *reinterpret_cast<uint4*>(vl + d * L::VS + 16 * b + 8 * og) = v;
-            }
+            for (int j = 0; j < NCH; j++) put(std::false_type{}, j, kl, vl, buf, kbase);
+        } else {
+#pragma unroll
+            for (int j = 0; j < NCH; j++) put(std::true_type{}, j, kl, vl, buf, kbase);
         }
     };
 
     int kbase = kbeg;
+    fetch_entries(kbase);
     if (niter > 0) load(kbase);
     for (int it = 0; it < niter; ++it, kbase += kPfKeys) {
         const int buf = it & 1;
@@ -257,43 +321,59 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         // keys of block grp that have no valid table entry are masked like causal ones
         const bool blk_valid = blk_ok[buf][grp] != 0;
         const bool need_mask = kbase + kPfKeys - 1 > kw_min || __builtin_amdgcn_ballot_w64(!blk_valid) != 0;
+        const int key0 = kbase + 16 * grp;  // the lane's keys are key0 + 4u + j
         const __bf16* kl = lds + buf * L::STAGE;
         const __bf16* vl = kl + L::K_ELEMS;
 
-        // S^T tiles: sacc[r][u] = keys of tile u x query rows of tile r
+        // S^T tiles: sacc[r][u] = keys of tile u x query rows of tile r.  Fragment i = (step
+        // i / 4, tile i % 4) is read kRing fragments ahead of its products.
         f32x4_t sacc[R][4];
 #pragma unroll
         for (int r = 0; r < R; r++)
 #pragma unroll
             for (int u = 0; u < 4; u++) sacc[r][u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        auto kread = [&](int i) {
+            return *reinterpret_cast<const bf16x8_t*>(kl + (16 * (i & 3) + col) * L::KS + 32 * (i >> 2) + 8 * grp);
+        };
+        {
+            bf16x8_t kf[kRing];
 #pragma unroll
-        for (int st = 0; st < NS; st++) {
+            for (int i = 0; i < kRing; i++) kf[i] = kread(i);
 #pragma unroll
-            for (int u = 0; u < 4; u++) {
-                const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kl + (16 * u + col) * L::KS + 32 * st + 8 * grp);
+            for (int i = 0; i < 4 * NS; i++) {
 #pragma unroll
-                for (int r = 0; r < R; r++) sacc[r][u] = mfma_16x16x32(ka, qb[r][st], sacc[r][u]);
+                for (int r = 0; r < R; r++) sacc[r][i & 3] = mfma_16x16x32(kf[i % kRing], qb[r][i >> 2], sacc[r][i & 3]);
+                if (i + kRing < 4 * NS) kf[i % kRing] = kread(i + kRing);
             }
+            ring_schedule<4 * NS, R>();
         }
 
         // online softmax; lane holds keys 16*grp + 4u + j of its row
         bf16x8_t pb[R][2];
 #pragma unroll
         for (int r = 0; r < R; r++) {
+            // raw scores; the scale (> 0) is applied to the max and inside the exponent's FMA
             float z[4][4];
+            if (need_mask) {
+                const int lim = blk_valid ? klim[r] - key0 : -1;  // last visible key offset
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+#pragma unroll
+                    for (int j = 0; j < 4; j++) z[u][j] = 4 * u + j > lim ? -__builtin_inff() : sacc[r][u][j];
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+#pragma unroll
+                    for (int j = 0; j < 4; j++) z[u][j] = sacc[r][u][j];
+            }
             float mx = -__builtin_inff();
 #pragma unroll
             for (int u = 0; u < 4; u++)
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    float v = sacc[r][u][j] * sc;
-                    if (need_mask)
-                        v = (kbase + 16 * grp + 4 * u + j > klim[r] || !blk_valid) ? -__builtin_inff() : v;
-                    z[u][j] = v;
-                    mx = __builtin_fmaxf(mx, v);
-                }
+                mx = __builtin_fmaxf(__builtin_fmaxf(mx, __builtin_fmaxf(z[u][0], z[u][1])),
+                                     __builtin_fmaxf(z[u][2], z[u][3]));
             mx = __builtin_fmaxf(mx, swizzle_xor16(mx));
             mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
+            mx *= sc;
             const bool up = mx > m[r] + kPfMargin;
             if (__builtin_amdgcn_ballot_w64(up)) {
                 const float mn = up ? mx : m[r];
@@ -310,8 +390,11 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
 #pragma unroll
                 for (int v2 = 0; v2 < 2; v2++) {
                     const int u = 2 * h2 + v2;
-                    const uint32_t p01 = pack_bf16x2(fast_exp2(z[u][0] - m[r]), fast_exp2(z[u][1] - m[r]));
-                    const uint32_t p23 = pack_bf16x2(fast_exp2(z[u][2] - m[r]), fast_exp2(z[u][3] - m[r]));
+                    const float nm = -m[r];
+                    const uint32_t p01 = pack_bf16x2(fast_exp2(__builtin_fmaf(z[u][0], sc, nm)),
+                                                     fast_exp2(__builtin_fmaf(z[u][1], sc, nm)));
+                    const uint32_t p23 = pack_bf16x2(fast_exp2(__builtin_fmaf(z[u][2], sc, nm)),
+                                                     fast_exp2(__builtin_fmaf(z[u][3], sc, nm)));
                     pw[h2][2 * v2] = p01;
                     pw[h2][2 * v2 + 1] = p23;
                     ls = dot2_bf16(p01, kBf16OnePair, ls);
@@ -323,15 +406,22 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
                 pb[r][h2] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[h2][0], pw[h2][1], pw[h2][2], pw[h2][3]));
         }
 
-        // O^T += V^T P^T: V^T rows = channels, k = keys 16*grp + 8*h2 + 0..7
+        // O^T += V^T P^T: V^T rows = channels, k = keys 16*grp + 8*h2 + 0..7; fragment
+        // i = (half i / ND, channel tile i % ND), read kRing ahead.
+        auto vread = [&](int i) {
+            return *reinterpret_cast<const bf16x8_t*>(vl + (16 * (i % ND) + col) * L::VS + 16 * grp + 8 * (i / ND));
+        };
+        {
+            bf16x8_t vf[kRing];
 #pragma unroll
-        for (int h2 = 0; h2 < 2; h2++) {
+            for (int i = 0; i < kRing; i++) vf[i] = vread(i);
 #pragma unroll
-            for (int d = 0; d < ND; d++) {
-                const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(vl + (16 * d + col) * L::VS + 16 * grp + 8 * h2);
+            for (int i = 0; i < 2 * ND; i++) {
 #pragma unroll
-                for (int r = 0; r < R; r++) o[r][d] = mfma_16x16x32(va, pb[r][h2], o[r][d]);
+                for (int r = 0; r < R; r++) o[r][i % ND] = mfma_16x16x32(vf[i % kRing], pb[r][i / ND], o[r][i % ND]);
+                if (i + kRing < 2 * ND) vf[i % kRing] = vread(i + kRing);
             }
+            ring_schedule<2 * ND, R>();
         }
     }
 
