@@ -53,6 +53,9 @@ def parse_args():
                    choices=["llama3_8b_decode", "long_context", "mixed_continuous_batch", "fp8_chunked_prefill"])
     p.add_argument("--layers", type=int, default=2, help="layer pools cycled through (>= 2)")
     p.add_argument("--partition-size", type=int, default=0, help="split-K partition (0 = library's choice)")
+    p.add_argument("--extra-workload", default="fp8_chunked_prefill",
+                   choices=["none", "fp8_chunked_prefill", "llama3_8b_decode", "long_context", "mixed_continuous_batch"],
+                   help="second workload measured in the same run and reported under extra_step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device copy (HBM counter calibration) and exit")
@@ -105,22 +108,29 @@ def make_batch(name):
     return W.WORKLOADS[name]()
 
 
-def source_digest():
-    """Hash of the decode kernel's sources, to tell whether stored counter readings still apply."""
+KERNEL_SOURCES = {
+    "decode": ("decode.hip", "pa_device.hpp", "pa_internal.hpp"),
+    "prefill": ("prefill.hip", "pa_device.hpp", "pa_internal.hpp"),
+}
+
+
+def source_digest(kernel="decode"):
+    """Hash of one kernel's sources, to tell whether stored counter readings still apply."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_461_amd", "csrc")
-    for f in ("decode.hip", "prefill.hip", "pa_device.hpp", "pa_internal.hpp"):
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload, digest):
-    """HBM bytes per decode launch from the committed counter runs, if they were taken on
+def stored_traffic(workload, digest, kernel="decode"):
+    """HBM bytes per launch of `kernel` from the committed counter runs, if they were taken on
     the current kernel sources for this workload; else None."""
+    key = workload if kernel == "decode" else "%s/%s" % (workload, kernel)
     try:
         with open(TRAFFIC_FILE) as fh:
-            rec = json.load(fh).get(workload)
+            rec = json.load(fh).get(key)
     except (OSError, ValueError):
         return None
     if not rec or rec.get("source_digest") != digest:
@@ -199,36 +209,19 @@ def cpu_baseline(batch, min_seconds=1.5):
             "seconds_per_step": dt, "seqs_per_s_per_layer": batch.num_seqs / dt}
 
 
-def main():
-    args = parse_args()
-    if args.gpus != 1:
-        print("bench.py runs on one GPU: this build has no multi-GPU path (--gpus %d requested); "
-              "sequences and KV heads shard across GPUs with no exchange inside attention, so the "
-              "one-GPU figure is the per-GPU figure." % args.gpus, file=sys.stderr)
-        sys.exit(2)
-    if args.layers < 1 or args.steps < 1 or args.warmup < 0:
-        sys.exit("--layers and --steps must be >= 1, --warmup >= 0")
-
+def measure(batch, dev, layers, steps, warmup, partition_size=0):
+    """Fill the pools, time `steps` steps after `warmup` untimed ones, then time each kernel of
+    the step alone; returns the result fields for this workload."""
     import torch
-
-    if not torch.cuda.is_available():
-        sys.exit("bench.py needs a GPU")
-    if args.copy_probe:
-        copy_probe()
-        return
 
     from paged_kv_cache_461_amd import ops
 
-    ops.library()  # fails loudly if the HIP library is missing
-    dev = "cuda:0"
-    torch.cuda.set_device(0)
-    batch = make_batch(args.workload)
     S, Hq, Hkv, D, B = batch.num_seqs, batch.num_heads, batch.num_kv_heads, batch.head_dim, batch.block_size
     print("# workload %s: %d seqs, ctx %d..%d, pool %.1f MB x2 per layer, %d layers" % (
-        batch.name, S, batch.context_lens.min(), batch.context_lens.max(), batch.pool_bytes / 1e6, args.layers),
+        batch.name, S, batch.context_lens.min(), batch.context_lens.max(), batch.pool_bytes / 1e6, layers),
         file=sys.stderr, flush=True)
     t0 = time.time()
-    pools = fill_pools(batch, args.layers, dev)
+    pools = fill_pools(batch, layers, dev)
     print("# pools filled in %.1f s" % (time.time() - t0), file=sys.stderr, flush=True)
 
     # Rows of sequences with more than one query row go to the chunked-prefill call; the
@@ -240,7 +233,7 @@ def main():
     tables = torch.from_numpy(batch.block_tables).to(dev)
     ctx = torch.from_numpy(batch.context_lens).to(dev)
     cu = torch.from_numpy(batch.cu_query_lens).to(dev)
-    P = args.partition_size
+    P = partition_size
     Sd = S - Sp
     dec_max_ctx = int(batch.context_lens[Sp:].max()) if Sd else 0
     ws = ops.decode_workspace(Sd, Hq, Hkv, D, dec_max_ctx, B, P, device=dev) if Sd else None
@@ -276,7 +269,7 @@ def main():
         if Sd:
             decode(i)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
 
@@ -285,11 +278,11 @@ def main():
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     end.record(stream)
     torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / args.steps
+    ms_per_step = start.elapsed_time(end) / steps
 
     # Profiled pass: each kernel of the step launched K times back to back (cycling the layer
     # pools as in the step) between two HIP events on the launch stream; the average is the
@@ -306,26 +299,26 @@ def main():
 
     from paged_kv_cache_461_amd import workloads as W
 
-    kernels = {"kv_write": round(launches(write, args.steps), 2)}
+    kernels = {"kv_write": round(launches(write, steps), 2)}
     if Sp:
-        kernels["chunked_prefill"] = round(launches(prefill, args.steps), 2)
+        kernels["chunked_prefill"] = round(launches(prefill, steps), 2)
     if Sd:
-        kernels["decode_stream"] = round(launches(lambda r: decode(r, 1), args.steps), 2)
-        kernels["decode_merge"] = round(launches(lambda r: decode(args.steps - 1, 2), args.steps), 2)
+        kernels["decode_stream"] = round(launches(lambda r: decode(r, 1), steps), 2)
+        kernels["decode_merge"] = round(launches(lambda r: decode(steps - 1, 2), steps), 2)
     kernels["timing"] = ("K back-to-back launches of each kernel between two HIP events on the launch stream, "
                          "after the timed region")
 
     step_bytes = batch.decode_bytes() + batch.write_bytes()
     value = step_bytes / (ms_per_step * 1e-3) / 1e12
-    digest = source_digest()
+    digest = source_digest("decode")
     eq = W.ELEM_BYTES[batch.q_dtype]
     res = {
         "metric": METRIC,
         "value": round(value, 4),
         "unit": "TB/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -337,7 +330,7 @@ def main():
             "block_size": B, "cache_dtype": {W.BF16: "bf16", W.F32: "f32", W.FP8_E4M3: "fp8_e4m3"}[batch.cache_dtype],
             "context_lens": "seeded, %d..%d, sum %d" % (
                 batch.context_lens.min(), batch.context_lens.max(), int(batch.context_lens.sum())),
-            "num_blocks": batch.num_blocks, "layers_cycled": args.layers,
+            "num_blocks": batch.num_blocks, "layers_cycled": layers,
             "partition_size": "auto (equal chunks per wave)" if P == 0 else P,
         },
         "frac_of_hbm_peak": round(value * 1e3 / HBM_PEAK_GBS, 4),
@@ -364,10 +357,47 @@ def main():
         tflops = flops / (kernels["chunked_prefill"] * 1e-6) / 1e12
         res["roofline_prefill"] = {"bound": "mfma", "kernel": "prefill_kernel (+ merge)",
                                    "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                   "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                                   "algorithmic_flops_per_launch": flops}
+                                   "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                                   "traffic": stored_traffic(batch.name, source_digest("prefill"), "prefill"),
+                                   "algorithmic_flops_per_launch": flops, "source_digest": source_digest("prefill")}
     if "roofline" not in res:
         res["roofline"] = dict(res["roofline_prefill"])
+    return res, stream
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU: this build has no multi-GPU path (--gpus %d requested); "
+              "sequences and KV heads shard across GPUs with no exchange inside attention, so the "
+              "one-GPU figure is the per-GPU figure." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if args.layers < 1 or args.steps < 1 or args.warmup < 0:
+        sys.exit("--layers and --steps must be >= 1, --warmup >= 0")
+
+    import torch
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    from paged_kv_cache_461_amd import ops
+
+    ops.library()  # fails loudly if the HIP library is missing
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    batch = make_batch(args.workload)
+    res, stream = measure(batch, dev, args.layers, args.steps, args.warmup, args.partition_size)
+    if args.extra_workload != "none" and args.extra_workload != args.workload:
+        # The rest of the hot path in the same run: the fp8 cache (in-kernel dequant) and the
+        # chunked-prefill kernel, on the mixed step (one layer, fewer steps).
+        extra = make_batch(args.extra_workload)
+        xres, _ = measure(extra, dev, 1, max(5, args.steps // 5), min(args.warmup, 2))
+        keep = ("value", "unit", "ms_per_step", "steps", "warmup", "config", "seqs_per_s_per_layer", "step_bytes",
+                "kernels_us", "roofline", "roofline_prefill")
+        res["extra_step"] = {k: xres[k] for k in keep if k in xres}
     probe = read_probe(stream)
     res["hbm_read_probe"] = probe
     if res["roofline"]["bound"] == "hbm":
