@@ -7,9 +7,10 @@
 //
 // Work decomposition.  The K/V blocks of every (sequence, kv head) pair -- a "run" -- are
 // laid end to end, sequence-major then kv head, into one list of U units (one unit = one
-// 16-token block of one kv head).  The list is cut into equal chunks of C units and the
-// waves of a persistent grid take chunks w, w + NW, ... (by default C = ceil(U / NW): one
-// chunk per wave, so every wave moves the same number of bytes and the kernel has no tail).
+// 16-token block of one kv head).  The list is cut into chunks of C units and the waves of a
+// persistent grid take one chunk each, or chunks w, w + NW, ... for a caller-given size (by
+// default C = ceil(U / NW): one chunk per wave, so every wave moves the same number of bytes
+// and the kernel has no tail).  Chunk k runs on XCD k mod 8.
 // A chunk that covers runs r1..r2 attends each covered piece of a run on its own (online
 // softmax state reset per piece) and stores the piece's normalised row and (max, sum) as a
 // partial result; a run covered by one piece writes its output row directly.  The merge
@@ -437,6 +438,14 @@ struct Variant {
     static constexpr int kDepth = kQueryInLds ? 3 : 2;
 };
 
+// Chunks of the unit list: chunk k = units [k*C, (k+1)*C).
+struct ChunkMap {
+    int64_t C;
+    __device__ int64_t start(int64_t k) const { return k * C; }
+    __device__ int64_t size(int64_t) const { return C; }
+    __device__ int64_t of_unit(int64_t u) const { return u / C; }
+};
+
 template <int QT, int KT, int D, int G>
 __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(const DecodeArgs a)
 {
@@ -459,14 +468,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(const Dec
     __syncthreads();
 
     // Chunk size: one chunk of ceil(U / NW) units per wave (at least kMinChunkBlocks), or the
-    // caller's chunk size with chunks dealt round-robin to the waves.
-    int64_t C = 0;
+    // caller's chunk size with chunks dealt round-robin to the waves.  Workgroups are dealt to
+    // the 8 XCDs round-robin; the wave's first chunk is chosen so that chunk k runs on XCD
+    // k mod 8, which gives every XCD the same mix of sequences, kv heads and block ranges (with
+    // 4 consecutive chunks per workgroup, an XCD would see a fixed part of every run).
+    const int64_t first = (gridDim.x & 7) == 0
+                              ? 8 * kDecodeWaves * (int64_t)(blockIdx.x >> 3) + 8 * wave_in_wg + (blockIdx.x & 7)
+                              : w;
+    ChunkMap cm{};
     const Plan pl = plan_wave(a, lctx, lane, [&](int64_t U) {
-        C = a.chunk_blocks > 0 ? (int64_t)a.chunk_blocks : max((U + NW - 1) / NW, (int64_t)kMinChunkBlocks);
-        return w * C;
+        cm.C = a.chunk_blocks > 0 ? (int64_t)a.chunk_blocks : max((U + NW - 1) / NW, (int64_t)kMinChunkBlocks);
+        return cm.start(first);
     });
     const int64_t U = pl.U;
-    const int64_t nchunks = min((U + C - 1) / C, a.max_chunks);
+    const int64_t nchunks = U > 0 ? min(cm.of_unit(U - 1) + 1, a.max_chunks) : 0;
 
     const unsigned char* kpool = static_cast<const unsigned char*>(a.k_pool) + lane * 16;
     const unsigned char* vpool = static_cast<const unsigned char*>(a.v_pool) + lane * 16;
@@ -474,9 +489,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(const Dec
     const int32_t* tables = a.block_tables;
     const int mbps = a.max_blocks_per_seq;
 
-    for (int64_t k = w; k < nchunks; k += NW) {
-        const int n = (int)min(C, U - k * C);  // blocks of this chunk (>= 1)
-        const Pos p0 = k == w ? pl.p : plan_wave(a, lctx, lane, [&](int64_t) { return k * C; }).p;
+    for (int64_t k = first; k < nchunks; k += NW) {
+        const int n = (int)min(cm.size(k), U - cm.start(k));  // blocks of this chunk (>= 1)
+        const Pos p0 = k == first ? pl.p : plan_wave(a, lctx, lane, [&](int64_t) { return cm.start(k); }).p;
 
         // table cursor: the block whose table entry is fetched next (it stops at the chunk's
         // last block, whose entry then feeds the fill-in loads past the end)
@@ -546,7 +561,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(const Dec
             if (first && lane == 0) {
                 // every run with blocks is entered at its block 0 by exactly one wave, which
                 // records the chunk range covering it for the merge
-                const int64_t k_last = (cc.run_start + cc.nbs - 1) / C;
+                const int64_t k_last = cm.of_unit(cc.run_start + cc.nbs - 1);
                 a.run_info[2 * run] = (int32_t)k;
                 a.run_info[2 * run + 1] = (int32_t)(k_last - k + 1);
             }
