@@ -209,8 +209,11 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
     const unsigned char* kpool = static_cast<const unsigned char*>(a.k_pool);
     const unsigned char* vpool = static_cast<const unsigned char*>(a.v_pool);
     const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-    uint4 kr[NCH], vr[NCH];
-    uint32_t okbits = 0;  // bit j: piece j comes from a block that holds tokens of this range
+    // NSET register sets: the loads for iteration it + NSET are in flight while it is computed
+    // (two sets measured no faster than one on the 512-row fp8 chunk, so one)
+    constexpr int NSET = 1;
+    uint4 kr[NSET][NCH], vr[NSET][NCH];
+    uint32_t okbits[NSET] = {};  // bit j: piece j comes from a block that holds tokens of the range
     __shared__ int blk_ok[2][4];  // per buffer: block b of the iteration has a valid table entry
 
     // The block of piece j is the same for all 64 lanes of a wave (a tile is a whole number of
@@ -220,15 +223,16 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
     static_assert(CH_PER_TILE % 64 == 0, "wave-uniform block per piece");
     const int last_blk = kstop > 0 ? (kstop - 1) >> 4 : 0;
     int ent[NCH];
-    auto fetch_entries = [&](int kbase) {
+    auto fetch_entries = [&](int kbase) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < NCH; j++) {
             const int b = __builtin_amdgcn_readfirstlane((tid + kPrefillThreads * j) / CH_PER_TILE);
             ent[j] = table[min((kbase >> 4) + b, last_blk)];
         }
     };
-    auto load = [&](int kbase) {
-        okbits = 0;
+    auto load = [&](auto set_tag, int kbase) __attribute__((always_inline)) {
+        constexpr int SET = decltype(set_tag)::value;
+        okbits[SET] = 0;
 #pragma unroll
         for (int j = 0; j < NCH; j++) {
             const int c = tid + kPrefillThreads * j;
@@ -238,21 +242,22 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
             const bool ok = kbase + 16 * b < kstop && phys >= 0 && (int64_t)phys < a.num_blocks;
             // a block with no valid entry still reads block 0 (the pool has one); store() zeroes it
             const int64_t base = ((int64_t)(ok ? phys : 0) * a.num_kv_heads + g) * TILE_BYTES + off;
-            kr[j] = load16(kpool + base);
-            vr[j] = load16(vpool + base);
-            okbits |= ok ? 1u << j : 0u;
+            kr[SET][j] = load16(kpool + base);
+            vr[SET][j] = load16(vpool + base);
+            okbits[SET] |= ok ? 1u << j : 0u;
         }
         fetch_entries(kbase + kPfKeys);  // for the next load, one compute phase away
     };
 
     // Convert and place piece j.  MASK: zero tokens at or past nval of the piece's block (the
     // range end, or the whole block when its table entry is invalid).
-    auto put = [&](auto mask_tag, int j, __bf16* kl, __bf16* vl, int buf, int kbase) {
+    auto put = [&](auto mask_tag, auto set_tag, int j, __bf16* kl, __bf16* vl, int buf, int kbase) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
+        constexpr int SET = decltype(set_tag)::value;
         const int c = tid + kPrefillThreads * j;
         const int b = c / CH_PER_TILE;
         const int off = (c % CH_PER_TILE) * 16;
-        const bool blk = okbits >> j & 1u;
+        const bool blk = okbits[SET] >> j & 1u;
         if (off == 0) blk_ok[buf][b] = blk;  // one piece per block starts it
         const int nval = MASK ? (blk ? min(kstop - (kbase + 16 * b), 16) : 0) : 16;  // valid tokens
         // K: 64-byte channel slices, token-major: a piece is 16 bytes of one token
@@ -262,7 +267,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
         const bool kzero = MASK && tok >= nval;
         if constexpr (KT == kFP8) {
             const int c8 = (64 * slice + (off & 63)) >> 3;
-            const uint4 w = kr[j];
+            const uint4 w = kr[SET][j];
             u32x4_t lo = {e4m3x2_to_bf16x2<false>(w.x), e4m3x2_to_bf16x2<true>(w.x), e4m3x2_to_bf16x2<false>(w.y),
                           e4m3x2_to_bf16x2<true>(w.y)};
             u32x4_t hi = {e4m3x2_to_bf16x2<false>(w.z), e4m3x2_to_bf16x2<true>(w.z), e4m3x2_to_bf16x2<false>(w.w),
@@ -272,7 +277,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
             *reinterpret_cast<u32x4_t*>(krow + 8 * k_pos_of_chunk<KT, D>(c8 + 1)) = hi;
             // V: 16 tokens of channel d side by side
             const int d = off >> 4;
-            const uint4 v = vr[j];
+            const uint4 v = vr[SET][j];
             u32x4_t vlo = {e4m3x2_to_bf16x2<false>(v.x), e4m3x2_to_bf16x2<true>(v.x), e4m3x2_to_bf16x2<false>(v.y),
                            e4m3x2_to_bf16x2<true>(v.y)};
             u32x4_t vhi = {e4m3x2_to_bf16x2<false>(v.z), e4m3x2_to_bf16x2<true>(v.z), e4m3x2_to_bf16x2<false>(v.w),
@@ -285,39 +290,36 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
             *reinterpret_cast<u32x4_t*>(vl + d * L::VS + 16 * b + 8) = vhi;
         } else {
             const int c8 = (32 * slice + ((off & 63) >> 1)) >> 3;
-            u32x4_t k = __builtin_bit_cast(u32x4_t, kr[j]);
+            u32x4_t k = __builtin_bit_cast(u32x4_t, kr[SET][j]);
             if (kzero) k = u32x4_t{0, 0, 0, 0};
             *reinterpret_cast<u32x4_t*>(krow + 8 * k_pos_of_chunk<KT, D>(c8)) = k;
             // V: groups of 8 tokens, channel-major
             const int gi = off >> 4;
             const int og = gi / D, d = gi % D;
-            u32x4_t v = __builtin_bit_cast(u32x4_t, vr[j]);
+            u32x4_t v = __builtin_bit_cast(u32x4_t, vr[SET][j]);
             if constexpr (MASK) v = keep_bf16(v, nval - 8 * og);
             *reinterpret_cast<u32x4_t*>(vl + d * L::VS + 16 * b + 8 * og) = v;
         }
     };
-    auto store = [&](int buf, int kbase) {
+    auto store = [&](auto set_tag, int buf, int kbase) __attribute__((always_inline)) {
+        constexpr int SET = decltype(set_tag)::value;
         __bf16* kl = lds + buf * L::STAGE;
         __bf16* vl = kl + L::K_ELEMS;
         // all four blocks valid and inside the range: no token to zero (wave-uniform)
-        if (kbase + kPfKeys <= kstop && okbits == (1u << NCH) - 1) {
+        if (kbase + kPfKeys <= kstop && okbits[SET] == (1u << NCH) - 1) {
 #pragma unroll
-            for (int j = 0; j < NCH; j++) put(std::false_type{}, j, kl, vl, buf, kbase);
+            for (int j = 0; j < NCH; j++) put(std::false_type{}, set_tag, j, kl, vl, buf, kbase);
         } else {
 #pragma unroll
-            for (int j = 0; j < NCH; j++) put(std::true_type{}, j, kl, vl, buf, kbase);
+            for (int j = 0; j < NCH; j++) put(std::true_type{}, set_tag, j, kl, vl, buf, kbase);
         }
     };
 
-    int kbase = kbeg;
-    fetch_entries(kbase);
-    if (niter > 0) load(kbase);
-    for (int it = 0; it < niter; ++it, kbase += kPfKeys) {
-        const int buf = it & 1;
-        store(buf, kbase);
-        __syncthreads();
-        if (it + 1 < niter) load(kbase + kPfKeys);
-        if (kbase > pw_max) continue;  // every row of this wave is done (uniform)
+    // Iteration it: stage set it % NSET into LDS buffer it % 2, barrier, issue the loads of
+    // iteration it + NSET into the freed set (unconditionally: past the range they read block 0
+    // and are never stored), then compute on the buffer.
+    auto compute = [&](int buf, int kbase) __attribute__((always_inline)) {
+        if (kbase > pw_max) return;  // every row of this wave is done (uniform)
         // keys of block grp that have no valid table entry are masked like causal ones
         const bool blk_valid = blk_ok[buf][grp] != 0;
         const bool need_mask = kbase + kPfKeys - 1 > kw_min || __builtin_amdgcn_ballot_w64(!blk_valid) != 0;
@@ -332,7 +334,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
         for (int r = 0; r < R; r++)
 #pragma unroll
             for (int u = 0; u < 4; u++) sacc[r][u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        auto kread = [&](int i) {
+        auto kread = [&](int i) __attribute__((always_inline)) {
             return *reinterpret_cast<const bf16x8_t*>(kl + (16 * (i & 3) + col) * L::KS + 32 * (i >> 2) + 8 * grp);
         };
         {
@@ -408,7 +410,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
 
         // O^T += V^T P^T: V^T rows = channels, k = keys 16*grp + 8*h2 + 0..7; fragment
         // i = (half i / ND, channel tile i % ND), read kRing ahead.
-        auto vread = [&](int i) {
+        auto vread = [&](int i) __attribute__((always_inline)) {
             return *reinterpret_cast<const bf16x8_t*>(vl + (16 * (i % ND) + col) * L::VS + 16 * grp + 8 * (i / ND));
         };
         {
@@ -423,6 +425,23 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
             }
             ring_schedule<2 * ND, R>();
         }
+    };
+    auto iteration = [&](auto set_tag, int it) __attribute__((always_inline)) {
+        const int kbase = kbeg + it * kPfKeys;
+        store(set_tag, it & 1, kbase);
+        __syncthreads();
+        load(set_tag, kbase + NSET * kPfKeys);
+        compute(it & 1, kbase);
+    };
+    fetch_entries(kbeg);
+    if (niter > 0) {
+        load(std::integral_constant<int, 0>{}, kbeg);
+        if constexpr (NSET > 1) load(std::integral_constant<int, 1>{}, kbeg + kPfKeys);
+    }
+    for (int it = 0; it < niter; it += NSET) {
+        iteration(std::integral_constant<int, 0>{}, it);
+        if constexpr (NSET > 1)
+            if (it + 1 < niter) iteration(std::integral_constant<int, 1>{}, it + 1);
     }
 
     // ---- epilogue: lane holds channels 16d + 4*grp + 0..3 of its row
