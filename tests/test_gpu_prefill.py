@@ -130,3 +130,20 @@ def test_empty_sequences_and_rows_are_skipped():
     b = W.build_batch([50, 80, 30], num_heads=8, num_kv_heads=2, head_dim=64, q_dtype=W.BF16, cache_dtype=W.BF16,
                       seed=4, query_lens=[0, 20, 0])
     prefill_and_compare(b)
+
+
+def test_rows_before_the_context_start_are_zero():
+    """q_len above the context length (outside the contract): rows whose position would be
+    negative get zeros, the others attend over the positions that exist (as the oracle)."""
+    b = W.build_batch([8], num_heads=8, num_kv_heads=2, head_dim=64, q_dtype=W.BF16, cache_dtype=W.BF16,
+                      seed=12, query_lens=[8])
+    kp_h, vp_h = oracle_pool(b, include_new=True)
+    db = DeviceBatch(b)
+    db.ctx = torch.tensor([5], dtype=torch.int32, device="cuda")
+    out = db.prefill(to_dev(kp_h, b.cache_dtype), to_dev(vp_h, b.cache_dtype))
+    ref = oracle.paged_attention(b.query_raw(), b.q_dtype, kp_h, vp_h, b.cache_dtype, b.block_tables,
+                                 np.array([5], dtype=np.int32), b.num_heads, b.num_kv_heads, b.head_dim,
+                                 b.block_size, b.scale, cu_query_lens=b.cu_query_lens)
+    got = out_to_f64(out)
+    assert np.all(got[:3] == 0.0)
+    assert_close(b, got, ref)
