@@ -24,7 +24,8 @@ def lib():
 
 
 def declared_symbols():
-    text = open(HEADER).read()
+    with open(HEADER) as fh:
+        text = fh.read()
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(pa_\w+)\s*\(", text, re.M)))
 
 

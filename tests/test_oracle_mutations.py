@@ -16,7 +16,8 @@ import oracle
 from paged_kv_cache_461_amd import workloads as W
 from tests import test_oracle_pins as pins
 
-SRC = open(os.path.join(os.path.dirname(oracle.__file__), "pa_oracle.c")).read()
+with open(os.path.join(os.path.dirname(oracle.__file__), "pa_oracle.c")) as _fh:
+    SRC = _fh.read()
 
 MUTANTS = {
     "gqa_map_modulo": ("const int g = h / G;", "const int g = h % J->hkv;"),
