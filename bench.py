@@ -56,6 +56,8 @@ def parse_args():
     p.add_argument("--extra-workload", default="fp8_chunked_prefill",
                    choices=["none", "fp8_chunked_prefill", "llama3_8b_decode", "long_context", "mixed_continuous_batch"],
                    help="second workload measured in the same run and reported under extra_step")
+    p.add_argument("--fused-append", action="store_true",
+                   help="decode rows append their new token inside the decode call (pa_paged_attention_decode_append)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device copy (HBM counter calibration) and exit")
@@ -209,9 +211,11 @@ def cpu_baseline(batch, min_seconds=1.5):
             "seconds_per_step": dt, "seqs_per_s_per_layer": batch.num_seqs / dt}
 
 
-def measure(batch, dev, layers, steps, warmup, partition_size=0):
+def measure(batch, dev, layers, steps, warmup, partition_size=0, fused=False):
     """Fill the pools, time `steps` steps after `warmup` untimed ones, then time each kernel of
-    the step alone; returns the result fields for this workload."""
+    the step alone; returns the result fields for this workload.  fused: decode rows append
+    their new token inside the decode call (pa_paged_attention_decode_append); otherwise every
+    new row goes through pa_kv_cache_write first."""
     import torch
 
     from paged_kv_cache_461_amd import ops
@@ -243,10 +247,14 @@ def measure(batch, dev, layers, steps, warmup, partition_size=0):
     outs = [torch.empty_like(p[3]) for p in pools]
     stream = torch.cuda.current_stream()
 
+    # rows appended by pa_kv_cache_write: all of them, or only the chunk rows when the decode
+    # call appends its own
+    Rw = Rp if (fused and Sd) else batch.num_rows
+
     def write(r):
         kp, vp, (nk, nv, nslots), q, ks, vs = pools[r % len(pools)]
-        ops.kv_cache_write(nk, nv, kp, vp, nslots, num_kv_heads=Hkv, head_dim=D, block_size=B, k_scale=ks,
-                           v_scale=vs, stream=stream)
+        ops.kv_cache_write(nk[:Rw], nv[:Rw], kp, vp, nslots[:Rw], num_kv_heads=Hkv, head_dim=D, block_size=B,
+                           k_scale=ks, v_scale=vs, stream=stream)
 
     def prefill(r):
         kp, vp, _, q, ks, vs = pools[r % len(pools)]
@@ -256,14 +264,18 @@ def measure(batch, dev, layers, steps, warmup, partition_size=0):
                                             v_scale=vs, workspace=pf_ws, stream=stream)
 
     def decode(r, phase=3):
-        kp, vp, _, q, ks, vs = pools[r % len(pools)]
-        ops.paged_attention_decode(outs[r % len(pools)][Rp:], q[Rp:], kp, vp, tables[Sp:], ctx[Sp:],
-                                   max_context_len=dec_max_ctx, num_kv_heads=Hkv, scale=batch.scale, block_size=B,
-                                   k_scale=ks, v_scale=vs, partition_size=P, workspace=ws, phase=phase,
-                                   stream=stream)
+        kp, vp, (nk, nv, _), q, ks, vs = pools[r % len(pools)]
+        common = dict(max_context_len=dec_max_ctx, num_kv_heads=Hkv, scale=batch.scale, block_size=B, k_scale=ks,
+                      v_scale=vs, partition_size=P, workspace=ws, phase=phase, stream=stream)
+        if fused:
+            ops.paged_attention_decode_append(outs[r % len(pools)][Rp:], q[Rp:], nk[Rp:].view(Sd, Hkv, D),
+                                              nv[Rp:].view(Sd, Hkv, D), kp, vp, tables[Sp:], ctx[Sp:], **common)
+        else:
+            ops.paged_attention_decode(outs[r % len(pools)][Rp:], q[Rp:], kp, vp, tables[Sp:], ctx[Sp:], **common)
 
     def step(i):
-        write(i)
+        if Rw:
+            write(i)
         if Sp:
             prefill(i)
         if Sd:
@@ -299,14 +311,15 @@ def measure(batch, dev, layers, steps, warmup, partition_size=0):
 
     from paged_kv_cache_461_amd import workloads as W
 
-    kernels = {"kv_write": round(launches(write, steps), 2)}
+    kernels = {"kv_write": round(launches(write, steps), 2)} if Rw else {}
     if Sp:
         kernels["chunked_prefill"] = round(launches(prefill, steps), 2)
     if Sd:
         kernels["decode_stream"] = round(launches(lambda r: decode(r, 1), steps), 2)
         kernels["decode_merge"] = round(launches(lambda r: decode(steps - 1, 2), steps), 2)
     kernels["timing"] = ("K back-to-back launches of each kernel between two HIP events on the launch stream, "
-                         "after the timed region")
+                         "after the timed region" + ("; decode_stream includes the fused append of the decode "
+                                                     "rows' new tokens" if fused and Sd else ""))
 
     step_bytes = batch.decode_bytes() + batch.write_bytes()
     value = step_bytes / (ms_per_step * 1e-3) / 1e12
@@ -332,6 +345,7 @@ def measure(batch, dev, layers, steps, warmup, partition_size=0):
                 batch.context_lens.min(), batch.context_lens.max(), int(batch.context_lens.sum())),
             "num_blocks": batch.num_blocks, "layers_cycled": layers,
             "partition_size": "auto (equal chunks per wave)" if P == 0 else P,
+            "append": "fused into the decode call" if fused and Sd else "pa_kv_cache_write",
         },
         "frac_of_hbm_peak": round(value * 1e3 / HBM_PEAK_GBS, 4),
         "seqs_per_s_per_layer": round(S / (ms_per_step * 1e-3), 1),
@@ -345,6 +359,8 @@ def measure(batch, dev, layers, steps, warmup, partition_size=0):
         dec = dataclasses.replace(batch, context_lens=batch.context_lens[Sp:], query_lens=ql[Sp:],
                                   block_tables=batch.block_tables[Sp:])
         part_bytes = dec.decode_bytes() - dec.num_rows * Hq * D * eq
+        if fused:
+            part_bytes += dec.write_bytes() - 8 * dec.num_rows  # appended rows (no slot ids: the table gives them)
         achieved = part_bytes / (kernels["decode_stream"] * 1e-6) / 1e9
         res["roofline"] = {"bound": "hbm", "kernel": "decode_stream_kernel", "achieved": round(achieved, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -389,12 +405,12 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     batch = make_batch(args.workload)
-    res, stream = measure(batch, dev, args.layers, args.steps, args.warmup, args.partition_size)
+    res, stream = measure(batch, dev, args.layers, args.steps, args.warmup, args.partition_size, args.fused_append)
     if args.extra_workload != "none" and args.extra_workload != args.workload:
         # The rest of the hot path in the same run: the fp8 cache (in-kernel dequant) and the
         # chunked-prefill kernel, on the mixed step (one layer, fewer steps).
         extra = make_batch(args.extra_workload)
-        xres, _ = measure(extra, dev, 1, max(5, args.steps // 5), min(args.warmup, 2))
+        xres, _ = measure(extra, dev, 1, max(5, args.steps // 5), min(args.warmup, 2), 0, args.fused_append)
         keep = ("value", "unit", "ms_per_step", "steps", "warmup", "config", "seqs_per_s_per_layer", "step_bytes",
                 "kernels_us", "roofline", "roofline_prefill")
         res["extra_step"] = {k: xres[k] for k in keep if k in xres}

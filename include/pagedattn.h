@@ -209,6 +209,32 @@ int32_t pa_paged_attention_chunked_prefill(void* out, const void* query, int32_t
                                            int32_t partition_size, void* workspace,
                                            size_t workspace_bytes, void* stream);
 
+/*
+ * Decode with the step's append fused in (one launch instead of pa_kv_cache_write followed by
+ * pa_paged_attention_decode_phase).  Every sequence s with context_lens[s] >= 1 first stores its
+ * new token -- new_key[s] and new_value[s] -- at position context_lens[s] - 1, i.e. slot
+ * block_tables[s][(ctx - 1) / block_size] * block_size + (ctx - 1) % block_size, exactly as
+ * pa_kv_cache_write would (same bytes, including the fp8 encode); then the decode runs as
+ * pa_paged_attention_decode_phase with the same arguments.
+ *   new_key, new_value  device [num_seqs][num_kv_heads][head_dim] in q_dtype (the source dtype
+ *                  of the append), 16-byte aligned.
+ *   k_pool, v_pool device pools, written at the new tokens' slots.
+ * The store is done in phase 1, by the wave that later reads the token's block, so the new
+ * token is attended to in the same call.  A new token's block must not be shared with another
+ * sequence (the same rule as for pa_kv_cache_write's distinct slots).  Other arguments, errors
+ * and the workspace as for pa_paged_attention_decode_phase; phase 2 alone appends nothing.
+ */
+int32_t pa_paged_attention_decode_append(int32_t phase, void* out, const void* query, int32_t q_dtype,
+                                         const void* new_key, const void* new_value, void* k_pool,
+                                         void* v_pool, int64_t num_blocks, int32_t cache_dtype,
+                                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                         const int32_t* context_lens, int32_t max_context_len,
+                                         int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t block_size, float scale,
+                                         const float* k_scale, const float* v_scale,
+                                         int32_t partition_size, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
 /* KV bytes one token occupies over num_layers layers: layers x kv_heads x head_dim x 2 (K and
  * V) x element bytes (page 1, section 2.1: 131072 for 32 x 8 x 128 bf16).  -1 on bad input. */
 int64_t pa_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim,

@@ -256,14 +256,18 @@ int64_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t nu
         .total;
 }
 
-int32_t pa_paged_attention_decode_phase(int32_t phase, void* out, const void* query, int32_t q_dtype,
-                                        const void* k_pool, const void* v_pool, int64_t num_blocks,
-                                        int32_t cache_dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                        const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
-                                        int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                                        int32_t block_size, float scale, const float* k_scale,
-                                        const float* v_scale, int32_t partition_size, void* workspace,
-                                        size_t workspace_bytes, void* stream)
+}  // extern "C"
+
+namespace {
+
+// Decode, with the fused append when new_key is not null.
+int32_t decode_call(int32_t phase, void* out, const void* query, int32_t q_dtype, const void* new_key,
+                    const void* new_value, const void* k_pool, const void* v_pool, int64_t num_blocks,
+                    int32_t cache_dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale, const float* k_scale,
+                    const float* v_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                    void* stream)
 {
     if (phase < 1 || phase > 3) return fail(PA_ERR_INVALID_ARG, "phase %d (1, 2 or 3)", phase);
     int32_t st = check_decode_shape(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
@@ -289,6 +293,10 @@ int32_t pa_paged_attention_decode_phase(int32_t phase, void* out, const void* qu
     if (cache_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale))
         return fail(PA_ERR_INVALID_ARG, "an fp8 cache needs k_scale and v_scale");
     if (!(scale == scale)) return fail(PA_ERR_INVALID_ARG, "scale is NaN");
+    if ((new_key == nullptr) != (new_value == nullptr))
+        return fail(PA_ERR_INVALID_ARG, "new_key and new_value must both be given");
+    if (new_key && (!aligned16(new_key) || !aligned16(new_value)))
+        return fail(PA_ERR_INVALID_ARG, "new_key and new_value must be 16-byte aligned");
     const DecodePlan pl =
         plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len, partition_size);
     if (pl.total > 0) {
@@ -303,8 +311,10 @@ int32_t pa_paged_attention_decode_phase(int32_t phase, void* out, const void* qu
     pa::DecodeArgs a{};
     a.out = out;
     a.query = query;
-    a.k_pool = k_pool;
-    a.v_pool = v_pool;
+    a.k_pool = const_cast<void*>(k_pool);  // written only by the fused append
+    a.v_pool = const_cast<void*>(v_pool);
+    a.new_key = new_key;
+    a.new_value = new_value;
     a.num_blocks = num_blocks;
     a.block_tables = block_tables;
     a.max_blocks_per_seq = max_blocks_per_seq;
@@ -327,6 +337,43 @@ int32_t pa_paged_attention_decode_phase(int32_t phase, void* out, const void* qu
                                      static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(PA_ERR_HIP, "decode launch (phase %d): %s", phase, hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_paged_attention_decode_phase(int32_t phase, void* out, const void* query, int32_t q_dtype,
+                                        const void* k_pool, const void* v_pool, int64_t num_blocks,
+                                        int32_t cache_dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
+                                        int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t block_size, float scale, const float* k_scale,
+                                        const float* v_scale, int32_t partition_size, void* workspace,
+                                        size_t workspace_bytes, void* stream)
+{
+    return decode_call(phase, out, query, q_dtype, nullptr, nullptr, k_pool, v_pool, num_blocks, cache_dtype,
+                       block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_heads,
+                       num_kv_heads, head_dim, block_size, scale, k_scale, v_scale, partition_size, workspace,
+                       workspace_bytes, stream);
+}
+
+int32_t pa_paged_attention_decode_append(int32_t phase, void* out, const void* query, int32_t q_dtype,
+                                         const void* new_key, const void* new_value, void* k_pool, void* v_pool,
+                                         int64_t num_blocks, int32_t cache_dtype, const int32_t* block_tables,
+                                         int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                         int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+                                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                                         const float* k_scale, const float* v_scale, int32_t partition_size,
+                                         void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (num_seqs > 0 && (!new_key || !new_value))
+        return fail(PA_ERR_INVALID_ARG, "null new_key / new_value");
+    return decode_call(phase, out, query, q_dtype, num_seqs > 0 ? new_key : nullptr,
+                       num_seqs > 0 ? new_value : nullptr, k_pool, v_pool, num_blocks, cache_dtype, block_tables,
+                       max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_heads, num_kv_heads,
+                       head_dim, block_size, scale, k_scale, v_scale, partition_size, workspace, workspace_bytes,
+                       stream);
 }
 
 int32_t pa_paged_attention_decode(void* out, const void* query, int32_t q_dtype, const void* k_pool,

@@ -36,6 +36,7 @@
 // attended; all loop bounds are wave-uniform, so the waits on the ring stay counted.
 #include <float.h>
 
+#include "kv_store.hpp"
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
@@ -427,6 +428,54 @@ __device__ __forceinline__ void cursor_next(Cursor& c, const int* lctx, int num_
     c.nbs = nblocks(c.ctx);
 }
 
+// Move the cursor to block 0 of the next run (next kv head, or the next non-empty sequence).
+__device__ __forceinline__ void next_run(Cursor& c, const int* lctx, int num_seqs, int num_kv_heads)
+{
+    c.run_start += c.nbs;
+    c.j = 0;
+    if (++c.g < num_kv_heads) return;
+    c.g = 0;
+    do {
+        ++c.s;
+        c.ctx = c.s < num_seqs ? lctx[c.s] : 0;
+    } while (c.ctx == 0 && c.s < num_seqs);
+    c.nbs = nblocks(c.ctx);
+}
+
+// Fused append: the chunk that holds a run's last block is the only one that reads it, so its
+// wave stores the run's new token (position ctx - 1, source row [s][g] of new_key/new_value)
+// before streaming, with the same piece stores as the append kernel; a workgroup-scope fence
+// then orders those stores before the wave's own loads of the block.  Lanes 0..P-1 store the
+// K row's P 16-byte pieces, lanes P..2P-1 the V row's.
+template <int ST, int CT, int D>
+__device__ __forceinline__ void append_chunk_tokens(const DecodeArgs& a, const int* lctx, const Pos& p0, int64_t u_end,
+                                                    int lane)
+{
+    constexpr int ES = DtypeBytes<ST>::value;
+    constexpr int N = 16 / ES;  // source elements per piece
+    constexpr int P = D / N;    // pieces per source row
+    static_assert(2 * P <= 64, "the K and V rows of a token fit one wave");
+    const int Hkv = a.num_kv_heads, NS = a.num_seqs;
+    Cursor c = cursor_at(p0, lctx);
+    bool stored = false;
+    while (c.s < NS && c.run_start + c.nbs <= u_end) {  // this run ends inside the chunk
+        const int t = c.ctx - 1;
+        const int phys = a.block_tables[(int64_t)c.s * a.max_blocks_per_seq + t / kBlockSize];
+        if (lane < 2 * P && phys >= 0 && (int64_t)phys < a.num_blocks) {
+            const int kv = lane / P, piece = lane % P;
+            const unsigned char* src = static_cast<const unsigned char*>(kv ? a.new_value : a.new_key) +
+                                       (((int64_t)c.s * Hkv + c.g) * D + piece * N) * ES;
+            const int64_t tile = ((int64_t)phys * Hkv + c.g) * kBlockSize * D;
+            unsigned char* pool = static_cast<unsigned char*>(kv ? a.v_pool : a.k_pool);
+            const float sc = CT == kFP8 && ST != CT ? (kv ? a.v_scale : a.k_scale)[c.g] : 1.0f;
+            store_kv_piece<ST, CT>(load16(src), pool, tile, piece * N, t % kBlockSize, kv, D, kBlockSize, sc);
+        }
+        stored = true;
+        next_run(c, lctx, NS, Hkv);
+    }
+    if (stored) __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+}
+
 // ---- the streaming kernel ---------------------------------------------------------------
 
 // Per (cache dtype): where the query lives and how deep the K/V ring is.  Measured on the
@@ -492,6 +541,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(const Dec
     for (int64_t k = first; k < nchunks; k += NW) {
         const int n = (int)min(cm.size(k), U - cm.start(k));  // blocks of this chunk (>= 1)
         const Pos p0 = k == first ? pl.p : plan_wave(a, lctx, lane, [&](int64_t) { return cm.start(k); }).p;
+        if (a.new_key != nullptr) append_chunk_tokens<QT, KT, D>(a, lctx, p0, cm.start(k) + n, lane);
 
         // table cursor: the block whose table entry is fetched next (it stops at the chunk's
         // last block, whose entry then feeds the fill-in loads past the end)

@@ -2,15 +2,9 @@
 //
 // Each decode step produces the new token's K/V and stores it in the cache (page 1,
 // section 1, the prefill/decode diagram); the slot is physical block * block_size + offset
-// from the sequence's block table (page 1, section 4).
-//
-// One thread moves one 16-byte piece of one source row (token, kv head, K or V).  A K piece
-// lands contiguously inside one 64-byte channel slice of the tile; a V piece is spread over
-// its channels' token groups (layout in include/pagedattn.h), so V is written with
-// element-sized stores that touch only this token's bytes.  Same-dtype append copies bits.
-// bf16/fp32 -> OCP E4M3 divides by the head's scale in binary32 (round to nearest even) and
-// converts with v_cvt_pk_fp8_f32 after clamping to +-448 (saturation), NaN handled explicitly.
-#include "pa_device.hpp"
+// from the sequence's block table (page 1, section 4).  One thread moves one 16-byte piece of
+// one source row (token, kv head, K or V); the piece store is kv_store.hpp's.
+#include "kv_store.hpp"
 #include "pa_internal.hpp"
 
 namespace pa {
@@ -44,57 +38,10 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const KvWriteArgs a)
 
     const unsigned char* src = static_cast<const unsigned char*>(kv ? a.value : a.key) +
                                (((tok * Hkv + h) * D) + (int64_t)piece * N) * ES;
-    const uint4 raw = load16(src);
-    const int d0 = piece * N;
-    const int64_t tile = (blk * Hkv + h) * (int64_t)B * D;   // element offset of the tile
-    const int64_t slice = tile + (int64_t)(d0 / W) * B * W;  // element offset of the slice
+    const int64_t tile = (blk * Hkv + h) * (int64_t)B * D;  // element offset of the tile
     unsigned char* pool = static_cast<unsigned char*>(kv ? a.v_pool : a.k_pool);
-
-    uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
-    // V: token group (o / T), channel d, position o % T inside the channel's 16-byte piece
-    const int T = (16 / EC) < B ? (16 / EC) : B;
-    const int64_t vbase = tile + ((int64_t)(o / T) * D + d0) * T + (o % T);
-    if constexpr (ST == CT) {
-        if (kv == 0) {
-            *reinterpret_cast<uint4*>(pool + (slice + (int64_t)o * W + d0 % W) * EC) = raw;
-        } else {
-#pragma unroll
-            for (int i = 0; i < N; i++) {
-                const int64_t e = vbase + (int64_t)i * T;
-                if constexpr (EC == 4)
-                    reinterpret_cast<uint32_t*>(pool)[e] = words[i];
-                else
-                    reinterpret_cast<uint16_t*>(pool)[e] = (uint16_t)(words[i / 2] >> (16 * (i % 2)));
-            }
-        }
-    } else {
-        static_assert(CT == kFP8, "conversions go to E4M3 only");
-        const float sc = (kv ? a.v_scale : a.k_scale)[h];
-        uint32_t codes[N];
-#pragma unroll
-        for (int i = 0; i < N; i++) {
-            float x;
-            if constexpr (ST == kBF16)
-                x = bf16_bits_to_f32((words[i / 2] >> (16 * (i % 2))) & 0xFFFFu);
-            else
-                x = as_float(words[i]);
-            codes[i] = f32_to_e4m3(__fdiv_rn(x, sc));
-        }
-        if (kv == 0) {
-            unsigned char* dst = pool + slice + (int64_t)o * W + d0 % W;
-            if constexpr (N == 8) {
-                uint2 packed;
-                packed.x = codes[0] | codes[1] << 8 | codes[2] << 16 | codes[3] << 24;
-                packed.y = codes[4] | codes[5] << 8 | codes[6] << 16 | codes[7] << 24;
-                *reinterpret_cast<uint2*>(dst) = packed;
-            } else {
-                *reinterpret_cast<uint32_t*>(dst) = codes[0] | codes[1] << 8 | codes[2] << 16 | codes[3] << 24;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < N; i++) pool[vbase + (int64_t)i * T] = (unsigned char)codes[i];
-        }
-    }
+    const float sc = CT == kFP8 && ST != CT ? (kv ? a.v_scale : a.k_scale)[h] : 1.0f;
+    store_kv_piece<ST, CT>(load16(src), pool, tile, piece * N, o, kv, D, B, sc);
 }
 
 template <int ST, int CT>

@@ -33,8 +33,10 @@ constexpr int kMaxDecodeSeqs = 16384;  // context lengths of a call are staged i
 struct DecodeArgs {
     void* out;
     const void* query;
-    const void* k_pool;
-    const void* v_pool;
+    void* k_pool;     // written only by the fused append
+    void* v_pool;
+    const void* new_key;    // fused append: [num_seqs][Hkv][D] rows in the query dtype, or null
+    const void* new_value;
     int64_t num_blocks;
     const int32_t* block_tables;
     int32_t max_blocks_per_seq;

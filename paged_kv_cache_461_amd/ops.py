@@ -27,7 +27,7 @@ EXPORTS = (
     "pa_kv_cache_write", "pa_decode_workspace_size",
     "pa_paged_attention_decode", "pa_paged_attention_decode_phase", "pa_kv_bytes_per_token",
     "pa_pool_bytes", "pa_probe_tile_read", "pa_status_string", "pa_last_error",
-    "pa_chunked_prefill_workspace_size", "pa_paged_attention_chunked_prefill",
+    "pa_chunked_prefill_workspace_size", "pa_paged_attention_chunked_prefill", "pa_paged_attention_decode_append",
 )
 
 
@@ -57,6 +57,8 @@ def library():
         lib.pa_paged_attention_decode.argtypes = dec
         lib.pa_paged_attention_decode_phase.restype = I32
         lib.pa_paged_attention_decode_phase.argtypes = [I32] + dec
+        lib.pa_paged_attention_decode_append.restype = I32
+        lib.pa_paged_attention_decode_append.argtypes = [I32, P, P, I32, P, P] + dec[3:]
         lib.pa_chunked_prefill_workspace_size.restype = I64
         lib.pa_chunked_prefill_workspace_size.argtypes = [I32] * 9
         lib.pa_paged_attention_chunked_prefill.restype = I32
@@ -223,6 +225,37 @@ def paged_attention_chunked_prefill(out, query, cu_query_lens, k_pool, v_pool, b
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(library().pa_paged_attention_chunked_prefill(
         _ptr(out), _ptr(query), dtype_code(query), _ptr(cu_query_lens), rows, int(max_query_len), _ptr(k_pool),
+        _ptr(v_pool), nb, dtype_code(k_pool), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        int(max_context_len), S, Hq, num_kv_heads, D, block_size, float(scale), _ptr(k_scale), _ptr(v_scale),
+        int(partition_size), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def paged_attention_decode_append(out, query, new_key, new_value, k_pool, v_pool, block_tables, context_lens, *,
+                                  max_context_len, num_kv_heads, scale, block_size=16, k_scale=None, v_scale=None,
+                                  partition_size=0, workspace=None, phase=3, stream=None):
+    """Store each sequence's new K/V row at position context_lens[s] - 1, then decode
+    (pa_paged_attention_decode_append).  new_key/new_value: [S][Hkv][D] in the query dtype."""
+    for n, t in (("out", out), ("query", query), ("new_key", new_key), ("new_value", new_value),
+                 ("k_pool", k_pool), ("v_pool", v_pool)):
+        _dev(n, t)
+    _dev("block_tables", block_tables, torch.int32)
+    _dev("context_lens", context_lens, torch.int32)
+    _dev("k_scale", k_scale, torch.float32)
+    _dev("v_scale", v_scale, torch.float32)
+    _dev("workspace", workspace)
+    if query.dim() != 3 or out.shape != query.shape or out.dtype != query.dtype:
+        raise ValueError("query and out must both be [num_seqs][num_heads][head_dim] of one dtype")
+    S, Hq, D = query.shape
+    if new_key.shape != (S, num_kv_heads, D) or new_value.shape != new_key.shape or new_key.dtype != query.dtype \
+            or new_value.dtype != query.dtype:
+        raise ValueError("new_key/new_value must be [%d][%d][%d] in the query dtype" % (S, num_kv_heads, D))
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables must be [num_seqs][max_blocks] and context_lens [num_seqs]")
+    nb = num_pool_blocks(k_pool, num_kv_heads, D, block_size)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().pa_paged_attention_decode_append(
+        int(phase), _ptr(out), _ptr(query), dtype_code(query), _ptr(new_key), _ptr(new_value), _ptr(k_pool),
         _ptr(v_pool), nb, dtype_code(k_pool), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
         int(max_context_len), S, Hq, num_kv_heads, D, block_size, float(scale), _ptr(k_scale), _ptr(v_scale),
         int(partition_size), _ptr(workspace), ws_bytes, _stream(stream)))

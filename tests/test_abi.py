@@ -223,3 +223,31 @@ def test_prefill_workspace_size(lib):
         got = lib.pa_chunked_prefill_workspace_size(rows, S, max_q, Hq, Hkv, D, 16, max_ctx, P)
         assert got == expect(*args), args
     assert lib.pa_chunked_prefill_workspace_size(10, 1, 11, 32, 8, 128, 16, 100, 0) == -1
+
+
+def _fused(lib, **kw):
+    a = dict(phase=3, out=FAKE, query=FAKE, q_dtype=BF16, nk=FAKE, nv=FAKE, k_pool=FAKE, v_pool=FAKE, num_blocks=100,
+             cache_dtype=BF16, block_tables=FAKE, mbps=256, context_lens=FAKE, max_ctx=4096, S=64, Hq=32, Hkv=8,
+             D=128, B=16, scale=0.088, k_scale=None, v_scale=None, P=0, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.pa_paged_attention_decode_append(
+        a["phase"], a["out"], a["query"], a["q_dtype"], a["nk"], a["nv"], a["k_pool"], a["v_pool"], a["num_blocks"],
+        a["cache_dtype"], a["block_tables"], a["mbps"], a["context_lens"], a["max_ctx"], a["S"], a["Hq"], a["Hkv"],
+        a["D"], a["B"], a["scale"], a["k_scale"], a["v_scale"], a["P"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nk=None), ops.PA_ERR_INVALID_ARG),
+    (dict(nv=None), ops.PA_ERR_INVALID_ARG),
+    (dict(nk=FAKE + 8), ops.PA_ERR_INVALID_ARG),
+    (dict(D=96), ops.PA_ERR_UNSUPPORTED),
+    (dict(phase=0), ops.PA_ERR_INVALID_ARG),
+    (dict(ws=None, ws_bytes=0), ops.PA_ERR_WORKSPACE),
+])
+def test_fused_append_rejects_before_launch(lib, kw, status):
+    assert _fused(lib, **kw) == status
+    assert lib.pa_last_error() != b""
+
+
+def test_fused_append_empty_batch_is_ok(lib):
+    assert _fused(lib, S=0, out=None, query=None, nk=None, nv=None) == ops.PA_OK

@@ -11,8 +11,10 @@ import numpy as np
 import pytest
 import torch
 
+from paged_kv_cache_461_amd import ops
 from paged_kv_cache_461_amd import workloads as W
-from tests.gpu_util import (DeviceBatch, assert_close, device_step, oracle_sampled_rows, out_to_f64, to_host_raw)
+from tests.gpu_util import (DeviceBatch, assert_close, device_step, oracle_sampled_rows, out_to_f64, to_dev,
+                            to_host_raw)
 
 pytestmark = pytest.mark.gpu
 
@@ -71,3 +73,27 @@ def test_fp8_chunked_prefill_full():
     picks = [(0, i) for i in (0, 1, 127, 128, 255, 384, 510, 511)]
     picks += [(s, 0) for s in sample_seqs(b)]
     full_step_and_check(b, picks)
+
+
+def test_llama3_8b_decode_full_fused_append():
+    """The fused append + decode call as bench.py times it, at full size."""
+    b = W.llama3_8b_decode()
+    db = DeviceBatch(b)
+    kp, vp = db.empty_pools(poison=False)
+    db.fill_history(kp, vp)
+    k, v, _ = b.new_tokens()
+    shape = (b.num_seqs, b.num_kv_heads, b.head_dim)
+    nk, nv = to_dev(k, b.src_dtype).view(shape), to_dev(v, b.src_dtype).view(shape)
+    out = torch.empty_like(db.query)
+    ws = ops.decode_workspace(b.num_seqs, b.num_heads, b.num_kv_heads, b.head_dim, b.max_context_len, b.block_size)
+    ops.paged_attention_decode_append(out, db.query, nk, nv, kp, vp, db.tables, db.ctx,
+                                      max_context_len=b.max_context_len, num_kv_heads=b.num_kv_heads, scale=b.scale,
+                                      block_size=b.block_size, workspace=ws)
+    picks = [(s, 0) for s in sample_seqs(b)]
+    ref, used, kp_h, vp_h = oracle_sampled_rows(b, picks)
+    tile = b.num_kv_heads * b.block_size * b.head_dim
+    ids = torch.from_numpy(used).cuda()
+    for dev_pool, host_pool in ((kp, kp_h), (vp, vp_h)):
+        got = to_host_raw(dev_pool.view(-1, tile)[ids]).reshape(-1)
+        assert np.array_equal(got.view(np.uint8), host_pool.view(np.uint8))
+    assert_close(b, out_to_f64(out)[[s for s, _ in picks]], ref)
