@@ -7,7 +7,8 @@ product package.  The arithmetic lives in ``pa_oracle.c`` (plain C99, float64, c
 with gcc -O2, no fast-math); this module only builds it and marshals numpy arrays.
 
 Element types are passed as numpy arrays of their raw bits: fp32 as ``float32``, bf16 as
-``uint16`` and OCP fp8 E4M3 as ``uint8``.  Dtype codes: 0 fp32, 1 bf16, 2 fp8 e4m3.
+``uint16`` and OCP fp8 E4M3 / E5M2 as ``uint8``.  Dtype codes: 0 fp32, 1 bf16, 2 fp8 e4m3,
+3 fp8 e5m2.
 
 Pins (tests/test_oracle_*.py check this module against what the pages and mathematics fix):
   * attention == torch scaled_dot_product_attention in float64 on the contiguous
@@ -20,6 +21,7 @@ Pins (tests/test_oracle_*.py check this module against what the pages and mathem
   * E4M3 decode table == torch.float8_e4m3fn for all 256 codes; encode == torch's
     round-to-nearest-even cast wherever that cast does not overflow, saturation to 448
     above it, and round trip on every finite code;
+  * E5M2: the same three pins against torch.float8_e5m2 (saturation at 57344);
   * KV bytes per token == 131072 for 32 layers x 8 kv heads x 128 x bf16.
 """
 from __future__ import annotations
@@ -31,8 +33,8 @@ import threading
 
 import numpy as np
 
-F32, BF16, FP8_E4M3 = 0, 1, 2
-_NP_OF = {F32: np.float32, BF16: np.uint16, FP8_E4M3: np.uint8}
+F32, BF16, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3
+_NP_OF = {F32: np.float32, BF16: np.uint16, FP8_E4M3: np.uint8, FP8_E5M2: np.uint8}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "pa_oracle.c")
@@ -74,6 +76,14 @@ def _bind(lib):
     lib.oracle_e4m3_encode_array.argtypes = [P, P, L]
     lib.oracle_e4m3_decode_array.restype = None
     lib.oracle_e4m3_decode_array.argtypes = [P, P, L]
+    lib.oracle_e5m2_to_double.restype = D
+    lib.oracle_e5m2_to_double.argtypes = [ctypes.c_uint8]
+    lib.oracle_e5m2_encode.restype = ctypes.c_uint8
+    lib.oracle_e5m2_encode.argtypes = [ctypes.c_float]
+    lib.oracle_e5m2_encode_array.restype = None
+    lib.oracle_e5m2_encode_array.argtypes = [P, P, L]
+    lib.oracle_e5m2_decode_array.restype = None
+    lib.oracle_e5m2_decode_array.argtypes = [P, P, L]
     lib.oracle_kv_bytes_per_token.restype = L
     lib.oracle_kv_bytes_per_token.argtypes = [I, I, I, I]
     return lib
@@ -131,6 +141,24 @@ def e4m3_encode(y) -> np.ndarray:
     y = np.ascontiguousarray(y, dtype=np.float32)
     out = np.empty(y.shape, dtype=np.uint8)
     lib.oracle_e4m3_encode_array(_ptr(y), _ptr(out), y.size)
+    return out
+
+
+def e5m2_to_float64(codes) -> np.ndarray:
+    """Value of each E5M2 code (+-inf for S.11111.00, NaN for S.11111.mm with mm != 0)."""
+    lib = _load()
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    lib.oracle_e5m2_decode_array(_ptr(c), _ptr(out), c.size)
+    return out
+
+
+def e5m2_encode(y) -> np.ndarray:
+    """Round binary32 values to E5M2 codes (nearest-even, saturating at +-57344)."""
+    lib = _load()
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.empty(y.shape, dtype=np.uint8)
+    lib.oracle_e5m2_encode_array(_ptr(y), _ptr(out), y.size)
     return out
 
 

@@ -15,7 +15,8 @@
  *     gives 16 tokens as the default block size and says the kernel reads KV block by
  *     block through the table instead of assuming contiguity);
  *   - several query heads share one KV head (GQA)            (page 1, section 10);
- *   - the KV cache may be stored as 8-bit floats, e4m3 preferred over e5m2, with
+ *   - the KV cache may be stored as 8-bit floats, e4m3 preferred over e5m2 (which can drift
+ *     numerically on long sequences), with
  *     per-tensor or per-head scales                          (page 1, section 15; page 2,
  *     "quantisation"; page 3, section 2.4).
  * Each decode step produces the new token's K/V and stores it in the cache, and the new
@@ -43,7 +44,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8_E4M3 = 2 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8_E4M3 = 2, OR_FP8_E5M2 = 3 };
 
 enum {
     OR_OK = 0,
@@ -59,6 +60,7 @@ static int elem_bytes(int dtype)
     case OR_F32: return 4;
     case OR_BF16: return 2;
     case OR_FP8_E4M3: return 1;
+    case OR_FP8_E5M2: return 1;
     default: return 0;
     }
 }
@@ -125,6 +127,41 @@ double oracle_e4m3_to_double(uint8_t c)
     return s ? -v : v;
 }
 
+/* OCP 8-bit float E5M2: 1 sign bit, 5 exponent bits (bias 15), 2 mantissa bits; exponent 0
+ * is subnormal (m * 2^-16); exponent 31 holds the infinities (m = 0) and NaNs (m != 0);
+ * largest finite value 57344. */
+double oracle_e5m2_to_double(uint8_t c)
+{
+    int s = c >> 7, e = (c >> 2) & 31, m = c & 3;
+    double v;
+    if (e == 31)
+        v = m ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)m, -16);
+    else
+        v = ldexp((double)(4 + m), e - 17); /* (1 + m/4) * 2^(e-15) */
+    return s ? -v : v;
+}
+
+/* Nearest code to a (finite, 0 <= a < value(top)) among codes 0..top, ties to the even code
+ * (the code's low bit is the mantissa's low bit).  Codes 0..top are increasing in value. */
+static int nearest_code(double a, int top, double (*value)(uint8_t))
+{
+    int lo = 0, hi = top; /* invariant: value(lo) <= a < value(hi) */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (value((uint8_t)mid) <= a)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    double dlo = a - value((uint8_t)lo); /* exact: both have few bits */
+    double dhi = value((uint8_t)hi) - a;
+    if (dlo < dhi) return lo;
+    if (dhi < dlo) return hi;
+    return (lo % 2 == 0) ? lo : hi;
+}
+
 /* Round a binary32 value to E4M3 with round-to-nearest-even, saturating finite
  * magnitudes above the largest finite value (448) to +-448; NaN keeps its sign bit and
  * maps to S.1111.111.  Found by comparing |y| against the sorted table of the 127
@@ -135,26 +172,22 @@ uint8_t oracle_e4m3_encode(float y)
     if (isnan(y)) return sign | 0x7f;
     double a = fabs((double)y);
     if (a >= 448.0) return sign | 0x7e;
-    /* largest code lo in [0, 125] with value(lo) <= a (binary search over codes) */
-    int lo = 0, hi = 126; /* invariant: value(lo) <= a < value(hi) */
-    while (hi - lo > 1) {
-        int mid = (lo + hi) / 2;
-        if (oracle_e4m3_to_double((uint8_t)mid) <= a)
-            lo = mid;
-        else
-            hi = mid;
-    }
-    double dlo = a - oracle_e4m3_to_double((uint8_t)lo); /* exact: both have few bits */
-    double dhi = oracle_e4m3_to_double((uint8_t)hi) - a;
-    int code;
-    if (dlo < dhi)
-        code = lo;
-    else if (dhi < dlo)
-        code = hi;
-    else
-        code = (lo % 2 == 0) ? lo : hi; /* tie: even mantissa (code parity = mantissa LSB) */
-    return sign | (uint8_t)code;
+    return sign | (uint8_t)nearest_code(a, 0x7e, oracle_e4m3_to_double);
 }
+
+/* The same rule for E5M2: round to nearest even, finite magnitudes (and infinities) at or
+ * above the largest finite value saturate to +-57344 (S.11110.11), NaN keeps its sign and
+ * maps to S.11111.11. */
+uint8_t oracle_e5m2_encode(float y)
+{
+    uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    if (isnan(y)) return sign | 0x7f;
+    double a = fabs((double)y);
+    if (a >= 57344.0) return sign | 0x7b;
+    return sign | (uint8_t)nearest_code(a, 0x7b, oracle_e5m2_to_double);
+}
+
+static int is_fp8(int dtype) { return dtype == OR_FP8_E4M3 || dtype == OR_FP8_E5M2; }
 
 static double load_elem(const unsigned char* base, int64_t idx, int dtype)
 {
@@ -166,6 +199,7 @@ static double load_elem(const unsigned char* base, int64_t idx, int dtype)
         return bf16_bits_to_double(b);
     }
     case OR_FP8_E4M3: return oracle_e4m3_to_double(base[idx]);
+    case OR_FP8_E5M2: return oracle_e5m2_to_double(base[idx]);
     default: return NAN;
     }
 }
@@ -174,9 +208,9 @@ static double load_elem(const unsigned char* base, int64_t idx, int dtype)
 
 /* For every token i with slot_mapping[i] >= 0 the token goes to physical block
  * slot / block_size at offset slot % block_size, for every kv head and channel.  Same
- * source and cache dtype: the element's bits are copied.  fp32/bf16 source into an E4M3
- * cache: the stored code is e4m3(fl32(x / scale[h])) -- one IEEE binary32 division by that
- * head's scale, then the rounding above. */
+ * source and cache dtype: the element's bits are copied.  fp32/bf16 source into an E4M3 (E5M2)
+ * cache: the stored code is e4m3(fl32(x / scale[h])) (e5m2(...)) -- one IEEE binary32 division
+ * by that head's scale, then the rounding above. */
 int oracle_kv_cache_write(const void* key, const void* value, int src_dtype,
                           void* k_pool, void* v_pool, int cache_dtype, int64_t num_blocks,
                           const int64_t* slot_mapping, int64_t num_tokens,
@@ -185,9 +219,9 @@ int oracle_kv_cache_write(const void* key, const void* value, int src_dtype,
 {
     int es = elem_bytes(src_dtype), ec = elem_bytes(cache_dtype);
     if (!es || !ec) return OR_ERR_DTYPE;
-    if (src_dtype == OR_FP8_E4M3) return OR_ERR_DTYPE;
-    if (src_dtype != cache_dtype && cache_dtype != OR_FP8_E4M3) return OR_ERR_DTYPE;
-    if (cache_dtype == OR_FP8_E4M3 && (!k_scale || !v_scale)) return OR_ERR_ARG;
+    if (is_fp8(src_dtype)) return OR_ERR_DTYPE;
+    if (src_dtype != cache_dtype && !is_fp8(cache_dtype)) return OR_ERR_DTYPE;
+    if (is_fp8(cache_dtype) && (!k_scale || !v_scale)) return OR_ERR_ARG;
     if (!layout_ok(head_dim, block_size, cache_dtype)) return OR_ERR_ARG;
     const unsigned char* src[2] = {(const unsigned char*)key, (const unsigned char*)value};
     unsigned char* dst[2] = {(unsigned char*)k_pool, (unsigned char*)v_pool};
@@ -217,7 +251,7 @@ int oracle_kv_cache_write(const void* key, const void* value, int src_dtype,
                             x = (float)bf16_bits_to_double(bb);
                         }
                         float y = x / scl[kv][h]; /* binary32 division, round to nearest */
-                        dst[kv][di] = oracle_e4m3_encode(y);
+                        dst[kv][di] = cache_dtype == OR_FP8_E4M3 ? oracle_e4m3_encode(y) : oracle_e5m2_encode(y);
                     }
                 }
             }
@@ -262,7 +296,7 @@ static int attend_row(const job_t* J, int s, int64_t row, int i, int q_len, int 
     if (n <= 0) return OR_OK;
     if ((n + B - 1) / B > J->mbps) return OR_ERR_BOUNDS;
     double ks = 1.0, vs = 1.0;
-    if (J->cache_dtype == OR_FP8_E4M3) {
+    if (is_fp8(J->cache_dtype)) {
         ks = (double)J->k_scale[g];
         vs = (double)J->v_scale[g];
     }
@@ -345,10 +379,10 @@ int oracle_paged_attention(double* out, const void* query, int q_dtype,
                            int num_heads, int num_kv_heads, int head_dim, int block_size,
                            double scale, const float* k_scale, const float* v_scale, int nthreads)
 {
-    if (!elem_bytes(q_dtype) || q_dtype == OR_FP8_E4M3 || !elem_bytes(cache_dtype)) return OR_ERR_DTYPE;
+    if (!elem_bytes(q_dtype) || is_fp8(q_dtype) || !elem_bytes(cache_dtype)) return OR_ERR_DTYPE;
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads) return OR_ERR_ARG;
     if (!layout_ok(head_dim, block_size, cache_dtype)) return OR_ERR_ARG;
-    if (cache_dtype == OR_FP8_E4M3 && (!k_scale || !v_scale)) return OR_ERR_ARG;
+    if (is_fp8(cache_dtype) && (!k_scale || !v_scale)) return OR_ERR_ARG;
     if (num_seqs == 0) return OR_OK;
     for (int s = 0; s < num_seqs; s++)
         if (cu_q[s + 1] < cu_q[s]) return OR_ERR_ARG;
@@ -408,4 +442,14 @@ void oracle_e4m3_encode_array(const float* y, uint8_t* codes, int64_t n)
 void oracle_e4m3_decode_array(const uint8_t* codes, double* out, int64_t n)
 {
     for (int64_t i = 0; i < n; i++) out[i] = oracle_e4m3_to_double(codes[i]);
+}
+
+void oracle_e5m2_encode_array(const float* y, uint8_t* codes, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) codes[i] = oracle_e5m2_encode(y[i]);
+}
+
+void oracle_e5m2_decode_array(const uint8_t* codes, double* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = oracle_e5m2_to_double(codes[i]);
 }

@@ -28,9 +28,17 @@ MUTANTS = {
     "v_scale_dropped": ("(vs * load_elem(J->vp", "(1.0 * load_elem(J->vp"),
     "k_scale_dropped": ("(ks * load_elem(J->kp", "(1.0 * load_elem(J->kp"),
     "write_slot_offset": ("int o = (int)(slot % block_size);", "int o = (int)(slot % block_size) ^ 1;"),
-    "e4m3_tie_away": ("code = (lo % 2 == 0) ? lo : hi;", "code = hi;"),
+    "fp8_tie_away": ("    return (lo % 2 == 0) ? lo : hi;", "    return hi;"),
     "e4m3_subnormal_scale": ("v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
     "e4m3_no_saturation": ("if (a >= 448.0) return sign | 0x7e;", "if (a >= 464.0) return sign | 0x7f;"),
+    "e5m2_subnormal_scale": ("v = ldexp((double)m, -16);", "v = ldexp((double)m, -15);"),
+    "e5m2_bias_off_by_one": ("v = ldexp((double)(4 + m), e - 17);", "v = ldexp((double)(4 + m), e - 16);"),
+    "e5m2_inf_read_as_nan": ("v = m ? NAN : INFINITY;", "v = NAN;"),
+    "e5m2_no_saturation": ("if (a >= 57344.0) return sign | 0x7b;", "if (a >= 61440.0) return sign | 0x7c;"),
+    "e5m2_cache_encoded_as_e4m3": ("cache_dtype == OR_FP8_E4M3 ? oracle_e4m3_encode(y) : oracle_e5m2_encode(y)",
+                                   "oracle_e4m3_encode(y)"),
+    "e5m2_cache_read_as_e4m3": ("case OR_FP8_E5M2: return oracle_e5m2_to_double(base[idx]);",
+                                "case OR_FP8_E5M2: return oracle_e4m3_to_double(base[idx]);"),
     "fp8_multiply_not_divide": ("float y = x / scl[kv][h];", "float y = x * scl[kv][h];"),
     "softmax_denominator_dropped": ("for (int dd = 0; dd < D; dd++) out[dd] /= den;", ""),
     "kv_bytes_missing_factor_2": ("head_dim * 2 * elem_bytes(dtype)", "head_dim * elem_bytes(dtype)"),
@@ -46,6 +54,10 @@ def _checks():
     yield lambda: pins.test_e4m3_decode_table_matches_torch()
     yield lambda: pins.test_e4m3_encode_matches_torch_rne(0.0103125)
     yield lambda: pins.test_e4m3_round_trip_and_ties()
+    yield lambda: pins.test_decode_equals_sdpa(pins.CASES[7])
+    yield lambda: pins.test_e5m2_decode_table_matches_torch()
+    yield lambda: pins.test_e5m2_encode_matches_torch_rne(8.7e-5)
+    yield lambda: pins.test_e5m2_round_trip_and_ties()
     yield lambda: pins.test_kv_size_closed_forms()
 
 

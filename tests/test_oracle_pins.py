@@ -6,7 +6,8 @@
 * exact invariance under relabelling physical blocks, and the pages' worked block map
   (page 1, section 4);
 * closed-form special cases of softmax attention;
-* the OCP E4M3 codec against torch.float8_e4m3fn and its defining constants;
+* the OCP E4M3 and E5M2 codecs against torch.float8_e4m3fn / torch.float8_e5m2 and their
+  defining constants;
 * the KV-size closed forms (page 1, section 2.1; page 3, section 2.1).
 """
 import json
@@ -48,17 +49,22 @@ def run_oracle(batch, kp, vp, **kw):
                                   cu_query_lens=cu, k_scale=batch.k_scale, v_scale=batch.v_scale, **kw)
 
 
+FP8_CODEC = {W.FP8_E4M3: (oracle.e4m3_encode, oracle.e4m3_to_float64),
+             W.FP8_E5M2: (oracle.e5m2_encode, oracle.e5m2_to_float64)}
+
+
 def stored_values(batch, s):
     """float64 K, V of sequence s as the cache holds them ([ctx][Hkv][D]), computed without
-    the oracle's layout: fp32/bf16 rows are stored exactly; fp8 rows are the E4M3 code of
-    fl32(x / scale) times the scale."""
+    the oracle's layout: fp32/bf16 rows are stored exactly; fp8 rows are the E4M3 (E5M2) code
+    of fl32(x / scale) times the scale."""
     k, v = batch.token_values(s)
     k, v = k.astype(np.float64), v.astype(np.float64)
-    if batch.cache_dtype == W.FP8_E4M3:
+    if batch.cache_dtype in FP8_CODEC:
+        encode, decode = FP8_CODEC[batch.cache_dtype]
         out = []
         for x, sc in ((k, batch.k_scale), (v, batch.v_scale)):
             y = (x.astype(np.float32) / sc[None, :, None]).astype(np.float32)
-            out.append(oracle.e4m3_to_float64(oracle.e4m3_encode(y)) * sc[None, :, None].astype(np.float64))
+            out.append(decode(encode(y)) * sc[None, :, None].astype(np.float64))
         k, v = out
     return k, v
 
@@ -95,6 +101,8 @@ CASES = [
     ([300, 129], 32, 8, 128, 16, W.BF16, W.BF16),
     ([50, 130, 7], 8, 2, 128, 16, W.BF16, W.FP8_E4M3),
     ([33, 18], 4, 1, 64, 16, W.F32, W.FP8_E4M3),
+    ([70, 3, 129], 8, 2, 128, 16, W.BF16, W.FP8_E5M2),
+    ([21, 48], 4, 2, 64, 16, W.F32, W.FP8_E5M2),
 ]
 
 
@@ -336,6 +344,57 @@ def test_e4m3_round_trip_and_ties():
     mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
     got = oracle.e4m3_encode(mids)
     want = np.where(np.arange(126) % 2 == 0, np.arange(126), np.arange(1, 127)).astype(np.uint8)
+    assert np.array_equal(got, want)
+
+
+# ---- E5M2 codec ----------------------------------------------------------------------------------
+
+def test_e5m2_decode_table_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e5m2_to_float64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e5m2).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok])
+    # defining constants of OCP E5M2: bias 15, two mantissa bits, IEEE-style specials
+    assert ours[0x7B] == 57344.0 and ours[0x04] == 2.0 ** -14 and ours[0x01] == 2.0 ** -16
+    assert ours[0x3C] == 1.0 and ours[0x7C] == np.inf and ours[0xFC] == -np.inf
+    assert np.isnan(ours[0x7D]) and np.isnan(ours[0x7F]) and np.isnan(ours[0xFF])
+    assert np.signbit(ours[0x80]) and ours[0x80] == 0.0
+    # every E5M2 value is the top byte of a binary16 value (same exponent field and bias)
+    half = torch.from_numpy((codes.astype(np.uint16) << 8).view(np.int16)).view(torch.float16)
+    h = half.to(torch.float64).numpy()
+    assert np.array_equal(ours[ok], h[ok])
+
+
+@pytest.mark.parametrize("scale", [1.0, 8.7e-5, 3.0, 1.0 / 57344.0, 2.0 ** -20])
+def test_e5m2_encode_matches_torch_rne(scale):
+    x = _all_bf16_as_f32()
+    with np.errstate(over="ignore", invalid="ignore"):  # inf / NaN inputs are part of the sweep
+        y = (x / np.float32(scale)).astype(np.float32)
+    ours = oracle.e5m2_encode(y)
+    ref = torch.from_numpy(y).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    inrange = np.abs(y) < 61440.0       # torch rounds to inf from the 57344/65536 midpoint up
+    finite = np.isfinite(y)
+    sel = inrange & finite
+    assert np.array_equal(ours[sel], ref[sel])
+    big = finite & ~inrange
+    assert np.all(ours[big] == np.where(np.signbit(y[big]), 0xFB, 0x7B))
+    nan = np.isnan(y)
+    assert np.all((ours[nan] & 0x7F) == 0x7F)
+    inf = np.isinf(y)
+    assert np.all(ours[inf] == np.where(np.signbit(y[inf]), 0xFB, 0x7B))
+
+
+def test_e5m2_round_trip_and_ties():
+    codes = np.array([c for c in range(256) if (c & 0x7F) < 0x7C], dtype=np.uint8)
+    vals = oracle.e5m2_to_float64(codes).astype(np.float32)
+    assert np.array_equal(oracle.e5m2_encode(vals), codes)
+    pos = oracle.e5m2_to_float64(np.arange(0x7C, dtype=np.uint8))
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    got = oracle.e5m2_encode(mids)
+    n = 0x7B
+    want = np.where(np.arange(n) % 2 == 0, np.arange(n), np.arange(1, n + 1)).astype(np.uint8)
     assert np.array_equal(got, want)
 
 
