@@ -14,8 +14,10 @@
  *   - several query heads share one KV head (grouped-query attention; page 1, section 10);
  *   - each decode step writes the new token's K and V into its block slot before attending
  *     (page 1, section 1, the prefill/decode diagram);
- *   - the cache may be stored as 8-bit E4M3 floats with per-head scales (page 1, section 15;
- *     page 2, quantisation; page 3, section 2.4);
+ *   - the cache may be stored as 8-bit floats, E4M3 or E5M2, with per-head scales (page 1,
+ *     section 15; page 2, quantisation, which also names per-tensor scales -- pass one value
+ *     repeated per head; page 3, section 2.4, which prefers E4M3 because E5M2 can drift on
+ *     long sequences);
  *   - a long prompt may be processed in chunks that run alongside decode rows (page 1,
  *     section 12; page 3, section 2.3).
  *
@@ -38,7 +40,9 @@
  *   - Functions are stateless and may be called from several host threads at once.
  *
  * Element types (pa_dtype):  PA_F32 IEEE binary32; PA_BF16 bfloat16; PA_FP8_E4M3 the OCP
- * 8-bit float E4M3 (bias 7, no infinities, S.1111.111 = NaN, largest finite 448).
+ * 8-bit float E4M3 (bias 7, no infinities, S.1111.111 = NaN, largest finite 448);
+ * PA_FP8_E5M2 the OCP 8-bit float E5M2 (bias 15, S.11111.00 = +-inf, S.11111.mm with mm != 0
+ * = NaN, largest finite 57344).
  *
  * Pool layout.  k_pool and v_pool are each [num_blocks][num_kv_heads][block_size*head_dim]
  * elements of cache_dtype.  With e = element bytes, W = 64/e and T = min(16/e, block_size),
@@ -52,7 +56,8 @@
  * channels).
  *
  * Supported shapes: head_dim 64 or 128; block_size 16; num_heads / num_kv_heads in
- * {1, 2, 4, 8}; (q dtype, cache dtype) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)};
+ * {1, 2, 4, 8}; (q dtype, cache dtype) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3),
+ * (BF16, FP8_E5M2)};
  * up to 16384 sequences per decode call; chunked prefill with BF16 queries only.
  * Anything else returns PA_ERR_UNSUPPORTED.
  */
@@ -74,7 +79,7 @@ typedef enum {
     PA_ERR_HIP = 4          /* a HIP launch failed                                       */
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype;
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2, PA_FP8_E5M2 = 3 } pa_dtype;
 
 /*
  * Paged KV append (the step that stores each new token's K and V in its block slot).
@@ -83,10 +88,12 @@ typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype;
  *   slot_mapping   device int64 [num_tokens]; token i goes to physical block
  *                  slot / block_size at offset slot % block_size.  A negative slot skips the
  *                  token; a slot >= num_blocks*block_size is also skipped.
- *   k_scale, v_scale  device fp32 [num_kv_heads] for an FP8_E4M3 cache, else NULL.
+ *   k_scale, v_scale  device fp32 [num_kv_heads] for an fp8 cache, else NULL.
  * src_dtype == cache_dtype copies the bits.  A BF16 or F32 source into an FP8_E4M3 cache
  * stores e4m3(fl32(x / scale[h])): one binary32 division (round to nearest even), then
- * round-to-nearest-even to E4M3 saturating at +-448, NaN kept as NaN with its sign.  Only
+ * round-to-nearest-even to E4M3 saturating at +-448, NaN kept as NaN with its sign.  An
+ * FP8_E5M2 cache stores e5m2(fl32(x / scale[h])) by the same rule, saturating at +-57344
+ * (infinities included) and storing NaN as S.11111.11.  Only
  * the addressed slots are written; every other byte of the pools is left unchanged.  Slots
  * must be distinct within one call.
  */
@@ -117,7 +124,7 @@ int64_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t nu
  *   context_lens   device int32 [num_seqs]; a sequence with 0 positions gets zeros.
  *   max_context_len  host bound on context_lens (sizes the launch and the workspace).
  *   scale          softmax scale applied to q.k (1/sqrt(head_dim) for standard attention).
- *   k_scale, v_scale device fp32 [num_kv_heads] for an FP8_E4M3 cache (the stored code times
+ *   k_scale, v_scale device fp32 [num_kv_heads] for an fp8 cache (the stored code times
  *                  the scale is the cached value), else NULL.
  *   partition_size 0 = automatic, else a multiple of block_size.  The work is the list of
  *                  every (sequence, kv head) pair's blocks laid end to end; it is cut into

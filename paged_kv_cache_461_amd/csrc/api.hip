@@ -38,9 +38,12 @@ int elem_bytes(int32_t dt)
     case PA_F32: return 4;
     case PA_BF16: return 2;
     case PA_FP8_E4M3: return 1;
+    case PA_FP8_E5M2: return 1;
     default: return 0;
     }
 }
+
+bool is_fp8(int32_t dt) { return dt == PA_FP8_E4M3 || dt == PA_FP8_E5M2; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -102,7 +105,7 @@ int32_t check_decode_shape(int32_t num_seqs, int32_t num_heads, int32_t num_kv_h
                     num_kv_heads, head_dim, block_size, max_context_len, partition_size);
     if (num_heads % num_kv_heads)
         return fail(PA_ERR_INVALID_ARG, "num_heads %d is not a multiple of num_kv_heads %d", num_heads, num_kv_heads);
-    if (!elem_bytes(q_dtype) || !elem_bytes(cache_dtype) || q_dtype == PA_FP8_E4M3)
+    if (!elem_bytes(q_dtype) || !elem_bytes(cache_dtype) || is_fp8(q_dtype))
         return fail(PA_ERR_INVALID_ARG, "unknown dtype (q %d, cache %d)", q_dtype, cache_dtype);
     const int32_t g = num_heads / num_kv_heads;
     if (g != 1 && g != 2 && g != 4 && g != 8)
@@ -110,7 +113,7 @@ int32_t check_decode_shape(int32_t num_seqs, int32_t num_heads, int32_t num_kv_h
     if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
     if (block_size != pa::kBlockSize) return fail(PA_ERR_UNSUPPORTED, "block_size %d (supported: 16)", block_size);
     const bool combo = (q_dtype == PA_F32 && cache_dtype == PA_F32) || (q_dtype == PA_BF16 && cache_dtype == PA_BF16) ||
-                       (q_dtype == PA_BF16 && cache_dtype == PA_FP8_E4M3);
+                       (q_dtype == PA_BF16 && is_fp8(cache_dtype));
     if (!combo) return fail(PA_ERR_UNSUPPORTED, "(q dtype %d, cache dtype %d) not supported", q_dtype, cache_dtype);
     if (partition_size > 0 && partition_size % block_size)
         return fail(PA_ERR_INVALID_ARG, "partition_size %d is not a multiple of block_size %d", partition_size, block_size);
@@ -219,9 +222,9 @@ int32_t pa_kv_cache_write(const void* key, const void* value, int32_t src_dtype,
         return fail(PA_ERR_INVALID_ARG, "negative or zero size (num_tokens=%d num_kv_heads=%d head_dim=%d "
                     "block_size=%d num_blocks=%lld)", num_tokens, num_kv_heads, head_dim, block_size,
                     (long long)num_blocks);
-    if (!elem_bytes(src_dtype) || !elem_bytes(cache_dtype) || src_dtype == PA_FP8_E4M3)
+    if (!elem_bytes(src_dtype) || !elem_bytes(cache_dtype) || is_fp8(src_dtype))
         return fail(PA_ERR_INVALID_ARG, "unknown dtype (src %d, cache %d)", src_dtype, cache_dtype);
-    if (!(src_dtype == cache_dtype || cache_dtype == PA_FP8_E4M3))
+    if (!(src_dtype == cache_dtype || is_fp8(cache_dtype)))
         return fail(PA_ERR_UNSUPPORTED, "append from dtype %d into a dtype %d cache", src_dtype, cache_dtype);
     if (head_dim % (64 / elem_bytes(cache_dtype)) || head_dim % (16 / elem_bytes(src_dtype)))
         return fail(PA_ERR_UNSUPPORTED, "head_dim %d is not a whole number of 64-byte cache slices", head_dim);
@@ -236,11 +239,11 @@ int32_t pa_kv_cache_write(const void* key, const void* value, int32_t src_dtype,
                     value, k_pool, v_pool, (const void*)slot_mapping);
     if (!aligned16(key) || !aligned16(value) || !aligned16(k_pool) || !aligned16(v_pool))
         return fail(PA_ERR_INVALID_ARG, "key, value and pools must be 16-byte aligned");
-    if (cache_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale))
+    if (is_fp8(cache_dtype) && (!k_scale || !v_scale))
         return fail(PA_ERR_INVALID_ARG, "an fp8 cache needs k_scale and v_scale");
     pa::KvWriteArgs a{key, value, k_pool, v_pool, num_blocks, slot_mapping, num_tokens, num_kv_heads, head_dim,
-                      block_size, cache_dtype == PA_FP8_E4M3 ? k_scale : nullptr,
-                      cache_dtype == PA_FP8_E4M3 ? v_scale : nullptr};
+                      block_size, is_fp8(cache_dtype) ? k_scale : nullptr,
+                      is_fp8(cache_dtype) ? v_scale : nullptr};
     hipError_t e = pa::launch_kv_write(src_dtype, cache_dtype, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(PA_ERR_HIP, "kv_cache_write launch: %s", hipGetErrorString(e));
     return ok();
@@ -290,7 +293,7 @@ int32_t decode_call(int32_t phase, void* out, const void* query, int32_t q_dtype
                     (const void*)context_lens);
     if (!aligned16(query) || !aligned16(k_pool) || !aligned16(v_pool))
         return fail(PA_ERR_INVALID_ARG, "query and pools must be 16-byte aligned");
-    if (cache_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale))
+    if (is_fp8(cache_dtype) && (!k_scale || !v_scale))
         return fail(PA_ERR_INVALID_ARG, "an fp8 cache needs k_scale and v_scale");
     if (!(scale == scale)) return fail(PA_ERR_INVALID_ARG, "scale is NaN");
     if ((new_key == nullptr) != (new_value == nullptr))
@@ -306,7 +309,7 @@ int32_t decode_call(int32_t phase, void* out, const void* query, int32_t q_dtype
         if (reinterpret_cast<uintptr_t>(workspace) % kWorkspaceAlign)
             return fail(PA_ERR_WORKSPACE, "workspace must be %d-byte aligned", (int)kWorkspaceAlign);
     }
-    const bool fp8 = cache_dtype == PA_FP8_E4M3;
+    const bool fp8 = is_fp8(cache_dtype);
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     pa::DecodeArgs a{};
     a.out = out;
@@ -429,7 +432,7 @@ int32_t pa_paged_attention_chunked_prefill(void* out, const void* query, int32_t
                     (const void*)block_tables, (const void*)context_lens);
     if (!aligned16(query) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool))
         return fail(PA_ERR_INVALID_ARG, "query, out and pools must be 16-byte aligned");
-    if (cache_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale))
+    if (is_fp8(cache_dtype) && (!k_scale || !v_scale))
         return fail(PA_ERR_INVALID_ARG, "an fp8 cache needs k_scale and v_scale");
     if (!(scale == scale)) return fail(PA_ERR_INVALID_ARG, "scale is NaN");
     const PrefillPlan pl = plan_prefill(num_query_rows, num_seqs, max_query_len, num_heads, num_kv_heads, head_dim,
@@ -444,7 +447,7 @@ int32_t pa_paged_attention_chunked_prefill(void* out, const void* query, int32_t
             return fail(PA_ERR_WORKSPACE, "workspace must be %d-byte aligned", (int)kWorkspaceAlign);
     }
     if (pl.grid == 0) return ok();
-    const bool fp8 = cache_dtype == PA_FP8_E4M3;
+    const bool fp8 = is_fp8(cache_dtype);
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     pa::PrefillArgs a{};
     a.out = out;

@@ -76,7 +76,7 @@ struct Acc {
 template <int QT, int KT, int D, int G>
 struct QRegs {
     using S = Shape<QT, KT, D, G>;
-    static constexpr int NQW = (KT == kFP8) ? 8 : 4;  // dwords per (slice, head)
+    static constexpr int NQW = kIsFp8<KT> ? 8 : 4;  // dwords per (slice, head)
     uint32_t w[S::NCH][G][NQW];
 };
 
@@ -152,15 +152,15 @@ __device__ __forceinline__ void qk_slice(const QSrc& q, int kp, int c, const uin
             acc[h] = dot2_bf16(kv.y, qw[1], acc[h]);
             acc[h] = dot2_bf16(kv.z, qw[2], acc[h]);
             acc[h] = dot2_bf16(kv.w, qw[3], acc[h]);
-        } else if constexpr (KT == kFP8) {
-            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<false>(kv.x), qw[0], acc[h]);
-            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<true>(kv.x), qw[1], acc[h]);
-            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<false>(kv.y), qw[2], acc[h]);
-            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<true>(kv.y), qw[3], acc[h]);
-            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<false>(kv.z), qw[4], acc[h]);
-            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<true>(kv.z), qw[5], acc[h]);
-            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<false>(kv.w), qw[6], acc[h]);
-            acc[h] = dot2_bf16(e4m3x2_to_bf16x2<true>(kv.w), qw[7], acc[h]);
+        } else if constexpr (kIsFp8<KT>) {
+            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, false>(kv.x), qw[0], acc[h]);
+            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, true>(kv.x), qw[1], acc[h]);
+            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, false>(kv.y), qw[2], acc[h]);
+            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, true>(kv.y), qw[3], acc[h]);
+            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, false>(kv.z), qw[4], acc[h]);
+            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, true>(kv.z), qw[5], acc[h]);
+            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, false>(kv.w), qw[6], acc[h]);
+            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, true>(kv.w), qw[7], acc[h]);
         } else {
             acc[h] = __builtin_fmaf(as_float(kv.x), as_float(qw[0]), acc[h]);
             acc[h] = __builtin_fmaf(as_float(kv.y), as_float(qw[1]), acc[h]);
@@ -188,12 +188,12 @@ __device__ __forceinline__ void pv_load(Acc<QT, KT, D, G>& st, int c, const uint
             st.o[cg][h] = dot2_bf16(vv.z, pps[h][q * 4 + 2], st.o[cg][h]);
             st.o[cg][h] = dot2_bf16(vv.w, pps[h][q * 4 + 3], st.o[cg][h]);
         }
-    } else if constexpr (KT == kFP8) {
+    } else if constexpr (kIsFp8<KT>) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const uint32_t w = u4_get(vv, i);
-            const uint32_t lo = e4m3x2_to_bf16x2<false>(w);
-            const uint32_t hi = e4m3x2_to_bf16x2<true>(w);
+            const uint32_t lo = fp8x2_to_bf16x2<KT, false>(w);
+            const uint32_t hi = fp8x2_to_bf16x2<KT, true>(w);
 #pragma unroll
             for (int h = 0; h < G; h++) {
                 st.o[cg][h] = dot2_bf16(lo, pps[h][2 * i], st.o[cg][h]);
@@ -467,7 +467,7 @@ __device__ __forceinline__ void append_chunk_tokens(const DecodeArgs& a, const i
                                        (((int64_t)c.s * Hkv + c.g) * D + piece * N) * ES;
             const int64_t tile = ((int64_t)phys * Hkv + c.g) * kBlockSize * D;
             unsigned char* pool = static_cast<unsigned char*>(kv ? a.v_pool : a.k_pool);
-            const float sc = CT == kFP8 && ST != CT ? (kv ? a.v_scale : a.k_scale)[c.g] : 1.0f;
+            const float sc = kIsFp8<CT> && ST != CT ? (kv ? a.v_scale : a.k_scale)[c.g] : 1.0f;
             store_kv_piece<ST, CT>(load16(src), pool, tile, piece * N, t % kBlockSize, kv, D, kBlockSize, sc);
         }
         stored = true;
@@ -581,7 +581,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(const Dec
             }
         };
         load_query(cc);
-        float c2 = a.scale_log2 * (KT == kFP8 ? a.k_scale[cc.g] : 1.0f);
+        float c2 = a.scale_log2 * (kIsFp8<KT> ? a.k_scale[cc.g] : 1.0f);
 
         Acc<QT, KT, D, G> st;
         auto reset = [&]() {
@@ -617,7 +617,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(const Dec
             }
             const int64_t piece = run + k;
             if (whole) {
-                const float vs = KT == kFP8 ? a.v_scale[cc.g] : 1.0f;
+                const float vs = kIsFp8<KT> ? a.v_scale[cc.g] : 1.0f;
 #pragma unroll
                 for (int h = 0; h < G; h++) {
                     const float f = st.l[h] > 0.0f ? vs / st.l[h] : 0.0f;
@@ -673,7 +673,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(const Dec
                     const int j = (i + 1) % NST;  // the slot issued NST-1 steps ago
                     if (ta > 0 && cc.j == 0) {       // a new run: start its piece
                         load_query(cc);
-                        c2 = a.scale_log2 * (KT == kFP8 ? a.k_scale[cc.g] : 1.0f);
+                        c2 = a.scale_log2 * (kIsFp8<KT> ? a.k_scale[cc.g] : 1.0f);
                         reset();
                         piece_j0 = 0;
                     }
@@ -725,7 +725,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a)
             for (int j = 0; j < PER; j++) acc[j] = __builtin_fmaf(wgt, op[lane + 64 * j], acc[j]);
         }
     }
-    const float vs = KT == kFP8 ? a.v_scale[g] : 1.0f;
+    const float vs = kIsFp8<KT> ? a.v_scale[g] : 1.0f;
 #pragma unroll
     for (int j = 0; j < PER; j++) {
         const float v = L > 0.0f ? acc[j] / L * vs : 0.0f;
@@ -785,6 +785,7 @@ hipError_t launch_decode(int phase, int q_dtype, int cache_dtype, int head_dim, 
     if (q_dtype == kF32 && cache_dtype == kF32) return launch_d<kF32, kF32>(phase, head_dim, gqa, a, stream);
     if (q_dtype == kBF16 && cache_dtype == kBF16) return launch_d<kBF16, kBF16>(phase, head_dim, gqa, a, stream);
     if (q_dtype == kBF16 && cache_dtype == kFP8) return launch_d<kBF16, kFP8>(phase, head_dim, gqa, a, stream);
+    if (q_dtype == kBF16 && cache_dtype == kE5M2) return launch_d<kBF16, kE5M2>(phase, head_dim, gqa, a, stream);
     return hipErrorInvalidValue;
 }
 

@@ -6,9 +6,10 @@
 // the offset inside it (page 1, section 4).  Layouts are those of include/pagedattn.h: a K
 // piece lands contiguously inside one 64-byte channel slice of the (block, kv head) tile; a V
 // piece is spread over its channels' token groups, so V is written with element-sized stores
-// that touch only this token's bytes.  Same-dtype append copies bits; bf16/fp32 -> OCP E4M3
-// divides by the head's scale in binary32 (round to nearest even) and converts with
-// v_cvt_pk_fp8_f32 after clamping to +-448 (saturation), NaN handled explicitly.
+// that touch only this token's bytes.  Same-dtype append copies bits; bf16/fp32 -> OCP E4M3 or
+// E5M2 divides by the head's scale in binary32 (round to nearest even) and converts with
+// v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 after clamping to the format's largest finite value
+// (saturation), NaN handled explicitly.
 #pragma once
 
 #include "pa_device.hpp"
@@ -46,7 +47,7 @@ __device__ __forceinline__ void store_kv_piece(const uint4 raw, unsigned char* p
             }
         }
     } else {
-        static_assert(CT == kFP8, "conversions go to E4M3 only");
+        static_assert(kIsFp8<CT>, "conversions go to fp8 only");
         uint32_t codes[N];
 #pragma unroll
         for (int i = 0; i < N; i++) {
@@ -55,7 +56,7 @@ __device__ __forceinline__ void store_kv_piece(const uint4 raw, unsigned char* p
                 x = bf16_bits_to_f32((words[i / 2] >> (16 * (i % 2))) & 0xFFFFu);
             else
                 x = as_float(words[i]);
-            codes[i] = f32_to_e4m3(__fdiv_rn(x, scale));
+            codes[i] = f32_to_fp8<CT>(__fdiv_rn(x, scale));
         }
         if (kv == 0) {
             unsigned char* dst = pool + slice + (int64_t)o * W + d0 % W;

@@ -2,8 +2,8 @@
 //
 // Element conversions and cross-lane primitives, written directly against CDNA4
 // instructions through clang builtins: v_dot2c_f32_bf16, DPP row/quad moves, ds_swizzle,
-// v_exp_f32, v_cvt_scalef32_pk_bf16_fp8 (OCP E4M3 -> bf16 pair), v_cvt_pk_fp8_f32
-// (f32 -> OCP E4M3) and the gfx950 f32 -> bf16 pack.
+// v_exp_f32, v_cvt_scalef32_pk_bf16_fp8 / _bf8 (OCP E4M3 / E5M2 -> bf16 pair),
+// v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 (f32 -> OCP E4M3 / E5M2) and the gfx950 f32 -> bf16 pack.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -11,7 +11,11 @@
 
 namespace pa {
 
-enum Dtype : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+// kFP8 is OCP fp8 E4M3, kE5M2 OCP fp8 E5M2 (AMD's "bf8").
+enum Dtype : int { kF32 = 0, kBF16 = 1, kFP8 = 2, kE5M2 = 3 };
+
+template <int DT>
+constexpr bool kIsFp8 = DT == kFP8 || DT == kE5M2;
 
 template <int DT>
 struct DtypeBytes;
@@ -25,6 +29,10 @@ struct DtypeBytes<kBF16> {
 };
 template <>
 struct DtypeBytes<kFP8> {
+    static constexpr int value = 1;
+};
+template <>
+struct DtypeBytes<kE5M2> {
     static constexpr int value = 1;
 };
 
@@ -65,6 +73,25 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w)
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
+// Two OCP E5M2 bytes -> two bf16, exact (every E5M2 value, infinities and NaN included, is a
+// bf16 value).
+template <bool HI>
+__device__ __forceinline__ uint32_t e5m2x2_to_bf16x2(uint32_t w)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HI));
+}
+
+// Two fp8 bytes of cache format KT -> two bf16.
+template <int KT, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w)
+{
+    static_assert(kIsFp8<KT>, "fp8 formats only");
+    if constexpr (KT == kFP8)
+        return e4m3x2_to_bf16x2<HI>(w);
+    else
+        return e5m2x2_to_bf16x2<HI>(w);
+}
+
 // fp32 -> OCP E4M3 code: round to nearest even, finite overflow saturates to +-448, NaN
 // keeps its sign and becomes S.1111.111.
 __device__ __forceinline__ uint32_t f32_to_e4m3(float y)
@@ -72,6 +99,25 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float y)
     if (__builtin_isnan(y)) return (as_uint(y) >> 24 & 0x80u) | 0x7Fu;
     float c = __builtin_fminf(__builtin_fmaxf(y, -448.0f), 448.0f);
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
+}
+
+// fp32 -> OCP E5M2 code: round to nearest even; finite overflow and the infinities saturate
+// to +-57344 (the same saturating rule as E4M3), NaN keeps its sign and becomes S.11111.11.
+__device__ __forceinline__ uint32_t f32_to_e5m2(float y)
+{
+    if (__builtin_isnan(y)) return (as_uint(y) >> 24 & 0x80u) | 0x7Fu;
+    float c = __builtin_fminf(__builtin_fmaxf(y, -57344.0f), 57344.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c, c, 0, false) & 0xFFu;
+}
+
+template <int CT>
+__device__ __forceinline__ uint32_t f32_to_fp8(float y)
+{
+    static_assert(kIsFp8<CT>, "fp8 formats only");
+    if constexpr (CT == kFP8)
+        return f32_to_e4m3(y);
+    else
+        return f32_to_e5m2(y);
 }
 
 // v_exp_f32: 2^x.

@@ -27,13 +27,16 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-F32, BF16, FP8_E4M3 = 0, 1, 2
-DTYPE_NAMES = {F32: "f32", BF16: "bf16", FP8_E4M3: "fp8_e4m3"}
-ELEM_BYTES = {F32: 4, BF16: 2, FP8_E4M3: 1}
-RAW_NP = {F32: np.float32, BF16: np.uint16, FP8_E4M3: np.uint8}
-POISON = {F32: np.float32(np.nan), BF16: np.uint16(0x7FC0), FP8_E4M3: np.uint8(0x7F)}
+F32, BF16, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3
+DTYPE_NAMES = {F32: "f32", BF16: "bf16", FP8_E4M3: "fp8_e4m3", FP8_E5M2: "fp8_e5m2"}
+ELEM_BYTES = {F32: 4, BF16: 2, FP8_E4M3: 1, FP8_E5M2: 1}
+RAW_NP = {F32: np.float32, BF16: np.uint16, FP8_E4M3: np.uint8, FP8_E5M2: np.uint8}
+POISON = {F32: np.float32(np.nan), BF16: np.uint16(0x7FC0), FP8_E4M3: np.uint8(0x7F), FP8_E5M2: np.uint8(0x7F)}
+FP8_DTYPES = (FP8_E4M3, FP8_E5M2)
 
 FP8_E4M3_MAX = 448.0  # largest finite OCP E4M3 value, used only to size calibration scales
+FP8_E5M2_MAX = 57344.0  # largest finite OCP E5M2 value, likewise
+FP8_MAX = {FP8_E4M3: FP8_E4M3_MAX, FP8_E5M2: FP8_E5M2_MAX}
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -134,6 +137,7 @@ class PagedBatch:
     refcount: np.ndarray = field(default_factory=lambda: np.zeros(0, dtype=np.int32))
     k_scale: np.ndarray | None = None  # float32 [Hkv] for an fp8 cache
     v_scale: np.ndarray | None = None
+    fp8_scale: str = "head"  # fp8 scale granularity: "head" or "tensor" (one value repeated per head)
 
     # -- shapes ------------------------------------------------------------------------
     @property
@@ -299,7 +303,7 @@ class PagedBatch:
         b = self.kv_read_bytes(unique)
         b += self.num_rows * self.num_heads * self.head_dim * 2 * eq
         b += int(nblk.sum()) * 4 + self.num_seqs * 4
-        if self.cache_dtype == FP8_E4M3:
+        if self.cache_dtype in FP8_DTYPES:
             b += 2 * 4 * self.num_kv_heads
         return int(b)
 
@@ -314,14 +318,14 @@ class PagedBatch:
 def build_batch(context_lens, *, num_heads, num_kv_heads, head_dim, block_size=16, q_dtype=BF16,
                 cache_dtype=BF16, src_dtype=None, seed=0, query_lens=None, shared_prefix_len=0,
                 sharing=(), num_blocks=None, pool_slack=0.10, max_blocks_per_seq=None, layer=0,
-                name="custom", fp8_calibration_tokens=4096) -> PagedBatch:
+                name="custom", fp8_calibration_tokens=4096, fp8_scale="head") -> PagedBatch:
     ctx = np.asarray(context_lens, dtype=np.int32)
     S = ctx.shape[0]
     ql = np.ones(S, np.int32) if query_lens is None else np.asarray(query_lens, np.int32)
     if np.any(ql > np.maximum(ctx, 0)) or np.any(ql < 0):
         raise ValueError("query_lens must lie in [0, context_len]")
     if src_dtype is None:
-        src_dtype = q_dtype if cache_dtype == FP8_E4M3 else cache_dtype
+        src_dtype = q_dtype if cache_dtype in FP8_DTYPES else cache_dtype
     B = block_size
     sharing = np.asarray(sorted(set(int(s) for s in sharing)), dtype=np.int64)
     if shared_prefix_len % B:
@@ -360,21 +364,28 @@ def build_batch(context_lens, *, num_heads, num_kv_heads, head_dim, block_size=1
                        block_size=B, q_dtype=q_dtype, src_dtype=src_dtype, cache_dtype=cache_dtype,
                        context_lens=ctx, query_lens=ql, block_tables=tables, num_blocks=num_blocks,
                        seed=seed, layer=layer, shared_prefix_len=shared_prefix_len if len(sharing) else 0,
-                       sharing=sharing, refcount=alloc.refcount.copy())
-    if cache_dtype == FP8_E4M3:
+                       sharing=sharing, refcount=alloc.refcount.copy(), fp8_scale=fp8_scale)
+    if cache_dtype in FP8_DTYPES:
         batch.k_scale, batch.v_scale = fp8_calibration_scales(
-            num_kv_heads, head_dim, seed, layer, src_dtype, fp8_calibration_tokens)
+            num_kv_heads, head_dim, seed, layer, src_dtype, fp8_calibration_tokens, cache_dtype, fp8_scale)
     return batch
 
 
-def fp8_calibration_scales(num_kv_heads, head_dim, seed, layer, src_dtype, tokens=4096):
-    """Per-(layer, kv head) fp8 scales: amax over a seeded calibration batch of K (resp. V)
-    rows drawn like the workload, divided by the largest E4M3 value, as float32."""
+def fp8_calibration_scales(num_kv_heads, head_dim, seed, layer, src_dtype, tokens=4096, cache_dtype=FP8_E4M3,
+                           granularity="head"):
+    """fp8 scales for one layer: amax over a seeded calibration batch of K (resp. V) rows
+    drawn like the workload, divided by the format's largest finite value, as float32.
+    granularity "head" takes the amax per kv head; "tensor" takes one amax over all heads and
+    repeats it per head (a per-tensor scale)."""
+    if granularity not in ("head", "tensor"):
+        raise ValueError("fp8 scale granularity must be 'head' or 'tensor'")
     rng = np.random.default_rng([seed, 104, layer])
     cal = rng.standard_normal((tokens, 2, num_kv_heads, head_dim), dtype=np.float32)
     cal = raw_to_f32(to_raw(cal, src_dtype), src_dtype)
     amax = np.abs(cal).max(axis=(0, 3))  # [2][Hkv]
-    sc = (amax.astype(np.float64) / FP8_E4M3_MAX).astype(np.float32)
+    if granularity == "tensor":
+        amax = np.repeat(amax.max(axis=1, keepdims=True), num_kv_heads, axis=1)
+    sc = (amax.astype(np.float64) / FP8_MAX[cache_dtype]).astype(np.float32)
     return np.ascontiguousarray(sc[0]), np.ascontiguousarray(sc[1])
 
 
@@ -421,8 +432,10 @@ def mixed_continuous_batch(seed=0, num_seqs=256, num_sharing=64, prefix=2048,
 
 
 def fp8_chunked_prefill(seed=0, num_decode=128, chunk=512, chunk_ctx=8192,
-                        decode_range=(256, 8192), layer=0) -> PagedBatch:
-    """fp8 E4M3 KV cache with per-(layer, kv head) scales: sequence 0 is a 512-row prefill
+                        decode_range=(256, 8192), layer=0, cache_dtype=FP8_E4M3, fp8_scale="head",
+                        name="fp8_chunked_prefill") -> PagedBatch:
+    """fp8 KV cache (E4M3 unless cache_dtype says E5M2) with per-(layer, kv head) scales
+    (fp8_scale="tensor": one scale per layer, repeated per head): sequence 0 is a 512-row prefill
     chunk that is the last 512 positions of an 8192-token context; sequences 1..128 are
     decode rows with contexts uniform in [256, 8192].  32 query / 8 KV heads, head dim 128,
     bf16 queries and K/V rows."""
@@ -431,8 +444,8 @@ def fp8_chunked_prefill(seed=0, num_decode=128, chunk=512, chunk_ctx=8192,
     ctx = np.concatenate([[chunk_ctx], dec])
     ql = np.concatenate([[chunk], np.ones(num_decode, np.int64)])
     return build_batch(ctx, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16, q_dtype=BF16,
-                       cache_dtype=FP8_E4M3, src_dtype=BF16, seed=seed, layer=layer, query_lens=ql,
-                       name="fp8_chunked_prefill")
+                       cache_dtype=cache_dtype, src_dtype=BF16, seed=seed, layer=layer, query_lens=ql,
+                       name=name, fp8_scale=fp8_scale)
 
 
 WORKLOADS = {
@@ -441,4 +454,7 @@ WORKLOADS = {
     "long_context": long_context,
     "mixed_continuous_batch": mixed_continuous_batch,
     "fp8_chunked_prefill": fp8_chunked_prefill,
+    # the same step over an E5M2 cache with one scale per layer (per-tensor)
+    "fp8_e5m2_chunked_prefill": lambda seed=0, layer=0: fp8_chunked_prefill(
+        seed=seed, layer=layer, cache_dtype=FP8_E5M2, fp8_scale="tensor", name="fp8_e5m2_chunked_prefill"),
 }

@@ -12,7 +12,7 @@ from paged_kv_cache_461_amd import ops
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pagedattn.h")
-F32, BF16, FP8 = ops.F32, ops.BF16, ops.FP8_E4M3
+F32, BF16, FP8, E5M2 = ops.F32, ops.BF16, ops.FP8_E4M3, ops.FP8_E5M2
 FAKE = 0x10000  # a non-null 256-aligned address; never dereferenced by these calls
 
 
@@ -78,6 +78,10 @@ def _decode(lib, **kw):
     (dict(q_dtype=F32), ops.PA_ERR_UNSUPPORTED),             # f32 q over a bf16 cache
     (dict(q_dtype=FP8, cache_dtype=FP8), ops.PA_ERR_INVALID_ARG),
     (dict(cache_dtype=FP8), ops.PA_ERR_INVALID_ARG),         # fp8 without scales
+    (dict(cache_dtype=E5M2), ops.PA_ERR_INVALID_ARG),        # fp8 without scales
+    (dict(q_dtype=E5M2, cache_dtype=E5M2), ops.PA_ERR_INVALID_ARG),
+    (dict(q_dtype=F32, cache_dtype=E5M2), ops.PA_ERR_UNSUPPORTED),
+    (dict(cache_dtype=4), ops.PA_ERR_INVALID_ARG),           # unknown dtype code
     (dict(P=100), ops.PA_ERR_INVALID_ARG),                   # not a multiple of 16
     (dict(mbps=10), ops.PA_ERR_INVALID_ARG),                 # table shorter than max_ctx
     (dict(S=-1), ops.PA_ERR_INVALID_ARG),
@@ -139,6 +143,9 @@ def _write(lib, **kw):
     (dict(src=FP8, cache=FP8), ops.PA_ERR_INVALID_ARG),
     (dict(src=F32, cache=BF16), ops.PA_ERR_UNSUPPORTED),
     (dict(cache=FP8), ops.PA_ERR_INVALID_ARG),               # no scales
+    (dict(cache=E5M2), ops.PA_ERR_INVALID_ARG),              # no scales
+    (dict(src=E5M2, cache=E5M2), ops.PA_ERR_INVALID_ARG),
+    (dict(src=FP8, cache=E5M2), ops.PA_ERR_INVALID_ARG),
     (dict(D=72), ops.PA_ERR_UNSUPPORTED),                    # not whole 64-byte slices
     (dict(B=15), ops.PA_ERR_UNSUPPORTED),
     (dict(v_pool=FAKE + 4), ops.PA_ERR_INVALID_ARG),

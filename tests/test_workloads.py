@@ -62,6 +62,19 @@ def test_fp8_config_has_chunk_and_scales():
     assert np.all(b.k_scale > 0) and np.all(b.v_scale > 0)
 
 
+def test_e5m2_per_tensor_scales():
+    """The E5M2 step uses one scale per layer (the amax over all heads / 57344), repeated per
+    head; per-head scales of the same calibration batch are each at most that value."""
+    b = W.WORKLOADS["fp8_e5m2_chunked_prefill"]()
+    assert b.cache_dtype == W.FP8_E5M2 and b.fp8_scale == "tensor"
+    head_k, head_v = W.fp8_calibration_scales(b.num_kv_heads, b.head_dim, b.seed, b.layer, b.src_dtype,
+                                              cache_dtype=W.FP8_E5M2, granularity="head")
+    assert np.all(b.k_scale == head_k.max()) and np.all(b.v_scale == head_v.max())
+    assert len(set(head_k.tolist())) > 1
+    e4_k, _ = W.fp8_calibration_scales(b.num_kv_heads, b.head_dim, b.seed, b.layer, b.src_dtype)
+    np.testing.assert_allclose(head_k.astype(np.float64) * 57344.0, e4_k.astype(np.float64) * 448.0, rtol=1e-6)
+
+
 def test_shared_prefix_values_identical_and_written_once():
     b = W.build_batch([40, 50, 70], num_heads=4, num_kv_heads=2, head_dim=64, block_size=16,
                       q_dtype=W.BF16, cache_dtype=W.BF16, shared_prefix_len=32, sharing=[0, 2], seed=2)
