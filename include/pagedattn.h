@@ -254,7 +254,7 @@ int64_t pa_pool_bytes(int64_t num_blocks, int32_t num_kv_heads, int32_t head_dim
 /*
  * Measurement helper (not part of the attention path): read num_reads 4 KiB tiles of buf, tile
  * order[i] for i = 0 .. num_reads-1, with grid_workgroups x 256 threads (two tiles per wave and
- * iteration, 16-byte loads, each wave load one contiguous 1 KiB).  Timing it with a random
+ * iteration, 16-byte nontemporal loads, each wave load one contiguous 1 KiB).  Timing it with a random
  * order gives the HBM read bandwidth this GPU delivers for the scattered 4 KiB (block, kv head)
  * tiles of a paged pool, the practical ceiling the decode kernel is compared with.
  *   buf    device, buf_bytes bytes (16-byte aligned; whole tiles are used).

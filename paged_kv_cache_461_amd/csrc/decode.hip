@@ -19,7 +19,8 @@
 // chunk), so the workspace size depends only on the numbers of runs and chunks.
 //
 // Inside a wave, per 16-token block (pool layout in include/pagedattn.h) NCH K loads and NCH V
-// loads of 16 bytes per lane each read one contiguous 1 KiB slice:
+// loads of 16 bytes per lane each read one contiguous 1 KiB slice, with the nontemporal hint
+// (every K/V byte is read once per launch):
 //   QK^T: lane l holds channels of token l/4; bf16/fp8 K is multiplied with bf16 query pairs
 //         (held in VGPRs for the piece) by v_dot2c_f32_bf16 (fp8 first widened exactly to bf16
 //         pairs), fp32 K with FMAs; the 4 lanes of a token finish the dot product with two DPP
@@ -662,9 +663,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(const Dec
                     kv_nv[i] = bad ? 0 : ent_nv[i];
                     const int64_t off = (int64_t)phys * block_stride + (int64_t)ent_g[i] * S::TILE;
 #pragma unroll
-                    for (int c = 0; c < S::NCH; c++) kb[i][c] = load16(kpool + off + c * 1024);
+                    for (int c = 0; c < S::NCH; c++) kb[i][c] = load16_stream(kpool + off + c * 1024);
 #pragma unroll
-                    for (int c = 0; c < S::NCH; c++) vb[i][c] = load16(vpool + off + c * 1024);
+                    for (int c = 0; c < S::NCH; c++) vb[i][c] = load16_stream(vpool + off + c * 1024);
                 }
                 fetch_entry(ent[i], ent_nv[i], ent_g[i]);
 

@@ -169,6 +169,15 @@ __device__ __forceinline__ float wave_max(float x)
 
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// 16-byte load with the nontemporal hint (global_load_dwordx4 ... nt): for data read once per
+// launch, such as the K/V stream of decode.  Scattered 4 KiB tile reads run ~14% faster with
+// it on MI355X (6.0 -> 6.8 TB/s in a random-order read probe).
+__device__ __forceinline__ uint4 load16_stream(const void* p)
+{
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ uint32_t u4_get(const uint4& v, int i)
 {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;

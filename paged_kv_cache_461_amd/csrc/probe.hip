@@ -2,8 +2,9 @@
 // in a caller-given order (a random order mimics the scattered physical blocks of a paged KV
 // pool).  It is a measurement helper beside the attention path, not part of it.
 //
-// Each wave reads two whole tiles per iteration (8 loads of 16 bytes per lane, each one
-// contiguous 1 KiB), grid-striding over the order list; the XOR of everything read goes to
+// Each wave reads two whole tiles per iteration (8 nontemporal loads of 16 bytes per lane,
+// each one contiguous 1 KiB, as the decode kernel's K/V stream does), grid-striding over the
+// order list; the XOR of everything read goes to
 // `sink` only in an impossible case, so the loads cannot be removed.
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
@@ -30,7 +31,7 @@ __global__ __launch_bounds__(256) void tile_read_kernel(const unsigned char* __r
             o = o < 0 || o >= buf_tiles ? 0 : o;  // an order entry outside the buffer reads tile 0
             const unsigned char* p = buf + o * kProbeTile + lane * 16;
 #pragma unroll
-            for (int c = 0; c < 4; c++) v[u][c] = load16(p + c * 1024);
+            for (int c = 0; c < 4; c++) v[u][c] = load16_stream(p + c * 1024);
         }
 #pragma unroll
         for (int u = 0; u < 2; u++)
