@@ -65,8 +65,9 @@ int64_t max_units(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size, in
     return (int64_t)num_seqs * num_kv_heads * ((max_context_len + block_size - 1) / block_size);
 }
 
+// stream_waves: waves of the full persistent grid for the kernel variant.
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                       int32_t block_size, int32_t max_context_len, int32_t partition_size)
+                       int32_t block_size, int32_t max_context_len, int32_t partition_size, int64_t stream_waves)
 {
     DecodePlan pl{};
     const int64_t umax = max_units(num_seqs, num_kv_heads, block_size, max_context_len);
@@ -74,11 +75,11 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
     if (partition_size > 0) {
         pl.chunk_blocks = partition_size / block_size;
         pl.max_chunks = (umax + pl.chunk_blocks - 1) / pl.chunk_blocks;
-        waves = pl.max_chunks < pa::kStreamWaves ? pl.max_chunks : pa::kStreamWaves;
+        waves = pl.max_chunks < stream_waves ? pl.max_chunks : stream_waves;
     } else {
         pl.chunk_blocks = 0;
         const int64_t need = (umax + pa::kMinChunkBlocks - 1) / pa::kMinChunkBlocks;
-        waves = need < pa::kStreamWaves ? need : pa::kStreamWaves;
+        waves = need < stream_waves ? need : stream_waves;
     }
     pl.grid_workgroups = (int32_t)((waves + pa::kDecodeWaves - 1) / pa::kDecodeWaves);
     // automatic chunks: C >= ceil(U / NW) gives at most NW chunks
@@ -255,7 +256,9 @@ int64_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t nu
     if (check_decode_shape(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
                            partition_size, PA_BF16, PA_BF16) != PA_OK)
         return -1;
-    return plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len, partition_size)
+    // sized for the largest grid any dtype's kernel uses
+    return plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len, partition_size,
+                       pa::kStreamWavesMax)
         .total;
 }
 
@@ -300,8 +303,10 @@ int32_t decode_call(int32_t phase, void* out, const void* query, int32_t q_dtype
         return fail(PA_ERR_INVALID_ARG, "new_key and new_value must both be given");
     if (new_key && (!aligned16(new_key) || !aligned16(new_value)))
         return fail(PA_ERR_INVALID_ARG, "new_key and new_value must be 16-byte aligned");
-    const DecodePlan pl =
-        plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len, partition_size);
+    const int64_t stream_waves =
+        (int64_t)pa::kSimds * pa::decode_waves_per_simd(q_dtype, cache_dtype, head_dim, num_heads / num_kv_heads);
+    const DecodePlan pl = plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                                      partition_size, stream_waves);
     if (pl.total > 0) {
         if (!workspace || (int64_t)workspace_bytes < pl.total)
             return fail(PA_ERR_WORKSPACE, "workspace %zu bytes at %p, need %lld", workspace_bytes, workspace,

@@ -496,8 +496,32 @@ struct ChunkMap {
     __device__ int64_t of_unit(int64_t u) const { return u / C; }
 };
 
+// Occupancy of the streaming kernel, chosen per variant from measurements on MI355X (stream
+// kernel alone, Llama-shaped batch with the variant's heads):
+//   3 waves per SIMD (at most 168 VGPRs, no spills) where that measured faster: fp8 with G <= 4
+//     (70.3 -> 66.4 us at D 128) and D 64 with G <= 4 (bf16: 60.0 -> 55.5 us);
+//   2 forced for bf16 D 128 G 8, which otherwise takes 296 registers and runs one wave per
+//     SIMD (157 -> 139 us despite a few spills);
+//   otherwise the compiler's choice: 2 waves per SIMD for most variants (bf16 G 1 / 2 measured
+//     slower at 3), one for fp32 D 128, which measured slower when forced to 2 with spills.
+// The persistent grid has max(2, this) waves per SIMD.
+template <int KT, int D, int G>
+constexpr int stream_min_waves()
+{
+    if constexpr (KT == kF32) return 1;
+    else if constexpr (KT == kBF16) return D == 64 && G <= 4 ? 3 : D == 128 && G == 8 ? 2 : 1;
+    else return G <= 4 ? 3 : 1;
+}
+
+template <int KT, int D, int G>
+constexpr int stream_waves_per_simd()
+{
+    return stream_min_waves<KT, D, G>() > 2 ? stream_min_waves<KT, D, G>() : 2;
+}
+
 template <int QT, int KT, int D, int G>
-__global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(const DecodeArgs a)
+__global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) void decode_stream_kernel(
+    const DecodeArgs a)
 {
     using S = Shape<QT, KT, D, G>;
     constexpr bool QL = Variant<KT>::kQueryInLds;
@@ -779,6 +803,36 @@ hipError_t launch_d(int phase, int head_dim, int gqa, const DecodeArgs& a, hipSt
 }
 
 }  // namespace
+
+namespace {
+template <int KT, int D>
+int waves_g(int gqa)
+{
+    switch (gqa) {
+    case 1: return stream_waves_per_simd<KT, D, 1>();
+    case 2: return stream_waves_per_simd<KT, D, 2>();
+    case 4: return stream_waves_per_simd<KT, D, 4>();
+    default: return stream_waves_per_simd<KT, D, 8>();
+    }
+}
+template <int KT>
+int waves_d(int head_dim, int gqa)
+{
+    return head_dim == 64 ? waves_g<KT, 64>(gqa) : waves_g<KT, 128>(gqa);
+}
+}  // namespace
+
+int decode_waves_per_simd(int q_dtype, int cache_dtype, int head_dim, int gqa)
+{
+    (void)q_dtype;  // fp32 queries go with an fp32 cache, bf16 with the others
+    switch (cache_dtype) {
+    case kF32: return waves_d<kF32>(head_dim, gqa);
+    case kBF16: return waves_d<kBF16>(head_dim, gqa);
+    case kFP8: return waves_d<kFP8>(head_dim, gqa);
+    case kE5M2: return waves_d<kE5M2>(head_dim, gqa);
+    default: return 2;
+    }
+}
 
 hipError_t launch_decode(int phase, int q_dtype, int cache_dtype, int head_dim, int gqa, const DecodeArgs& a,
                          hipStream_t stream)

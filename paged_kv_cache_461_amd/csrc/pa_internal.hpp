@@ -26,7 +26,8 @@ struct KvWriteArgs {
 };
 
 // Decode: the streaming kernel (phase 1) and the merge kernel (phase 2).
-constexpr int kStreamWaves = 2048;   // waves of the persistent grid (8 per CU on 256 CUs)
+constexpr int kSimds = 1024;         // 256 CUs x 4 SIMDs
+constexpr int kStreamWavesMax = 3 * kSimds;  // largest persistent grid (3 waves per SIMD)
 constexpr int kMinChunkBlocks = 8;   // smallest automatic chunk, in (block, kv head) units
 constexpr int kMaxDecodeSeqs = 16384;  // context lengths of a call are staged in 64 KiB of LDS
 
@@ -90,6 +91,9 @@ hipError_t launch_kv_write(int src_dtype, int cache_dtype, const KvWriteArgs& a,
 
 // phase 1 = streaming kernel, 2 = merge kernel, 3 = both.  Returns hipErrorInvalidValue when
 // no kernel exists for the combination.
+// Waves per SIMD the streaming kernel of this variant is built for (2 or 3); the persistent
+// grid has that many waves per SIMD.
+int decode_waves_per_simd(int q_dtype, int cache_dtype, int head_dim, int gqa);
 hipError_t launch_decode(int phase, int q_dtype, int cache_dtype, int head_dim, int gqa,
                          const DecodeArgs& a, hipStream_t stream);
 
