@@ -557,8 +557,8 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) voi
     const int64_t U = pl.U;
     const int64_t nchunks = U > 0 ? min(cm.of_unit(U - 1) + 1, a.max_chunks) : 0;
 
-    const unsigned char* kpool = static_cast<const unsigned char*>(a.k_pool) + lane * 16;
-    const unsigned char* vpool = static_cast<const unsigned char*>(a.v_pool) + lane * 16;
+    const unsigned char* kpool = static_cast<const unsigned char*>(a.k_pool);
+    const unsigned char* vpool = static_cast<const unsigned char*>(a.v_pool);
     const int64_t block_stride = (int64_t)Hkv * S::TILE;
     const int32_t* tables = a.block_tables;
     const int mbps = a.max_blocks_per_seq;
@@ -681,15 +681,20 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) voi
             for (int i = 0; i < NST; i++) {
                 const int t = t0 + i;
                 {
-                    int phys = ent[i];
+                    // A step past the chunk's end, or a block id outside the pool, loads through
+                    // an empty buffer window: the loads return zeros without touching memory,
+                    // and the instruction stream (hence every wait count) stays the same.
+                    int phys = __builtin_amdgcn_readfirstlane(ent[i]);
                     const bool bad = phys < 0 || (int64_t)phys >= a.num_blocks;
                     phys = bad ? 0 : phys;
                     kv_nv[i] = bad ? 0 : ent_nv[i];
+                    const int window = bad || t >= n ? 0 : S::TILE;
                     const int64_t off = (int64_t)phys * block_stride + (int64_t)ent_g[i] * S::TILE;
+                    const TileWindow kw(kpool + off, window), vw(vpool + off, window);
 #pragma unroll
-                    for (int c = 0; c < S::NCH; c++) kb[i][c] = load16_stream(kpool + off + c * 1024);
+                    for (int c = 0; c < S::NCH; c++) kb[i][c] = kw.load_stream(lane * 16 + c * 1024);
 #pragma unroll
-                    for (int c = 0; c < S::NCH; c++) vb[i][c] = load16_stream(vpool + off + c * 1024);
+                    for (int c = 0; c < S::NCH; c++) vb[i][c] = vw.load_stream(lane * 16 + c * 1024);
                 }
                 fetch_entry(ent[i], ent_nv[i], ent_g[i]);
 

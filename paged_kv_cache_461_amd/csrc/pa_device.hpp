@@ -178,6 +178,24 @@ __device__ __forceinline__ uint4 load16_stream(const void* p)
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// A wave-uniform window of `bytes` bytes at `base`, read with buffer loads: an offset at or
+// past the end (a window of 0 bytes makes every offset so) returns zeros without a memory
+// access.  The descriptor is the raw-buffer form of the gfx9 family (stride 0, word 3
+// 0x00020000); loads carry the nontemporal hint.
+struct TileWindow {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ TileWindow(const void* base, int bytes)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000))
+    {
+    }
+    __device__ __forceinline__ uint4 load_stream(int offset) const
+    {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, kBufferNontemporal);
+        return make_uint4(v.x, v.y, v.z, v.w);
+    }
+    static constexpr int kBufferNontemporal = 2;  // the cache-policy bit printed as "nt"
+};
+
 __device__ __forceinline__ uint32_t u4_get(const uint4& v, int i)
 {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
