@@ -54,6 +54,8 @@ def parse_args():
                             "fp8_e5m2_chunked_prefill"])
     p.add_argument("--layers", type=int, default=2, help="layer pools cycled through (>= 2)")
     p.add_argument("--partition-size", type=int, default=0, help="split-K partition (0 = library's choice)")
+    p.add_argument("--block-size", type=int, default=16, choices=[16, 32],
+                   help="tokens per KV block of the pools (both workloads)")
     p.add_argument("--extra-workload", default="fp8_chunked_prefill",
                    choices=["none", "fp8_chunked_prefill", "fp8_e5m2_chunked_prefill", "llama3_8b_decode",
                             "long_context", "mixed_continuous_batch"],
@@ -106,10 +108,10 @@ def read_probe(stream, reps=10):
             "what": "2 GiB read as 4 KiB tiles in a seeded random order, 2048 workgroups x 256 threads"}
 
 
-def make_batch(name):
+def make_batch(name, block_size=16):
     from paged_kv_cache_461_amd import workloads as W
 
-    return W.WORKLOADS[name]()
+    return W.WORKLOADS[name](block_size=block_size)
 
 
 KERNEL_SOURCES = {
@@ -412,12 +414,12 @@ def main():
     ops.library()  # fails loudly if the HIP library is missing
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    batch = make_batch(args.workload)
+    batch = make_batch(args.workload, args.block_size)
     res, stream = measure(batch, dev, args.layers, args.steps, args.warmup, args.partition_size, args.fused_append)
     if args.extra_workload != "none" and args.extra_workload != args.workload:
         # The rest of the hot path in the same run: the fp8 cache (in-kernel dequant) and the
         # chunked-prefill kernel, on the mixed step (one layer).
-        extra = make_batch(args.extra_workload)
+        extra = make_batch(args.extra_workload, args.block_size)
         xres, _ = measure(extra, dev, 1, args.steps, min(args.warmup, 2), 0, args.fused_append)
         keep = ("value", "unit", "ms_per_step", "steps", "warmup", "config", "seqs_per_s_per_layer", "step_bytes",
                 "kernels_us", "roofline", "roofline_prefill")

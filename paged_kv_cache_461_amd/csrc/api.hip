@@ -59,10 +59,10 @@ struct DecodePlan {
     int64_t total;
 };
 
-// Work units (16-token blocks of one kv head) of the largest batch these arguments allow.
-int64_t max_units(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size, int32_t max_context_len)
+// Work units (16 tokens of one kv head) of the largest batch these arguments allow.
+int64_t max_units(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len)
 {
-    return (int64_t)num_seqs * num_kv_heads * ((max_context_len + block_size - 1) / block_size);
+    return (int64_t)num_seqs * num_kv_heads * ((max_context_len + pa::kUnitTokens - 1) / pa::kUnitTokens);
 }
 
 // stream_waves: waves of the full persistent grid for the kernel variant.
@@ -70,10 +70,11 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
                        int32_t block_size, int32_t max_context_len, int32_t partition_size, int64_t stream_waves)
 {
     DecodePlan pl{};
-    const int64_t umax = max_units(num_seqs, num_kv_heads, block_size, max_context_len);
+    (void)block_size;  // the plan counts 16-token units whatever the block size
+    const int64_t umax = max_units(num_seqs, num_kv_heads, max_context_len);
     int64_t waves;
     if (partition_size > 0) {
-        pl.chunk_blocks = partition_size / block_size;
+        pl.chunk_blocks = partition_size / pa::kUnitTokens;
         pl.max_chunks = (umax + pl.chunk_blocks - 1) / pl.chunk_blocks;
         waves = pl.max_chunks < stream_waves ? pl.max_chunks : stream_waves;
     } else {
@@ -112,7 +113,8 @@ int32_t check_decode_shape(int32_t num_seqs, int32_t num_heads, int32_t num_kv_h
     if (g != 1 && g != 2 && g != 4 && g != 8)
         return fail(PA_ERR_UNSUPPORTED, "GQA group %d (supported: 1, 2, 4, 8)", g);
     if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
-    if (block_size != pa::kBlockSize) return fail(PA_ERR_UNSUPPORTED, "block_size %d (supported: 16)", block_size);
+    if (block_size != 16 && block_size != 32)
+        return fail(PA_ERR_UNSUPPORTED, "block_size %d (supported: 16, 32)", block_size);
     const bool combo = (q_dtype == PA_F32 && cache_dtype == PA_F32) || (q_dtype == PA_BF16 && cache_dtype == PA_BF16) ||
                        (q_dtype == PA_BF16 && is_fp8(cache_dtype));
     if (!combo) return fail(PA_ERR_UNSUPPORTED, "(q dtype %d, cache dtype %d) not supported", q_dtype, cache_dtype);
@@ -331,6 +333,7 @@ int32_t decode_call(int32_t phase, void* out, const void* query, int32_t q_dtype
     a.num_seqs = num_seqs;
     a.num_heads = num_heads;
     a.num_kv_heads = num_kv_heads;
+    a.block_size = block_size;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.k_scale = fp8 ? k_scale : nullptr;
     a.v_scale = fp8 ? v_scale : nullptr;
@@ -469,6 +472,7 @@ int32_t pa_paged_attention_chunked_prefill(void* out, const void* query, int32_t
     a.num_query_rows = num_query_rows;
     a.num_heads = num_heads;
     a.num_kv_heads = num_kv_heads;
+    a.block_size = block_size;
     a.row_blocks = pl.row_blocks;
     a.num_splits = pl.num_splits;
     a.split_keys = pl.split_keys;

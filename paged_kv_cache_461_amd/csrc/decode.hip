@@ -53,9 +53,9 @@ struct Shape {
     static constexpr int NCH = D / W;      // 1 KiB slices per (block, kv head) tile
     static constexpr int KE = W / 4;       // K channels per lane per slice
     static constexpr int TPC = 16 / EB;    // V: tokens of one channel per 16-byte piece
-    static constexpr int NQ = kBlockSize / TPC;  // V: token groups per block
+    static constexpr int NQ = kUnitTokens / TPC;  // V: token groups per unit
     static constexpr int CG = D / 64;      // V: 64-channel groups (one channel per lane)
-    static constexpr int TILE = kBlockSize * D * EB;
+    static constexpr int TILE = kUnitTokens * D * EB;  // bytes of one unit (16 tokens, one kv head)
     static constexpr int QB = DtypeBytes<QT>::value;
     static constexpr int QBYTES = G * D * QB;  // one GQA group's query rows
     static_assert(TILE == NCH * 1024, "a tile is a whole number of 1 KiB slices");
@@ -250,7 +250,7 @@ __device__ __forceinline__ void attend_block(Acc<QT, KT, D, G>& st, const QSrc& 
 #pragma unroll
     for (int h = 0; h < G; h++) {
         s2[h] = quad_sum(acc[h]) * c2;
-        if (n_valid < kBlockSize) s2[h] = tok < n_valid ? s2[h] : -__builtin_inff();
+        if (n_valid < kUnitTokens) s2[h] = tok < n_valid ? s2[h] : -__builtin_inff();
     }
 
     bool need = false;
@@ -280,7 +280,7 @@ __device__ __forceinline__ void attend_block(Acc<QT, KT, D, G>& st, const QSrc& 
         if constexpr (KT == kF32) {
             st.l[h] += mine + other;
 #pragma unroll
-            for (int t = 0; t < kBlockSize; t++) ps[h][t] = as_float(__builtin_amdgcn_readlane(as_uint(mine), 4 * t));
+            for (int t = 0; t < kUnitTokens; t++) ps[h][t] = as_float(__builtin_amdgcn_readlane(as_uint(mine), 4 * t));
         } else {
             const uint32_t pp = pack_bf16x2(odd ? other : mine, odd ? mine : other);
             st.l[h] = dot2_bf16(pp, kBf16OnePair, st.l[h]);
@@ -289,7 +289,7 @@ __device__ __forceinline__ void attend_block(Acc<QT, KT, D, G>& st, const QSrc& 
         }
     }
 
-    if (n_valid < kBlockSize) {
+    if (n_valid < kUnitTokens) {
 #pragma unroll
         for (int c = 0; c < S::NCH; c++) pv_load<QT, KT, D, G>(st, c, mask_tail<QT, KT, D, G>(vb[c], c, n_valid), pps, ps);
     } else {
@@ -310,7 +310,7 @@ __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int c)
 
 __device__ __forceinline__ int seq_ctx(const DecodeArgs& a, int s) { return clamp_ctx(a, a.context_lens[s]); }
 
-__device__ __forceinline__ int nblocks(int ctx) { return (ctx + kBlockSize - 1) / kBlockSize; }
+__device__ __forceinline__ int nblocks(int ctx) { return (ctx + kUnitTokens - 1) / kUnitTokens; }
 
 __device__ __forceinline__ int wave_incl_scan(int x, int lane)
 {
@@ -456,20 +456,20 @@ __device__ __forceinline__ void append_chunk_tokens(const DecodeArgs& a, const i
     constexpr int N = 16 / ES;  // source elements per piece
     constexpr int P = D / N;    // pieces per source row
     static_assert(2 * P <= 64, "the K and V rows of a token fit one wave");
-    const int Hkv = a.num_kv_heads, NS = a.num_seqs;
+    const int Hkv = a.num_kv_heads, NS = a.num_seqs, B = a.block_size;
     Cursor c = cursor_at(p0, lctx);
     bool stored = false;
     while (c.s < NS && c.run_start + c.nbs <= u_end) {  // this run ends inside the chunk
         const int t = c.ctx - 1;
-        const int phys = a.block_tables[(int64_t)c.s * a.max_blocks_per_seq + t / kBlockSize];
+        const int phys = a.block_tables[(int64_t)c.s * a.max_blocks_per_seq + t / B];
         if (lane < 2 * P && phys >= 0 && (int64_t)phys < a.num_blocks) {
             const int kv = lane / P, piece = lane % P;
             const unsigned char* src = static_cast<const unsigned char*>(kv ? a.new_value : a.new_key) +
                                        (((int64_t)c.s * Hkv + c.g) * D + piece * N) * ES;
-            const int64_t tile = ((int64_t)phys * Hkv + c.g) * kBlockSize * D;
+            const int64_t tile = ((int64_t)phys * Hkv + c.g) * B * D;
             unsigned char* pool = static_cast<unsigned char*>(kv ? a.v_pool : a.k_pool);
             const float sc = kIsFp8<CT> && ST != CT ? (kv ? a.v_scale : a.k_scale)[c.g] : 1.0f;
-            store_kv_piece<ST, CT>(load16(src), pool, tile, piece * N, t % kBlockSize, kv, D, kBlockSize, sc);
+            store_kv_piece<ST, CT>(load16(src), pool, tile, piece * N, t % B, kv, D, B, sc);
         }
         stored = true;
         next_run(c, lctx, NS, Hkv);
@@ -559,7 +559,13 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) voi
 
     const unsigned char* kpool = static_cast<const unsigned char*>(a.k_pool);
     const unsigned char* vpool = static_cast<const unsigned char*>(a.v_pool);
-    const int64_t block_stride = (int64_t)Hkv * S::TILE;
+    // A block of B = 16 << ub tokens is 1 << ub units.  Unit `sub` of a block: its K slices are
+    // 1 KiB pieces at sub * 1 KiB + c * (B * 64) of the block's tile, its V loads the
+    // sub-th run of TILE bytes (the pool layout of include/pagedattn.h).
+    const int ub = a.block_size > kUnitTokens ? 1 : 0;
+    const int btile = S::TILE << ub;  // bytes of one (block, kv head) tile
+    const int kstride = a.block_size * 64;
+    const int64_t block_stride = (int64_t)Hkv * btile;
     const int32_t* tables = a.block_tables;
     const int mbps = a.max_blocks_per_seq;
 
@@ -572,10 +578,11 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) voi
         // last block, whose entry then feeds the fill-in loads past the end)
         Cursor tc = cursor_at(p0, lctx);
         int tcount = 0;
-        auto fetch_entry = [&](int& e, int& nv, int& g) {
-            e = tables[(int64_t)tc.s * mbps + tc.j];
-            nv = min(kBlockSize, tc.ctx - tc.j * kBlockSize);
+        auto fetch_entry = [&](int& e, int& nv, int& g, int& sub) {
+            e = tables[(int64_t)tc.s * mbps + (tc.j >> ub)];
+            nv = min(kUnitTokens, tc.ctx - tc.j * kUnitTokens);
             g = tc.g;
+            sub = tc.j & ub;
             if (tcount + 1 < n) {
                 cursor_next(tc, lctx, NS, Hkv);
                 ++tcount;
@@ -585,10 +592,11 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) voi
         Cursor cc = cursor_at(p0, lctx);
         int piece_j0 = cc.j;
 
-        // entry ring: physical id, valid tokens and kv head of blocks t .. t+NST-1
-        int ent[NST], ent_nv[NST], ent_g[NST];
+        // entry ring: physical id, valid tokens, kv head and unit of the block, for units
+        // t .. t+NST-1
+        int ent[NST], ent_nv[NST], ent_g[NST], ent_sub[NST];
 #pragma unroll
-        for (int i = 0; i < NST; i++) fetch_entry(ent[i], ent_nv[i], ent_g[i]);
+        for (int i = 0; i < NST; i++) fetch_entry(ent[i], ent_nv[i], ent_g[i], ent_sub[i]);
 
         auto query_row = [&](const Cursor& c) {
             return static_cast<const unsigned char*>(a.query) + ((int64_t)c.s * a.num_heads + (int64_t)c.g * G) * D * S::QB;
@@ -688,15 +696,17 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) voi
                     const bool bad = phys < 0 || (int64_t)phys >= a.num_blocks;
                     phys = bad ? 0 : phys;
                     kv_nv[i] = bad ? 0 : ent_nv[i];
-                    const int window = bad || t >= n ? 0 : S::TILE;
-                    const int64_t off = (int64_t)phys * block_stride + (int64_t)ent_g[i] * S::TILE;
-                    const TileWindow kw(kpool + off, window), vw(vpool + off, window);
+                    const bool none = bad || t >= n;
+                    const int sub = ent_sub[i];
+                    const int64_t off = (int64_t)phys * block_stride + (int64_t)ent_g[i] * btile;
+                    const TileWindow kw(kpool + off + sub * 1024, none ? 0 : btile - sub * 1024);
+                    const TileWindow vw(vpool + off + sub * S::TILE, none ? 0 : S::TILE);
 #pragma unroll
-                    for (int c = 0; c < S::NCH; c++) kb[i][c] = kw.load_stream(lane * 16 + c * 1024);
+                    for (int c = 0; c < S::NCH; c++) kb[i][c] = kw.load_stream(lane * 16, c * kstride);
 #pragma unroll
                     for (int c = 0; c < S::NCH; c++) vb[i][c] = vw.load_stream(lane * 16 + c * 1024);
                 }
-                fetch_entry(ent[i], ent_nv[i], ent_g[i]);
+                fetch_entry(ent[i], ent_nv[i], ent_g[i], ent_sub[i]);
 
                 const int ta = t - (NST - 1);
                 if (ta >= 0 && ta < n) {

@@ -188,9 +188,10 @@ struct TileWindow {
         : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000))
     {
     }
-    __device__ __forceinline__ uint4 load_stream(int offset) const
+    // bytes offset + soffset (offset per lane, soffset wave-uniform)
+    __device__ __forceinline__ uint4 load_stream(int offset, int soffset = 0) const
     {
-        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, kBufferNontemporal);
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, offset, soffset, kBufferNontemporal);
         return make_uint4(v.x, v.y, v.z, v.w);
     }
     static constexpr int kBufferNontemporal = 2;  // the cache-policy bit printed as "nt"

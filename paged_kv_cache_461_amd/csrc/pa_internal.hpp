@@ -6,7 +6,10 @@
 
 namespace pa {
 
-constexpr int kBlockSize = 16;      // tokens per KV block handled by the kernels
+// The attention kernels work in units of 16 tokens of one kv head: a 16-token block, or one
+// half of a 32-token block (the pool layout puts a 32-token block's two halves at fixed
+// offsets inside its tile).
+constexpr int kUnitTokens = 16;
 constexpr int kDecodeThreads = 256; // 4 waves per decode workgroup
 constexpr int kDecodeWaves = 4;
 
@@ -46,6 +49,7 @@ struct DecodeArgs {
     int32_t num_seqs;
     int32_t num_heads;
     int32_t num_kv_heads;
+    int32_t block_size;  // 16 or 32 tokens
     float scale_log2;  // softmax scale times log2(e): scores are kept in base 2
     const float* k_scale;
     const float* v_scale;
@@ -77,6 +81,7 @@ struct PrefillArgs {
     int32_t num_query_rows;
     int32_t num_heads;
     int32_t num_kv_heads;
+    int32_t block_size;  // 16 or 32 tokens
     int32_t row_blocks;  // workgroup row blocks per (sequence, kv head)
     int32_t num_splits;  // key ranges per row block
     int32_t split_keys;  // keys per range; 0 = each row block's keys cut into num_splits parts
@@ -89,11 +94,12 @@ struct PrefillArgs {
 
 hipError_t launch_kv_write(int src_dtype, int cache_dtype, const KvWriteArgs& a, hipStream_t stream);
 
-// phase 1 = streaming kernel, 2 = merge kernel, 3 = both.  Returns hipErrorInvalidValue when
-// no kernel exists for the combination.
 // Waves per SIMD the streaming kernel of this variant is built for (2 or 3); the persistent
 // grid has that many waves per SIMD.
 int decode_waves_per_simd(int q_dtype, int cache_dtype, int head_dim, int gqa);
+
+// phase 1 = streaming kernel, 2 = merge kernel, 3 = both.  Returns hipErrorInvalidValue when
+// no kernel exists for the combination.
 hipError_t launch_decode(int phase, int q_dtype, int cache_dtype, int head_dim, int gqa,
                          const DecodeArgs& a, hipStream_t stream);
 

@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
 {
     using L = PfLds<D>;
     constexpr int EB = kIsFp8<KT> ? 1 : 2;
-    constexpr int TILE_BYTES = kBlockSize * D * EB;  // one (block, kv head) tile
+    constexpr int TILE_BYTES = kUnitTokens * D * EB;  // one 16-token unit of one kv head
     constexpr int CH_PER_TILE = TILE_BYTES / 16;     // 16-byte pieces per tile
     constexpr int NCH = 4 * CH_PER_TILE / kPrefillThreads;  // K (and V) pieces per thread per iteration
     constexpr int ROWS = kPfWaves * R * 16;          // stacked rows per workgroup
@@ -221,13 +221,18 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
     // next load() needs, unconditionally (the index is clamped to the range's last block), so
     // a K/V load never waits on a table read.
     static_assert(CH_PER_TILE % 64 == 0, "wave-uniform block per piece");
-    const int last_blk = kstop > 0 ? (kstop - 1) >> 4 : 0;
+    // A block of 16 << ub tokens holds 1 << ub units; unit u of the range is unit u & ub of
+    // table entry u >> ub.  Inside a 32-token block's tile, unit `sub` has its K slices at
+    // sub * 1 KiB + slice * (B * 64) and its V at sub * TILE_BYTES (include/pagedattn.h).
+    const int ub = a.block_size > kUnitTokens ? 1 : 0;
+    const int kstride = a.block_size * 64;
+    const int last_unit = kstop > 0 ? (kstop - 1) >> 4 : 0;
     int ent[NCH];
     auto fetch_entries = [&](int kbase) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < NCH; j++) {
             const int b = __builtin_amdgcn_readfirstlane((tid + kPrefillThreads * j) / CH_PER_TILE);
-            ent[j] = table[min((kbase >> 4) + b, last_blk)];
+            ent[j] = table[min((kbase >> 4) + b, last_unit) >> ub];
         }
     };
     auto load = [&](auto set_tag, int kbase) __attribute__((always_inline)) {
@@ -241,9 +246,10 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
             const int phys = __builtin_amdgcn_readfirstlane(ent[j]);
             const bool ok = kbase + 16 * b < kstop && phys >= 0 && (int64_t)phys < a.num_blocks;
             // a block with no valid entry still reads block 0 (the pool has one); store() zeroes it
-            const int64_t base = ((int64_t)(ok ? phys : 0) * a.num_kv_heads + g) * TILE_BYTES + off;
-            kr[SET][j] = load16(kpool + base);
-            vr[SET][j] = load16(vpool + base);
+            const int sub = ((kbase >> 4) + b) & ub;
+            const int64_t tile = ((int64_t)(ok ? phys : 0) * a.num_kv_heads + g) * (TILE_BYTES << ub);
+            kr[SET][j] = load16(kpool + tile + sub * 1024 + (off >> 10) * kstride + (off & 1023));
+            vr[SET][j] = load16(vpool + tile + sub * TILE_BYTES + off);
             okbits[SET] |= ok ? 1u << j : 0u;
         }
         fetch_entries(kbase + kPfKeys);  // for the next load, one compute phase away

@@ -399,24 +399,24 @@ def tiny_fp32(seed=0) -> PagedBatch:
                        q_dtype=F32, cache_dtype=F32, seed=seed, num_blocks=32, name="tiny_fp32")
 
 
-def llama3_8b_decode(seed=0, num_seqs=64, ctx_range=(512, 4096), layer=0) -> PagedBatch:
+def llama3_8b_decode(seed=0, num_seqs=64, ctx_range=(512, 4096), layer=0, block_size=16) -> PagedBatch:
     """Llama-3-8B-shaped decode layer: 64 sequences, contexts uniform in [512, 4096],
     32 query / 8 KV heads, head dim 128, bf16, 16-token blocks, pool = used blocks + 10%."""
     rng = np.random.default_rng([seed, 100, 9999])
     ctx = rng.integers(ctx_range[0], ctx_range[1] + 1, size=num_seqs)
-    return build_batch(ctx, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16, q_dtype=BF16,
+    return build_batch(ctx, num_heads=32, num_kv_heads=8, head_dim=128, block_size=block_size, q_dtype=BF16,
                        cache_dtype=BF16, seed=seed, layer=layer, name="llama3_8b_decode")
 
 
-def long_context(seed=0, num_seqs=16, ctx=8192, layer=0) -> PagedBatch:
+def long_context(seed=0, num_seqs=16, ctx=8192, layer=0, block_size=16) -> PagedBatch:
     """Long-context split-K decode: 16 sequences of 8192 tokens (512 scattered blocks
     each), 32 query / 8 KV heads, head dim 128, bf16; one layer of the 32."""
-    return build_batch([ctx] * num_seqs, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+    return build_batch([ctx] * num_seqs, num_heads=32, num_kv_heads=8, head_dim=128, block_size=block_size,
                        q_dtype=BF16, cache_dtype=BF16, seed=seed, layer=layer, name="long_context")
 
 
 def mixed_continuous_batch(seed=0, num_seqs=256, num_sharing=64, prefix=2048,
-                           median=1024, sigma=1.0, clip=(32, 32768), layer=0) -> PagedBatch:
+                           median=1024, sigma=1.0, clip=(32, 32768), layer=0, block_size=16) -> PagedBatch:
     """Continuous-batching decode step: 256 sequences with log-normal contexts (median
     1024, sigma 1.0, clipped to [32, 32768]); 64 of them share a 2048-token prefix through
     the same leading physical blocks (refcount 64) and extend it by their own log-normal
@@ -426,14 +426,14 @@ def mixed_continuous_batch(seed=0, num_seqs=256, num_sharing=64, prefix=2048,
     sharing = np.sort(rng.choice(num_seqs, size=num_sharing, replace=False))
     ctx = own.astype(np.int64)
     ctx[sharing] = np.minimum(prefix + ctx[sharing], clip[1])
-    return build_batch(ctx, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16, q_dtype=BF16,
+    return build_batch(ctx, num_heads=32, num_kv_heads=8, head_dim=128, block_size=block_size, q_dtype=BF16,
                        cache_dtype=BF16, seed=seed, layer=layer, shared_prefix_len=prefix,
                        sharing=sharing, name="mixed_continuous_batch")
 
 
 def fp8_chunked_prefill(seed=0, num_decode=128, chunk=512, chunk_ctx=8192,
                         decode_range=(256, 8192), layer=0, cache_dtype=FP8_E4M3, fp8_scale="head",
-                        name="fp8_chunked_prefill") -> PagedBatch:
+                        name="fp8_chunked_prefill", block_size=16) -> PagedBatch:
     """fp8 KV cache (E4M3 unless cache_dtype says E5M2) with per-(layer, kv head) scales
     (fp8_scale="tensor": one scale per layer, repeated per head): sequence 0 is a 512-row prefill
     chunk that is the last 512 positions of an 8192-token context; sequences 1..128 are
@@ -443,7 +443,7 @@ def fp8_chunked_prefill(seed=0, num_decode=128, chunk=512, chunk_ctx=8192,
     dec = rng.integers(decode_range[0], decode_range[1] + 1, size=num_decode)
     ctx = np.concatenate([[chunk_ctx], dec])
     ql = np.concatenate([[chunk], np.ones(num_decode, np.int64)])
-    return build_batch(ctx, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16, q_dtype=BF16,
+    return build_batch(ctx, num_heads=32, num_kv_heads=8, head_dim=128, block_size=block_size, q_dtype=BF16,
                        cache_dtype=cache_dtype, src_dtype=BF16, seed=seed, layer=layer, query_lens=ql,
                        name=name, fp8_scale=fp8_scale)
 
@@ -455,6 +455,7 @@ WORKLOADS = {
     "mixed_continuous_batch": mixed_continuous_batch,
     "fp8_chunked_prefill": fp8_chunked_prefill,
     # the same step over an E5M2 cache with one scale per layer (per-tensor)
-    "fp8_e5m2_chunked_prefill": lambda seed=0, layer=0: fp8_chunked_prefill(
-        seed=seed, layer=layer, cache_dtype=FP8_E5M2, fp8_scale="tensor", name="fp8_e5m2_chunked_prefill"),
+    "fp8_e5m2_chunked_prefill": lambda seed=0, layer=0, block_size=16: fp8_chunked_prefill(
+        seed=seed, layer=layer, cache_dtype=FP8_E5M2, fp8_scale="tensor", name="fp8_e5m2_chunked_prefill",
+        block_size=block_size),
 }

@@ -74,7 +74,9 @@ def _decode(lib, **kw):
     (dict(Hq=30), ops.PA_ERR_INVALID_ARG),                  # 30 % 8 != 0
     (dict(Hq=24, Hkv=2), ops.PA_ERR_UNSUPPORTED),            # GQA 12
     (dict(D=96), ops.PA_ERR_UNSUPPORTED),
-    (dict(B=32), ops.PA_ERR_UNSUPPORTED),
+    (dict(B=8), ops.PA_ERR_UNSUPPORTED),
+    (dict(B=64), ops.PA_ERR_UNSUPPORTED),
+    (dict(B=32, P=48), ops.PA_ERR_INVALID_ARG),              # partition not a multiple of the block
     (dict(q_dtype=F32), ops.PA_ERR_UNSUPPORTED),             # f32 q over a bf16 cache
     (dict(q_dtype=FP8, cache_dtype=FP8), ops.PA_ERR_INVALID_ARG),
     (dict(cache_dtype=FP8), ops.PA_ERR_INVALID_ARG),         # fp8 without scales
@@ -97,6 +99,12 @@ def _decode(lib, **kw):
 def test_decode_rejects_before_launch(lib, kw, status):
     assert _decode(lib, **kw) == status
     assert lib.pa_last_error() != b""
+
+
+def test_decode_accepts_32_token_blocks(lib):
+    """Block size 32 passes the host checks (with a table long enough for it); the call then
+    stops at the workspace check, before any launch."""
+    assert _decode(lib, B=32, mbps=128, ws=None, ws_bytes=0) == ops.PA_ERR_WORKSPACE
 
 
 def test_decode_empty_batch_is_ok_without_launch(lib):

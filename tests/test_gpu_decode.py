@@ -52,6 +52,17 @@ def test_bf16_shapes(gqa, head_dim):
     step_and_compare(b, partition_size=256)
 
 
+@pytest.mark.parametrize("cache", [W.BF16, W.FP8_E4M3, W.FP8_E5M2, W.F32])
+@pytest.mark.parametrize("P", [0, 32, 256])
+def test_block_size_32(cache, P):
+    """32-token blocks: each block is two 16-token units at fixed offsets of its tile; ragged
+    contexts end in either half, and partitions of one block split runs inside a block pair."""
+    q = W.F32 if cache == W.F32 else W.BF16
+    b = W.build_batch([1, 15, 16, 17, 31, 32, 33, 100, 511, 1000], num_heads=16, num_kv_heads=4, head_dim=128,
+                      block_size=32, q_dtype=q, cache_dtype=cache, seed=32 + P)
+    step_and_compare(b, partition_size=P)
+
+
 @pytest.mark.parametrize("gqa", [1, 4, 8])
 def test_fp32_shapes(gqa):
     hkv = 2
@@ -248,14 +259,15 @@ def _fused(db, k_pool, v_pool, partition_size=0):
     return out
 
 
-@pytest.mark.parametrize("cache,P", [(W.BF16, 0), (W.BF16, 16), (W.BF16, 256), (W.FP8_E4M3, 0), (W.FP8_E4M3, 64),
-                                     (W.FP8_E5M2, 0), (W.F32, 0), (W.F32, 32)])
-def test_fused_append_equals_separate_calls(cache, P):
+@pytest.mark.parametrize("cache,P,B", [(W.BF16, 0, 16), (W.BF16, 16, 16), (W.BF16, 256, 16), (W.FP8_E4M3, 0, 16),
+                                       (W.FP8_E4M3, 64, 16), (W.FP8_E5M2, 0, 16), (W.F32, 0, 16), (W.F32, 32, 16),
+                                       (W.BF16, 0, 32), (W.FP8_E4M3, 32, 32)])
+def test_fused_append_equals_separate_calls(cache, P, B):
     """pa_paged_attention_decode_append writes the same pool bytes as pa_kv_cache_write and
     returns the same output bits as the decode that follows it; both match the oracle."""
     q = W.F32 if cache == W.F32 else W.BF16
     b = W.build_batch([1, 16, 17, 40, 333, 1000, 2048], num_heads=16, num_kv_heads=4, head_dim=128, q_dtype=q,
-                      cache_dtype=cache, seed=21)
+                      cache_dtype=cache, seed=21, block_size=B)
     kp_h, vp_h = oracle_pool(b, include_new=False)
     db = DeviceBatch(b)
     kp1, vp1 = to_dev(kp_h, cache), to_dev(vp_h, cache)

@@ -50,6 +50,16 @@ def test_mixed_chunks(cache, gqa, head_dim):
     prefill_and_compare(b)
 
 
+@pytest.mark.parametrize("cache", [W.BF16, W.FP8_E4M3])
+@pytest.mark.parametrize("P", [0, 32, 96])
+def test_block_size_32(cache, P):
+    """32-token blocks: a 64-key iteration spans two blocks (four 16-token units); split
+    ranges of 32 / 96 keys start in either half of a block pair."""
+    b = W.build_batch(MIXED[0], num_heads=16, num_kv_heads=4, head_dim=128, block_size=32, q_dtype=W.BF16,
+                      cache_dtype=cache, seed=320 + P, query_lens=MIXED[1])
+    prefill_and_compare(b, partition_size=P)
+
+
 @pytest.mark.parametrize("P", [16, 48, 64, 256, 1024, 0])
 def test_split_k_partition_sweep(P):
     """Fixed key ranges of every size (one block .. no split) give the same rows."""
