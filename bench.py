@@ -51,7 +51,7 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="llama3_8b_decode",
                    choices=["llama3_8b_decode", "long_context", "mixed_continuous_batch", "fp8_chunked_prefill",
-                            "fp8_e5m2_chunked_prefill"])
+                            "fp8_e5m2_chunked_prefill", "tiny_fp32"])
     p.add_argument("--layers", type=int, default=2, help="layer pools cycled through (>= 2)")
     p.add_argument("--partition-size", type=int, default=0, help="split-K partition (0 = library's choice)")
     p.add_argument("--block-size", type=int, default=16, choices=[16, 32],
@@ -62,6 +62,8 @@ def parse_args():
                    help="second workload measured in the same run and reported under extra_step")
     p.add_argument("--fused-append", action="store_true",
                    help="decode rows append their new token inside the decode call (pa_paged_attention_decode_append)")
+    p.add_argument("--graph", action="store_true",
+                   help="also replay the step from HIP graphs and report it under graph_step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device copy (HBM counter calibration) and exit")
@@ -128,6 +130,11 @@ def source_digest(kernel="decode"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
+
+
+def traffic_key(batch):
+    """Counter records are kept per workload, and per block size when it is not 16."""
+    return batch.name if batch.block_size == 16 else "%s/b%d" % (batch.name, batch.block_size)
 
 
 def stored_traffic(workload, digest, kernel="decode"):
@@ -219,11 +226,12 @@ def cpu_baseline(batch, min_seconds=1.5):
             "seconds_per_step": dt, "seqs_per_s_per_layer": batch.num_seqs / dt}
 
 
-def measure(batch, dev, layers, steps, warmup, partition_size=0, fused=False):
+def measure(batch, dev, layers, steps, warmup, partition_size=0, fused=False, graph=False):
     """Fill the pools, time `steps` steps after `warmup` untimed ones, then time each kernel of
     the step alone; returns the result fields for this workload.  fused: decode rows append
     their new token inside the decode call (pa_paged_attention_decode_append); otherwise every
-    new row goes through pa_kv_cache_write first."""
+    new row goes through pa_kv_cache_write first.  graph: also time the step captured in HIP
+    graphs (one per layer pool) and replayed."""
     import torch
 
     from paged_kv_cache_461_amd import ops
@@ -254,6 +262,7 @@ def measure(batch, dev, layers, steps, warmup, partition_size=0, fused=False):
     pf_ws = ops.chunked_prefill_workspace(Rp, Sp, pf_max_q, Hq, Hkv, D, pf_max_ctx, B, 0, device=dev) if Sp else None
     outs = [torch.empty_like(p[3]) for p in pools]
     stream = torch.cuda.current_stream()
+    cur = [stream]  # the launch stream (the capture stream while a graph is recorded)
 
     # rows appended by pa_kv_cache_write: all of them, or only the chunk rows when the decode
     # call appends its own
@@ -262,19 +271,19 @@ def measure(batch, dev, layers, steps, warmup, partition_size=0, fused=False):
     def write(r):
         kp, vp, (nk, nv, nslots), q, ks, vs = pools[r % len(pools)]
         ops.kv_cache_write(nk[:Rw], nv[:Rw], kp, vp, nslots[:Rw], num_kv_heads=Hkv, head_dim=D, block_size=B,
-                           k_scale=ks, v_scale=vs, stream=stream)
+                           k_scale=ks, v_scale=vs, stream=cur[0])
 
     def prefill(r):
         kp, vp, _, q, ks, vs = pools[r % len(pools)]
         ops.paged_attention_chunked_prefill(outs[r % len(pools)][:Rp], q[:Rp], cu[:Sp + 1], kp, vp, tables[:Sp],
                                             ctx[:Sp], max_query_len=pf_max_q, max_context_len=pf_max_ctx,
                                             num_kv_heads=Hkv, scale=batch.scale, block_size=B, k_scale=ks,
-                                            v_scale=vs, workspace=pf_ws, stream=stream)
+                                            v_scale=vs, workspace=pf_ws, stream=cur[0])
 
     def decode(r, phase=3):
         kp, vp, (nk, nv, _), q, ks, vs = pools[r % len(pools)]
         common = dict(max_context_len=dec_max_ctx, num_kv_heads=Hkv, scale=batch.scale, block_size=B, k_scale=ks,
-                      v_scale=vs, partition_size=P, workspace=ws, phase=phase, stream=stream)
+                      v_scale=vs, partition_size=P, workspace=ws, phase=phase, stream=cur[0])
         if fused:
             ops.paged_attention_decode_append(outs[r % len(pools)][Rp:], q[Rp:], nk[Rp:].view(Sd, Hkv, D),
                                               nv[Rp:].view(Sd, Hkv, D), kp, vp, tables[Sp:], ctx[Sp:], **common)
@@ -304,6 +313,36 @@ def measure(batch, dev, layers, steps, warmup, partition_size=0, fused=False):
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / steps
 
+    graph_res = None
+    if graph:
+        # The same K steps replayed from HIP graphs: one graph per layer pool, each holding one
+        # whole step (its launches record no memset and allocate nothing).
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            cur[0] = side
+            step(0)  # warm the side stream before capture
+            for r in range(len(pools)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    step(r)
+                graphs.append(g)
+        cur[0] = stream
+        torch.cuda.synchronize()
+        for i in range(max(warmup, 1)):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for i in range(steps):
+            graphs[i % len(graphs)].replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        gms = g0.elapsed_time(g1) / steps
+        graph_res = {"ms_per_step": round(gms, 5), "value": None, "replays": steps,
+                     "what": "the same steps replayed from HIP graphs (one per layer pool)"}
+
     # Profiled pass: each kernel of the step launched K times back to back (cycling the layer
     # pools as in the step) between two HIP events on the launch stream; the average is the
     # kernel's launch duration plus the inter-kernel gap, with no event inside a launch pair.
@@ -326,13 +365,17 @@ def measure(batch, dev, layers, steps, warmup, partition_size=0, fused=False):
         kernels["chunked_prefill"] = round(launches(prefill, steps), 2)
     if Sd:
         kernels["decode_stream"] = round(launches(lambda r: decode(r, 1), steps), 2)
-        kernels["decode_merge"] = round(launches(lambda r: decode(steps - 1, 2), steps), 2)
+        if ws is not None:  # no workspace: one chunk per run, the merge phase launches nothing
+            kernels["decode_merge"] = round(launches(lambda r: decode(steps - 1, 2), steps), 2)
     kernels["timing"] = ("K back-to-back launches of each kernel between two HIP events on the launch stream, "
                          "after the timed region" + ("; decode_stream includes the fused append of the decode "
                                                      "rows' new tokens" if fused and Sd else ""))
 
     step_bytes = batch.decode_bytes() + batch.write_bytes()
     value = step_bytes / (ms_per_step * 1e-3) / 1e12
+    if graph_res is not None:
+        graph_res["value"] = round(step_bytes / (graph_res["ms_per_step"] * 1e-3) / 1e12, 4)
+        graph_res["seqs_per_s_per_layer"] = round(S / (graph_res["ms_per_step"] * 1e-3), 1)
     digest = source_digest("decode")
     eq = W.ELEM_BYTES[batch.q_dtype]
     res = {
@@ -362,6 +405,8 @@ def measure(batch, dev, layers, steps, warmup, partition_size=0, fused=False):
         "step_bytes": int(step_bytes),
         "kernels_us": kernels,
     }
+    if graph_res is not None:
+        res["graph_step"] = graph_res
     if Sp:
         res["config"]["prefill_rows"] = Rp
     if Sd:
@@ -374,7 +419,7 @@ def measure(batch, dev, layers, steps, warmup, partition_size=0, fused=False):
         achieved = part_bytes / (kernels["decode_stream"] * 1e-6) / 1e9
         res["roofline"] = {"bound": "hbm", "kernel": "decode_stream_kernel", "achieved": round(achieved, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                           "traffic": stored_traffic(batch.name, digest),
+                           "traffic": stored_traffic(traffic_key(batch), digest),
                            "algorithmic_bytes_per_launch": int(part_bytes), "source_digest": digest}
     if Sp:
         pos = [np.arange(c - q, c, dtype=np.int64) for c, q in zip(batch.context_lens[:Sp], ql[:Sp])]
@@ -384,7 +429,7 @@ def measure(batch, dev, layers, steps, warmup, partition_size=0, fused=False):
         res["roofline_prefill"] = {"bound": "mfma", "kernel": "prefill_kernel (+ merge)",
                                    "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                    "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                                   "traffic": stored_traffic(batch.name, source_digest("prefill"), "prefill"),
+                                   "traffic": stored_traffic(traffic_key(batch), source_digest("prefill"), "prefill"),
                                    "algorithmic_flops_per_launch": flops, "source_digest": source_digest("prefill")}
     if "roofline" not in res:
         res["roofline"] = dict(res["roofline_prefill"])
@@ -415,7 +460,8 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     batch = make_batch(args.workload, args.block_size)
-    res, stream = measure(batch, dev, args.layers, args.steps, args.warmup, args.partition_size, args.fused_append)
+    res, stream = measure(batch, dev, args.layers, args.steps, args.warmup, args.partition_size, args.fused_append,
+                          args.graph)
     if args.extra_workload != "none" and args.extra_workload != args.workload:
         # The rest of the hot path in the same run: the fp8 cache (in-kernel dequant) and the
         # chunked-prefill kernel, on the mixed step (one layer).

@@ -108,8 +108,9 @@ int32_t pa_kv_cache_write(const void* key, const void* value, int32_t src_dtype,
 /*
  * Bytes of device workspace that pa_paged_attention_decode needs for these arguments
  * (partition_size 0 = automatic work split).  Depends only on the shapes, never on the
- * context lengths' values; 0 only for an empty batch.  Returns -1 for arguments the decode
- * call would reject.
+ * context lengths' values.  0 for an empty batch, and for an automatic split when
+ * max_context_len <= 128: every sequence then fits in one work chunk, nothing is split and no
+ * merge runs.  Returns -1 for arguments the decode call would reject.
  */
 int64_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size, int32_t max_context_len,
@@ -129,10 +130,11 @@ int64_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t nu
  *   k_scale, v_scale device fp32 [num_kv_heads] for an fp8 cache (the stored code times
  *                  the scale is the cached value), else NULL.
  *   partition_size 0 = automatic, else a multiple of block_size.  The work is the list of
- *                  every (sequence, kv head) pair's blocks laid end to end; it is cut into
- *                  chunks of partition_size / block_size blocks (automatic: equal chunks, one per
- *                  wave of a grid sized to fill the GPU), each chunk is attended independently
- *                  per sequence piece, and the pieces of a sequence are merged (split-K).  The
+ *                  every (sequence, kv head) pair's 16-token units laid end to end; it is cut
+ *                  into chunks of partition_size / 16 units (automatic: equal chunks, one per
+ *                  wave of a grid sized to fill the GPU; or, when max_context_len <= 128, one
+ *                  chunk per (sequence, kv head)), each chunk is attended independently per
+ *                  sequence piece, and the pieces of a sequence are merged (split-K).  The
  *                  result does not depend on the split beyond rounding.
  *   workspace      device scratch of at least pa_decode_workspace_size(...) bytes, 256-byte
  *                  aligned.  Contents need no initialisation and are undefined afterwards.

@@ -52,7 +52,7 @@ constexpr int64_t kWorkspaceAlign = 256;
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 struct DecodePlan {
-    int32_t chunk_blocks;  // 0 = balanced over the grid
+    int32_t chunk_blocks;  // 0 = balanced over the grid, -1 = one chunk per run
     int32_t grid_workgroups;
     int64_t max_chunks, max_pieces;
     int64_t o_bytes, ml_bytes, info_bytes;  // workspace regions, in this order
@@ -77,6 +77,14 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
         pl.chunk_blocks = partition_size / pa::kUnitTokens;
         pl.max_chunks = (umax + pl.chunk_blocks - 1) / pl.chunk_blocks;
         waves = pl.max_chunks < stream_waves ? pl.max_chunks : stream_waves;
+    } else if ((max_context_len + pa::kUnitTokens - 1) / pa::kUnitTokens <= pa::kMinChunkBlocks) {
+        // every run fits in one minimum chunk: one chunk per run, no split, no merge, no workspace
+        pl.chunk_blocks = -1;
+        const int64_t runs = (int64_t)num_seqs * num_kv_heads;
+        waves = runs < stream_waves ? runs : stream_waves;
+        pl.grid_workgroups = (int32_t)((waves + pa::kDecodeWaves - 1) / pa::kDecodeWaves);
+        pl.max_chunks = runs;
+        return pl;
     } else {
         pl.chunk_blocks = 0;
         const int64_t need = (umax + pa::kMinChunkBlocks - 1) / pa::kMinChunkBlocks;

@@ -549,13 +549,18 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) voi
     const int64_t first = (gridDim.x & 7) == 0
                               ? 8 * kDecodeWaves * (int64_t)(blockIdx.x >> 3) + 8 * wave_in_wg + (blockIdx.x & 7)
                               : w;
+    // chunk_blocks < 0: one chunk per run.  The host picks it when every run fits in one
+    // minimum chunk, so no run is split, nothing is merged and the merge launch is skipped
+    // (small batches, where a launch costs more than the work).  Chunk k is then run k.
+    const bool per_run = a.chunk_blocks < 0;
     ChunkMap cm{};
-    const Plan pl = plan_wave(a, lctx, lane, [&](int64_t U) {
+    const Plan pl = per_run ? Plan{0, Pos{NS, 0, 0, 0}} : plan_wave(a, lctx, lane, [&](int64_t U) {
         cm.C = a.chunk_blocks > 0 ? (int64_t)a.chunk_blocks : max((U + NW - 1) / NW, (int64_t)kMinChunkBlocks);
         return cm.start(first);
     });
     const int64_t U = pl.U;
-    const int64_t nchunks = U > 0 ? min(cm.of_unit(U - 1) + 1, a.max_chunks) : 0;
+    const int64_t nchunks =
+        per_run ? (int64_t)NS * Hkv : (U > 0 ? min(cm.of_unit(U - 1) + 1, a.max_chunks) : 0);
 
     const unsigned char* kpool = static_cast<const unsigned char*>(a.k_pool);
     const unsigned char* vpool = static_cast<const unsigned char*>(a.v_pool);
@@ -570,9 +575,33 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) voi
     const int mbps = a.max_blocks_per_seq;
 
     for (int64_t k = first; k < nchunks; k += NW) {
-        const int n = (int)min(cm.size(k), U - cm.start(k));  // blocks of this chunk (>= 1)
-        const Pos p0 = k == first ? pl.p : plan_wave(a, lctx, lane, [&](int64_t) { return cm.start(k); }).p;
-        if (a.new_key != nullptr) append_chunk_tokens<QT, KT, D>(a, lctx, p0, cm.start(k) + n, lane);
+        int n;           // units of this chunk
+        Pos p0;          // its first unit
+        int64_t u_end;   // list index one past its last unit
+        if (per_run) {
+            p0 = Pos{(int)(k / Hkv), (int)(k % Hkv), 0, 0};
+            n = nblocks(lctx[p0.s]);
+            u_end = n;
+            if (n == 0) {  // empty sequence: zero rows
+#pragma unroll
+                for (int h = 0; h < G; h++) {
+                    const int64_t row = (int64_t)p0.s * a.num_heads + (int64_t)p0.g * G + h;
+#pragma unroll
+                    for (int cg = 0; cg < S::CG; cg++) {
+                        if constexpr (QT == kBF16)
+                            static_cast<uint16_t*>(a.out)[row * D + cg * 64 + lane] = 0;
+                        else
+                            static_cast<float*>(a.out)[row * D + cg * 64 + lane] = 0.0f;
+                    }
+                }
+                continue;
+            }
+        } else {
+            n = (int)min(cm.size(k), U - cm.start(k));  // >= 1
+            p0 = k == first ? pl.p : plan_wave(a, lctx, lane, [&](int64_t) { return cm.start(k); }).p;
+            u_end = cm.start(k) + n;
+        }
+        if (a.new_key != nullptr) append_chunk_tokens<QT, KT, D>(a, lctx, p0, u_end, lane);
 
         // table cursor: the block whose table entry is fetched next (it stops at the chunk's
         // last block, whose entry then feeds the fill-in loads past the end)
@@ -641,7 +670,7 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) voi
             }
             const int64_t run = (int64_t)cc.s * Hkv + cc.g;
             const bool first = piece_j0 == 0, whole = first && cc.j == cc.nbs - 1;
-            if (first && lane == 0) {
+            if (first && lane == 0 && !per_run) {
                 // every run with blocks is entered at its block 0 by exactly one wave, which
                 // records the chunk range covering it for the merge
                 const int64_t k_last = cm.of_unit(cc.run_start + cc.nbs - 1);
@@ -785,7 +814,7 @@ hipError_t launch_phase_t(int phase, const DecodeArgs& a, hipStream_t stream)
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (phase & 2) {
+    if ((phase & 2) && a.chunk_blocks >= 0) {  // one chunk per run: nothing to merge
         const int64_t grid = (int64_t)a.num_seqs * a.num_heads;
         if (grid <= 0) return hipSuccess;
         if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;

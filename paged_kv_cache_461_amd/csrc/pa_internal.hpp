@@ -53,7 +53,8 @@ struct DecodeArgs {
     float scale_log2;  // softmax scale times log2(e): scores are kept in base 2
     const float* k_scale;
     const float* v_scale;
-    int32_t chunk_blocks;     // units per chunk; 0 = ceil(U / waves), at least kMinChunkBlocks
+    int32_t chunk_blocks;     // units per chunk; 0 = ceil(U / waves), at least kMinChunkBlocks;
+                              // -1 = one chunk per run (no split, no merge)
     int32_t grid_workgroups;  // workgroups of the streaming grid (4 waves each)
     int64_t max_chunks;       // chunks the workspace has room for
     int64_t max_pieces;       // pieces the workspace has room for (runs + max_chunks)

@@ -391,11 +391,11 @@ def fp8_calibration_scales(num_kv_heads, head_dim, seed, layer, src_dtype, token
 
 # ---- the five workloads ------------------------------------------------------------------
 
-def tiny_fp32(seed=0) -> PagedBatch:
+def tiny_fp32(seed=0, block_size=16) -> PagedBatch:
     """4 sequences, contexts {17, 33, 64, 100} (the new token included), 8 query / 2 KV
     heads, head dim 64, 16-token blocks, fp32, a 32-block pool handed out by a seeded
     permutation."""
-    return build_batch([17, 33, 64, 100], num_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+    return build_batch([17, 33, 64, 100], num_heads=8, num_kv_heads=2, head_dim=64, block_size=block_size,
                        q_dtype=F32, cache_dtype=F32, seed=seed, num_blocks=32, name="tiny_fp32")
 
 

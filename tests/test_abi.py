@@ -119,6 +119,8 @@ def test_workspace_size(lib):
         runs = S * Hkv
         G = Hq // Hkv
         units = S * Hkv * ((maxctx + 15) // 16)
+        if not P and -(-maxctx // 16) <= 8:
+            return 0  # every run fits one minimum chunk: one chunk per run, nothing to merge
         if P:
             chunks = -(-units // (P // 16))
         else:
@@ -133,6 +135,7 @@ def test_workspace_size(lib):
         S, Hq, Hkv, D, maxctx, P = args
         assert lib.pa_decode_workspace_size(S, Hq, Hkv, D, 16, maxctx, P) == expect(*args), args
     assert lib.pa_decode_workspace_size(0, 32, 8, 128, 16, 4096, 0) == 0
+    assert lib.pa_decode_workspace_size(64, 32, 8, 128, 16, 129, 0) > 0  # 9 units: balanced split
     assert lib.pa_decode_workspace_size(64, 30, 8, 128, 16, 4096, 512) == -1
     assert lib.pa_decode_workspace_size(64, 32, 8, 128, 16, 4096, 24) == -1   # not a multiple of 16
 

@@ -63,6 +63,32 @@ def test_block_size_32(cache, P):
     step_and_compare(b, partition_size=P)
 
 
+@pytest.mark.parametrize("cache", [W.BF16, W.FP8_E4M3, W.F32])
+def test_short_contexts_one_chunk_per_run(cache):
+    """max_context_len <= 128: one chunk per (sequence, kv head), no workspace and no merge.
+    2600 runs outnumber the grid's waves, some sequences are empty (zero rows), and the two
+    phase calls give the one-call bits (the merge phase has nothing to do)."""
+    q = W.F32 if cache == W.F32 else W.BF16
+    rng = np.random.default_rng(5)
+    ctx = rng.integers(1, 129, size=1300)
+    ctx[1] = 128
+    b = W.build_batch(ctx, num_heads=8, num_kv_heads=2, head_dim=128, q_dtype=q, cache_dtype=cache, seed=9)
+    assert ops.decode_workspace(b.num_seqs, 8, 2, 128, b.max_context_len, 16, 0) is None
+    db, kp, vp, _ = step_and_compare(b)
+    ctx0 = b.context_lens.copy()
+    ctx0[::97] = 0
+    db.ctx = torch.from_numpy(ctx0).cuda()
+    one = db.decode(kp, vp)
+    ref = oracle.paged_attention(b.query_raw(), b.q_dtype, to_host_raw(kp), to_host_raw(vp), b.cache_dtype,
+                                 b.block_tables, ctx0, 8, 2, 128, 16, b.scale, k_scale=b.k_scale, v_scale=b.v_scale)
+    assert_close(b, out_to_f64(one), ref)
+    assert torch.count_nonzero(one[::97].float()) == 0
+    two = torch.full_like(one, 7)
+    db.decode(kp, vp, phase=1, out=two, workspace=None)
+    db.decode(kp, vp, phase=2, out=two, workspace=None)
+    assert np.array_equal(to_host_raw(one).view(np.uint8), to_host_raw(two).view(np.uint8))
+
+
 @pytest.mark.parametrize("gqa", [1, 4, 8])
 def test_fp32_shapes(gqa):
     hkv = 2
@@ -259,15 +285,18 @@ def _fused(db, k_pool, v_pool, partition_size=0):
     return out
 
 
-@pytest.mark.parametrize("cache,P,B", [(W.BF16, 0, 16), (W.BF16, 16, 16), (W.BF16, 256, 16), (W.FP8_E4M3, 0, 16),
-                                       (W.FP8_E4M3, 64, 16), (W.FP8_E5M2, 0, 16), (W.F32, 0, 16), (W.F32, 32, 16),
-                                       (W.BF16, 0, 32), (W.FP8_E4M3, 32, 32)])
-def test_fused_append_equals_separate_calls(cache, P, B):
+@pytest.mark.parametrize("cache,P,B,short", [
+    (W.BF16, 0, 16, False), (W.BF16, 16, 16, False), (W.BF16, 256, 16, False), (W.FP8_E4M3, 0, 16, False),
+    (W.FP8_E4M3, 64, 16, False), (W.FP8_E5M2, 0, 16, False), (W.F32, 0, 16, False), (W.F32, 32, 16, False),
+    (W.BF16, 0, 32, False), (W.FP8_E4M3, 32, 32, False), (W.BF16, 0, 16, True), (W.FP8_E4M3, 0, 32, True)])
+def test_fused_append_equals_separate_calls(cache, P, B, short):
     """pa_paged_attention_decode_append writes the same pool bytes as pa_kv_cache_write and
-    returns the same output bits as the decode that follows it; both match the oracle."""
+    returns the same output bits as the decode that follows it; both match the oracle.  short:
+    contexts <= 128, so the automatic split is one chunk per (sequence, kv head)."""
     q = W.F32 if cache == W.F32 else W.BF16
-    b = W.build_batch([1, 16, 17, 40, 333, 1000, 2048], num_heads=16, num_kv_heads=4, head_dim=128, q_dtype=q,
-                      cache_dtype=cache, seed=21, block_size=B)
+    ctx = [1, 16, 17, 40, 100, 127, 128] if short else [1, 16, 17, 40, 333, 1000, 2048]
+    b = W.build_batch(ctx, num_heads=16, num_kv_heads=4, head_dim=128, q_dtype=q, cache_dtype=cache, seed=21,
+                      block_size=B)
     kp_h, vp_h = oracle_pool(b, include_new=False)
     db = DeviceBatch(b)
     kp1, vp1 = to_dev(kp_h, cache), to_dev(vp_h, cache)
