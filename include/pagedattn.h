@@ -78,7 +78,8 @@ typedef enum {
     PA_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent sizes          */
     PA_ERR_UNSUPPORTED = 2, /* valid request outside the support matrix above            */
     PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the required size       */
-    PA_ERR_HIP = 4          /* a HIP launch failed                                       */
+    PA_ERR_HIP = 4,         /* a HIP launch failed                                       */
+    PA_ERR_NO_BLOCKS = 5    /* the block manager has no free or evictable block left      */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2, PA_FP8_E5M2 = 3 } pa_dtype;
@@ -267,6 +268,91 @@ int64_t pa_pool_bytes(int64_t num_blocks, int32_t num_kv_heads, int32_t head_dim
  */
 int32_t pa_probe_tile_read(const void* buf, int64_t buf_bytes, const int32_t* order, int64_t num_reads,
                            int32_t grid_workgroups, void* sink, void* stream);
+
+/*
+ * Copy whole blocks inside the pools: for each pair i, block pairs[2i] -> block pairs[2i+1],
+ * every kv head, in both k_pool and v_pool (the copy-on-write of a shared tail block before a
+ * sequence appends into it; see the block manager below).
+ *   k_pool, v_pool  device pools (layout above) of num_blocks blocks of block_bytes each,
+ *                   block_bytes = num_kv_heads * block_size * head_dim * element bytes (a
+ *                   multiple of 16; pools 16-byte aligned).
+ *   pairs           device int32 [num_pairs][2] (source, destination).  A pair with an id
+ *                   outside [0, num_blocks) is skipped.  Destinations must be distinct and no
+ *                   destination may be a source of the same call.
+ */
+int32_t pa_copy_blocks(void* k_pool, void* v_pool, int64_t num_blocks, int64_t block_bytes, const int32_t* pairs,
+                       int32_t num_pairs, void* stream);
+
+/*
+ * Block manager (host only; no GPU work): the allocator of a pool's blocks, with reference
+ * counts, prefix caching and copy-on-write.
+ *   - Sequences reference blocks through their block tables (page 1, section 4); a block is
+ *     shared by every sequence whose table holds it and returns to the allocator when the
+ *     last one lets go (sharing across requests: page 2, the PagedAttention section).
+ *   - Prefix caching is block-granular (page 1, section 11; page 3, section 2.3): every full
+ *     block is keyed by a hash chained over the previous block and its own token ids, and a new
+ *     prompt whose leading full blocks match reuses them, so only the rest needs prefill.  A
+ *     partly filled block is never taken from the cache.  A hit is confirmed by comparing the
+ *     token ids and the chain's previous block, so a hash collision cannot share a block.
+ *   - Cached blocks nobody references stay cached until an allocation finds no never-used or
+ *     released block; then the one released longest ago is evicted.
+ *   - Appending into a partly filled block that other sequences also reference (after
+ *     pa_bm_fork) first moves the sequence to a private copy: the call returns the (source,
+ *     destination) pair, which the caller copies with pa_copy_blocks before writing the token.
+ * The manager is not thread-safe: one host thread at a time per manager.
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+typedef struct {
+    int64_t free_blocks;       /* never used or released uncached blocks */
+    int64_t evictable_blocks;  /* cached blocks no sequence references */
+    int64_t used_blocks;       /* blocks referenced by at least one sequence */
+    int64_t cached_blocks;     /* entries of the prefix cache (in use or evictable) */
+    int64_t lookups;           /* full prompt blocks looked up in the cache */
+    int64_t hits;              /* of those, found (prefix hit rate = hits / lookups) */
+    int64_t evictions;         /* cached blocks reused for other data */
+    int64_t cow_copies;        /* copy-on-write copies handed out */
+} pa_bm_stats;
+
+/* A manager for num_blocks blocks (ids 0 .. num_blocks-1) of block_size tokens; NULL for
+ * num_blocks outside [1, 2^31) or block_size < 1.  Blocks are handed out from id 0 upwards. */
+pa_block_manager* pa_bm_create(int64_t num_blocks, int32_t block_size);
+void pa_bm_destroy(pa_block_manager* bm);
+
+/* New sequence seq_id (>= 0, not already present) holding the prompt tokens[0 .. num_tokens).
+ * Leading full blocks found in the prefix cache are shared, at most (num_tokens - 1) /
+ * block_size of them so that at least one prompt token is computed; *cached_tokens (may be
+ * NULL) receives their token count.  The other blocks are allocated and the full ones
+ * registered in the cache.  The caller writes the K/V of tokens cached_tokens .. num_tokens-1
+ * (slots from pa_bm_block_table) before a later call attends over them.  PA_ERR_NO_BLOCKS
+ * leaves the manager unchanged. */
+int32_t pa_bm_add_sequence(pa_block_manager* bm, int64_t seq_id, const int32_t* tokens, int32_t num_tokens,
+                           int32_t* cached_tokens);
+
+/* Append one token to seq_id: *slot receives its pool slot (block * block_size + offset).  If
+ * the token lands in a partly filled block other sequences also reference, the sequence first
+ * moves to a fresh block: *copy_src / *copy_dst (may be NULL) receive the pair to copy with
+ * pa_copy_blocks before the token's K/V are written, else -1.  A block that becomes full is
+ * registered in the prefix cache.  PA_ERR_NO_BLOCKS leaves the manager unchanged. */
+int32_t pa_bm_append_token(pa_block_manager* bm, int64_t seq_id, int32_t token, int64_t* slot, int32_t* copy_src,
+                           int32_t* copy_dst);
+
+/* child_id (>= 0, new) shares every block of parent_id (parallel sampling, beam search). */
+int32_t pa_bm_fork(pa_block_manager* bm, int64_t parent_id, int64_t child_id);
+
+/* Drop seq_id: every block loses one reference; unreferenced cached blocks become evictable,
+ * other unreferenced blocks free. */
+int32_t pa_bm_free_sequence(pa_block_manager* bm, int64_t seq_id);
+
+/* seq_id's block table row (table may be NULL; PA_ERR_INVALID_ARG if it holds more than
+ * max_blocks blocks), its block count and token count (either may be NULL). */
+int32_t pa_bm_block_table(const pa_block_manager* bm, int64_t seq_id, int32_t* table, int32_t max_blocks,
+                          int32_t* num_blocks, int32_t* num_tokens);
+
+/* References held on block (-1 for an id outside the pool). */
+int32_t pa_bm_refcount(const pa_block_manager* bm, int32_t block);
+
+int32_t pa_bm_get_stats(const pa_block_manager* bm, pa_bm_stats* out);
 
 /* Static name of a status code. */
 const char* pa_status_string(int32_t status);

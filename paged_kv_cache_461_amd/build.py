@@ -2,9 +2,10 @@
 
     python -m paged_kv_cache_461_amd.build        # or: from paged_kv_cache_461_amd import build; build.build()
 
-Each .hip source under csrc/ is compiled to an object in csrc/_build/ (in parallel), then
-linked into paged_kv_cache_461_amd/libpagedattn.so.  Packed fp32 instructions are disabled
-for all device code.
+Each .hip source under csrc/ is compiled to an object in csrc/_build/ with hipcc, each .cpp
+source (host-only code) with g++, in parallel; the objects are linked into
+paged_kv_cache_461_amd/libpagedattn.so.  Packed fp32 instructions are disabled for all device
+code.
 """
 from __future__ import annotations
 
@@ -36,18 +37,25 @@ FILE_FLAGS = {
 }
 
 
+CXX = os.environ.get("CXX_HOST", "g++")
+HOST_CFLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(os.path.dirname(HERE), "include")]
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [CXX, *HOST_CFLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
+        raise RuntimeError("compile failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
     return obj
 
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp%d" % os.getpid()

@@ -10,6 +10,7 @@
 
 #include "../../include/pagedattn.h"
 #include "pa_internal.hpp"
+#include "pa_copy.hpp"
 
 namespace {
 
@@ -203,6 +204,7 @@ const char* pa_status_string(int32_t status)
     case PA_ERR_UNSUPPORTED: return "unsupported configuration";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_HIP: return "HIP launch failed";
+    case PA_ERR_NO_BLOCKS: return "no free or evictable block";
     default: return "unknown status";
     }
 }
@@ -492,6 +494,22 @@ int32_t pa_paged_attention_chunked_prefill(void* out, const void* query, int32_t
     hipError_t e = pa::launch_prefill(cache_dtype, head_dim, num_heads / num_kv_heads, a, pl.grid,
                                       static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(PA_ERR_HIP, "chunked prefill launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int32_t pa_copy_blocks(void* k_pool, void* v_pool, int64_t num_blocks, int64_t block_bytes, const int32_t* pairs,
+                       int32_t num_pairs, void* stream)
+{
+    if (num_pairs < 0 || num_blocks < 0 || block_bytes <= 0 || block_bytes % 16)
+        return fail(PA_ERR_INVALID_ARG, "num_pairs %d, num_blocks %lld, block_bytes %lld (a positive multiple of 16)",
+                    num_pairs, (long long)num_blocks, (long long)block_bytes);
+    if (num_pairs == 0) return ok();
+    if (!k_pool || !v_pool || !pairs || !aligned16(k_pool) || !aligned16(v_pool))
+        return fail(PA_ERR_INVALID_ARG, "null or misaligned pointer (k_pool %p v_pool %p pairs %p)", k_pool, v_pool,
+                    (const void*)pairs);
+    hipError_t e = pa::launch_copy_blocks(k_pool, v_pool, num_blocks, block_bytes, pairs, num_pairs,
+                                          static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "copy_blocks launch: %s", hipGetErrorString(e));
     return ok();
 }
 

@@ -22,7 +22,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedatt
 _lib = None
 _lock = threading.Lock()
 
-PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_NO_BLOCKS = range(6)
+
+
+class BmStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("free_blocks", "evictable_blocks", "used_blocks", "cached_blocks",
+                                              "lookups", "hits", "evictions", "cow_copies")]
 
 # Every symbol include/pagedattn.h declares.
 EXPORTS = (
@@ -30,6 +35,8 @@ EXPORTS = (
     "pa_paged_attention_decode", "pa_paged_attention_decode_phase", "pa_kv_bytes_per_token",
     "pa_pool_bytes", "pa_probe_tile_read", "pa_status_string", "pa_last_error",
     "pa_chunked_prefill_workspace_size", "pa_paged_attention_chunked_prefill", "pa_paged_attention_decode_append",
+    "pa_copy_blocks", "pa_bm_create", "pa_bm_destroy", "pa_bm_add_sequence", "pa_bm_append_token", "pa_bm_fork",
+    "pa_bm_free_sequence", "pa_bm_block_table", "pa_bm_refcount", "pa_bm_get_stats",
 )
 
 
@@ -72,6 +79,26 @@ def library():
         lib.pa_pool_bytes.argtypes = [I64, I32, I32, I32, I32]
         lib.pa_probe_tile_read.restype = I32
         lib.pa_probe_tile_read.argtypes = [P, I64, P, I64, I32, P, P]
+        lib.pa_copy_blocks.restype = I32
+        lib.pa_copy_blocks.argtypes = [P, P, I64, I64, P, I32, P]
+        lib.pa_bm_create.restype = P
+        lib.pa_bm_create.argtypes = [I64, I32]
+        lib.pa_bm_destroy.restype = None
+        lib.pa_bm_destroy.argtypes = [P]
+        lib.pa_bm_add_sequence.restype = I32
+        lib.pa_bm_add_sequence.argtypes = [P, I64, P, I32, P]
+        lib.pa_bm_append_token.restype = I32
+        lib.pa_bm_append_token.argtypes = [P, I64, I32, P, P, P]
+        lib.pa_bm_fork.restype = I32
+        lib.pa_bm_fork.argtypes = [P, I64, I64]
+        lib.pa_bm_free_sequence.restype = I32
+        lib.pa_bm_free_sequence.argtypes = [P, I64]
+        lib.pa_bm_block_table.restype = I32
+        lib.pa_bm_block_table.argtypes = [P, I64, P, I32, P, P]
+        lib.pa_bm_refcount.restype = I32
+        lib.pa_bm_refcount.argtypes = [P, I32]
+        lib.pa_bm_get_stats.restype = I32
+        lib.pa_bm_get_stats.argtypes = [P, ctypes.POINTER(BmStats)]
         lib.pa_status_string.restype = ctypes.c_char_p
         lib.pa_status_string.argtypes = [I32]
         lib.pa_last_error.restype = ctypes.c_char_p
@@ -279,3 +306,76 @@ def probe_tile_read(buf, order, sink, grid_workgroups=2048, stream=None):
     _dev("sink", sink)
     _check(library().pa_probe_tile_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(order), order.numel(),
                                         int(grid_workgroups), _ptr(sink), _stream(stream)))
+
+
+def copy_blocks(k_pool, v_pool, pairs, *, num_kv_heads, head_dim, block_size=16, stream=None):
+    """Copy pool blocks pairs[i][0] -> pairs[i][1] in both pools (pa_copy_blocks); pairs is a
+    device int32 tensor [n][2]."""
+    _dev("k_pool", k_pool)
+    _dev("v_pool", v_pool)
+    _dev("pairs", pairs, torch.int32)
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [n][2]")
+    nb = num_pool_blocks(k_pool, num_kv_heads, head_dim, block_size)
+    block_bytes = num_kv_heads * block_size * head_dim * k_pool.element_size()
+    _check(library().pa_copy_blocks(_ptr(k_pool), _ptr(v_pool), nb, block_bytes, _ptr(pairs), pairs.shape[0],
+                                    _stream(stream)))
+
+
+class BlockManager:
+    """The library's host-side block manager (pa_bm_*): refcounted blocks, block-granular
+    prefix caching, copy-on-write on append to a shared partial block."""
+
+    def __init__(self, num_blocks: int, block_size: int = 16):
+        self._lib = library()
+        self._h = self._lib.pa_bm_create(int(num_blocks), int(block_size))
+        if not self._h:
+            raise ValueError("bad block manager arguments (num_blocks %d, block_size %d)" % (num_blocks, block_size))
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+
+    def close(self):
+        if self._h:
+            self._lib.pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add_sequence(self, seq_id: int, tokens) -> int:
+        """Returns the number of leading prompt tokens served from the prefix cache."""
+        t = (ctypes.c_int32 * len(tokens))(*[int(x) for x in tokens])
+        cached = ctypes.c_int32(0)
+        _check(self._lib.pa_bm_add_sequence(self._h, int(seq_id), t, len(tokens), ctypes.byref(cached)))
+        return cached.value
+
+    def append_token(self, seq_id: int, token: int):
+        """Returns (slot, copy) where copy is None or the (source, destination) block pair."""
+        slot, src, dst = ctypes.c_int64(0), ctypes.c_int32(-1), ctypes.c_int32(-1)
+        _check(self._lib.pa_bm_append_token(self._h, int(seq_id), int(token), ctypes.byref(slot), ctypes.byref(src),
+                                            ctypes.byref(dst)))
+        return slot.value, (None if src.value < 0 else (src.value, dst.value))
+
+    def fork(self, parent: int, child: int):
+        _check(self._lib.pa_bm_fork(self._h, int(parent), int(child)))
+
+    def free_sequence(self, seq_id: int):
+        _check(self._lib.pa_bm_free_sequence(self._h, int(seq_id)))
+
+    def block_table(self, seq_id: int):
+        """(list of physical block ids, number of tokens)."""
+        nb, nt = ctypes.c_int32(0), ctypes.c_int32(0)
+        _check(self._lib.pa_bm_block_table(self._h, int(seq_id), None, 0, ctypes.byref(nb), ctypes.byref(nt)))
+        row = (ctypes.c_int32 * max(nb.value, 1))()
+        _check(self._lib.pa_bm_block_table(self._h, int(seq_id), row, nb.value, None, None))
+        return list(row)[:nb.value], nt.value
+
+    def refcount(self, block: int) -> int:
+        return self._lib.pa_bm_refcount(self._h, int(block))
+
+    def stats(self) -> dict:
+        st = BmStats()
+        _check(self._lib.pa_bm_get_stats(self._h, ctypes.byref(st)))
+        return {n: getattr(st, n) for n, _ in BmStats._fields_}

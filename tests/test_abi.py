@@ -270,3 +270,13 @@ def test_fused_append_rejects_before_launch(lib, kw, status):
 
 def test_fused_append_empty_batch_is_ok(lib):
     assert _fused(lib, S=0, out=None, query=None, nk=None, nv=None) == ops.PA_OK
+
+
+def test_copy_blocks_rejects_before_launch(lib):
+    P = ctypes.c_void_p
+    assert lib.pa_copy_blocks(FAKE, FAKE, 10, 4096, FAKE, 0, None) == ops.PA_OK  # nothing to copy
+    assert lib.pa_copy_blocks(FAKE, FAKE, 10, 4100, FAKE, 1, None) == ops.PA_ERR_INVALID_ARG  # not 16-byte pieces
+    assert lib.pa_copy_blocks(FAKE, FAKE, 10, 4096, FAKE, -1, None) == ops.PA_ERR_INVALID_ARG
+    assert lib.pa_copy_blocks(None, FAKE, 10, 4096, FAKE, 1, None) == ops.PA_ERR_INVALID_ARG
+    assert lib.pa_copy_blocks(FAKE + 8, FAKE, 10, 4096, FAKE, 1, None) == ops.PA_ERR_INVALID_ARG
+    assert P is not None
