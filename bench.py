@@ -54,7 +54,7 @@ def parse_args():
                             "fp8_e5m2_chunked_prefill", "tiny_fp32"])
     p.add_argument("--layers", type=int, default=2, help="layer pools cycled through (>= 2)")
     p.add_argument("--partition-size", type=int, default=0, help="split-K partition (0 = library's choice)")
-    p.add_argument("--block-size", type=int, default=16, choices=[16, 32],
+    p.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32],
                    help="tokens per KV block of the pools (both workloads)")
     p.add_argument("--extra-workload", default="fp8_chunked_prefill",
                    choices=["none", "fp8_chunked_prefill", "fp8_e5m2_chunked_prefill", "llama3_8b_decode",

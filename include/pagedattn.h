@@ -55,7 +55,8 @@
  * reads a whole 1 KiB K slice (16 tokens x 32 channels) or a 1 KiB V piece (8 tokens x 64
  * channels).
  *
- * Supported shapes: head_dim 64 or 128; block_size 16 or 32 for attention (the pages weigh
+ * Supported shapes: head_dim 64 or 128; block_size 16 or 32 for attention, also 8 with an
+ * F32 or BF16 cache (the pages weigh
  * block size against fragmentation and access efficiency: page 2, the PagedAttention section;
  * the append takes any block size the layout allows); num_heads / num_kv_heads in
  * {1, 2, 4, 8}; (q dtype, cache dtype) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3),
@@ -110,8 +111,8 @@ int32_t pa_kv_cache_write(const void* key, const void* value, int32_t src_dtype,
  * Bytes of device workspace that pa_paged_attention_decode needs for these arguments
  * (partition_size 0 = automatic work split).  Depends only on the shapes, never on the
  * context lengths' values.  0 for an empty batch, and for an automatic split when
- * max_context_len <= 128: every sequence then fits in one work chunk, nothing is split and no
- * merge runs.  Returns -1 for arguments the decode call would reject.
+ * max_context_len <= 128 (64 with 8-token blocks): every sequence then fits in one work chunk,
+ * nothing is split and no merge runs.  Returns -1 for arguments the decode call would reject.
  */
 int64_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size, int32_t max_context_len,
@@ -131,10 +132,11 @@ int64_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t nu
  *   k_scale, v_scale device fp32 [num_kv_heads] for an fp8 cache (the stored code times
  *                  the scale is the cached value), else NULL.
  *   partition_size 0 = automatic, else a multiple of block_size.  The work is the list of
- *                  every (sequence, kv head) pair's 16-token units laid end to end; it is cut
- *                  into chunks of partition_size / 16 units (automatic: equal chunks, one per
- *                  wave of a grid sized to fill the GPU; or, when max_context_len <= 128, one
- *                  chunk per (sequence, kv head)), each chunk is attended independently per
+ *                  every (sequence, kv head) pair's units (16 tokens, or one 8-token block)
+ *                  laid end to end; it is cut into chunks of partition_size tokens' units
+ *                  (automatic: equal chunks, one per wave of a grid sized to fill the GPU; or,
+ *                  when every sequence fits in 8 units, one chunk per (sequence, kv head)),
+ *                  each chunk is attended independently per
  *                  sequence piece, and the pieces of a sequence are merged (split-K).  The
  *                  result does not depend on the split beyond rounding.
  *   workspace      device scratch of at least pa_decode_workspace_size(...) bytes, 256-byte
@@ -200,7 +202,8 @@ int64_t pa_chunked_prefill_workspace_size(int32_t num_query_rows, int32_t num_se
  *                  outside [0, num_query_rows) is skipped.
  *   max_query_len  host bound on q_len (sizes the launch).
  *   k_pool .. v_scale, scale  as for pa_paged_attention_decode.
- *   partition_size 0 = automatic, else a multiple of block_size: the visible keys of each group
+ *   partition_size 0 = automatic, else a multiple of block_size (rounded up to a multiple of
+ *                  16 for 8-token blocks): the visible keys of each group
  *                  of rows are cut into ranges of partition_size keys that run on separate
  *                  workgroups and are merged (split-K).  Automatic splits only when the rows
  *                  alone do not fill the GPU.

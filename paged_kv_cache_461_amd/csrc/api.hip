@@ -60,10 +60,13 @@ struct DecodePlan {
     int64_t total;
 };
 
-// Work units (16 tokens of one kv head) of the largest batch these arguments allow.
-int64_t max_units(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len)
+// Tokens per work unit of the attention kernels: 16, or one 8-token block.
+int32_t unit_tokens(int32_t block_size) { return block_size < pa::kUnitTokens ? block_size : pa::kUnitTokens; }
+
+// Work units (unit_tokens tokens of one kv head) of the largest batch these arguments allow.
+int64_t max_units(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len, int32_t utok)
 {
-    return (int64_t)num_seqs * num_kv_heads * ((max_context_len + pa::kUnitTokens - 1) / pa::kUnitTokens);
+    return (int64_t)num_seqs * num_kv_heads * ((max_context_len + utok - 1) / utok);
 }
 
 // stream_waves: waves of the full persistent grid for the kernel variant.
@@ -71,14 +74,14 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
                        int32_t block_size, int32_t max_context_len, int32_t partition_size, int64_t stream_waves)
 {
     DecodePlan pl{};
-    (void)block_size;  // the plan counts 16-token units whatever the block size
-    const int64_t umax = max_units(num_seqs, num_kv_heads, max_context_len);
+    const int32_t utok = unit_tokens(block_size);
+    const int64_t umax = max_units(num_seqs, num_kv_heads, max_context_len, utok);
     int64_t waves;
     if (partition_size > 0) {
-        pl.chunk_blocks = partition_size / pa::kUnitTokens;
+        pl.chunk_blocks = partition_size / utok;
         pl.max_chunks = (umax + pl.chunk_blocks - 1) / pl.chunk_blocks;
         waves = pl.max_chunks < stream_waves ? pl.max_chunks : stream_waves;
-    } else if ((max_context_len + pa::kUnitTokens - 1) / pa::kUnitTokens <= pa::kMinChunkBlocks) {
+    } else if ((max_context_len + utok - 1) / utok <= pa::kMinChunkBlocks) {
         // every run fits in one minimum chunk: one chunk per run, no split, no merge, no workspace
         pl.chunk_blocks = -1;
         const int64_t runs = (int64_t)num_seqs * num_kv_heads;
@@ -122,8 +125,11 @@ int32_t check_decode_shape(int32_t num_seqs, int32_t num_heads, int32_t num_kv_h
     if (g != 1 && g != 2 && g != 4 && g != 8)
         return fail(PA_ERR_UNSUPPORTED, "GQA group %d (supported: 1, 2, 4, 8)", g);
     if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
-    if (block_size != 16 && block_size != 32)
-        return fail(PA_ERR_UNSUPPORTED, "block_size %d (supported: 16, 32)", block_size);
+    if (block_size != 8 && block_size != 16 && block_size != 32)
+        return fail(PA_ERR_UNSUPPORTED, "block_size %d (supported: 8, 16, 32)", block_size);
+    if (block_size == 8 && is_fp8(cache_dtype))
+        return fail(PA_ERR_UNSUPPORTED, "8-token blocks need a 16- or 32-bit cache (an fp8 V group of 8 tokens "
+                    "does not fill the kernels' 16-byte V pieces)");
     const bool combo = (q_dtype == PA_F32 && cache_dtype == PA_F32) || (q_dtype == PA_BF16 && cache_dtype == PA_BF16) ||
                        (q_dtype == PA_BF16 && is_fp8(cache_dtype));
     if (!combo) return fail(PA_ERR_UNSUPPORTED, "(q dtype %d, cache dtype %d) not supported", q_dtype, cache_dtype);
@@ -153,8 +159,9 @@ PrefillPlan plan_prefill(int32_t num_query_rows, int32_t num_seqs, int32_t max_q
     pl.row_blocks = (int32_t)(((int64_t)max_query_len * gqa + rows_per_wg - 1) / rows_per_wg);
     const int64_t base = (int64_t)num_seqs * num_kv_heads * pl.row_blocks;
     if (partition_size > 0) {
-        pl.split_keys = partition_size;
-        pl.num_splits = max_context_len > 0 ? (max_context_len + partition_size - 1) / partition_size : 1;
+        // key ranges start on 16-token units (an 8-token-block partition is rounded up)
+        pl.split_keys = (partition_size + pa::kUnitTokens - 1) / pa::kUnitTokens * pa::kUnitTokens;
+        pl.num_splits = max_context_len > 0 ? (max_context_len + pl.split_keys - 1) / pl.split_keys : 1;
     } else {
         pl.split_keys = 0;
         int64_t ns = base > 0 ? (kPrefillTargetWorkgroups + base - 1) / base : 1;

@@ -310,7 +310,10 @@ __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int c)
 
 __device__ __forceinline__ int seq_ctx(const DecodeArgs& a, int s) { return clamp_ctx(a, a.context_lens[s]); }
 
-__device__ __forceinline__ int nblocks(int ctx) { return (ctx + kUnitTokens - 1) / kUnitTokens; }
+// Tokens per work unit, as a shift: 16, or 8 for 8-token blocks (one block per unit, the unit's
+// upper half empty).
+__device__ __forceinline__ int unit_shift(int block_size) { return block_size < kUnitTokens ? 3 : 4; }
+__device__ __forceinline__ int nunits(int ctx, int ush) { return (ctx + (1 << ush) - 1) >> ush; }
 
 __device__ __forceinline__ int wave_incl_scan(int x, int lane)
 {
@@ -342,6 +345,7 @@ template <class ChunkStart>
 __device__ __forceinline__ Plan plan_wave(const DecodeArgs& a, const int* lctx, int lane, ChunkStart chunk_start)
 {
     const int Hkv = a.num_kv_heads, S = a.num_seqs;
+    const int ush = unit_shift(a.block_size);
     // total
     int64_t total = 0;
     for (int base = 0; base < S; base += kScanWindow) {
@@ -349,7 +353,7 @@ __device__ __forceinline__ Plan plan_wave(const DecodeArgs& a, const int* lctx, 
 #pragma unroll
         for (int i = 0; i < kScanPerLane; i++) {
             const int s = base + lane * kScanPerLane + i;
-            part += s < S ? nblocks(lctx[s]) : 0;
+            part += s < S ? nunits(lctx[s], ush) : 0;
         }
         total += __builtin_amdgcn_readlane(wave_incl_scan(part, lane), 63);
     }
@@ -368,7 +372,7 @@ __device__ __forceinline__ Plan plan_wave(const DecodeArgs& a, const int* lctx, 
 #pragma unroll
         for (int i = 0; i < kScanPerLane; i++) {
             const int s = base + lane * kScanPerLane + i;
-            nb[i] = s < S ? nblocks(lctx[s]) : 0;
+            nb[i] = s < S ? nunits(lctx[s], ush) : 0;
             part += nb[i];
         }
         const int incl = wave_incl_scan(part, lane);
@@ -400,17 +404,19 @@ __device__ __forceinline__ Plan plan_wave(const DecodeArgs& a, const int* lctx, 
 // the run's context length.  Sequences with no context are skipped.
 struct Cursor {
     int s, g, j, ctx, nbs;
+    int ush;  // unit_shift of the block size
     int64_t run_start;
 };
 
-__device__ __forceinline__ Cursor cursor_at(const Pos& p, const int* lctx)
+__device__ __forceinline__ Cursor cursor_at(const Pos& p, const int* lctx, int ush)
 {
     Cursor c;
+    c.ush = ush;
     c.s = p.s;
     c.g = p.g;
     c.j = p.j;
     c.ctx = lctx[p.s];
-    c.nbs = nblocks(c.ctx);
+    c.nbs = nunits(c.ctx, c.ush);
     c.run_start = p.run_start;
     return c;
 }
@@ -426,7 +432,7 @@ __device__ __forceinline__ void cursor_next(Cursor& c, const int* lctx, int num_
         ++c.s;
         c.ctx = c.s < num_seqs ? lctx[c.s] : 0;
     } while (c.ctx == 0 && c.s < num_seqs);
-    c.nbs = nblocks(c.ctx);
+    c.nbs = nunits(c.ctx, c.ush);
 }
 
 // Move the cursor to block 0 of the next run (next kv head, or the next non-empty sequence).
@@ -440,7 +446,7 @@ __device__ __forceinline__ void next_run(Cursor& c, const int* lctx, int num_seq
         ++c.s;
         c.ctx = c.s < num_seqs ? lctx[c.s] : 0;
     } while (c.ctx == 0 && c.s < num_seqs);
-    c.nbs = nblocks(c.ctx);
+    c.nbs = nunits(c.ctx, c.ush);
 }
 
 // Fused append: the chunk that holds a run's last block is the only one that reads it, so its
@@ -457,7 +463,7 @@ __device__ __forceinline__ void append_chunk_tokens(const DecodeArgs& a, const i
     constexpr int P = D / N;    // pieces per source row
     static_assert(2 * P <= 64, "the K and V rows of a token fit one wave");
     const int Hkv = a.num_kv_heads, NS = a.num_seqs, B = a.block_size;
-    Cursor c = cursor_at(p0, lctx);
+    Cursor c = cursor_at(p0, lctx, unit_shift(B));
     bool stored = false;
     while (c.s < NS && c.run_start + c.nbs <= u_end) {  // this run ends inside the chunk
         const int t = c.ctx - 1;
@@ -501,7 +507,7 @@ struct ChunkMap {
 //   3 waves per SIMD (at most 168 VGPRs, no spills) where that measured faster: fp8 with G <= 4
 //     (70.3 -> 66.4 us at D 128) and D 64 with G <= 4 (bf16: 60.0 -> 55.5 us);
 //   2 forced for bf16 D 128 G 8, which otherwise takes 296 registers and runs one wave per
-//     SIMD (157 -> 139 us despite a few spills);
+//     SIMD (157 -> 139 us despite a few spills), and for fp8 G 8 (it fits 256 registers);
 //   otherwise the compiler's choice: 2 waves per SIMD for most variants (bf16 G 1 / 2 measured
 //     slower at 3), one for fp32 D 128, which measured slower when forced to 2 with spills.
 // The persistent grid has max(2, this) waves per SIMD.
@@ -510,7 +516,7 @@ constexpr int stream_min_waves()
 {
     if constexpr (KT == kF32) return 1;
     else if constexpr (KT == kBF16) return D == 64 && G <= 4 ? 3 : D == 128 && G == 8 ? 2 : 1;
-    else return G <= 4 ? 3 : 1;
+    else return G <= 4 ? 3 : 2;
 }
 
 template <int KT, int D, int G>
@@ -519,7 +525,9 @@ constexpr int stream_waves_per_simd()
     return stream_min_waves<KT, D, G>() > 2 ? stream_min_waves<KT, D, G>() : 2;
 }
 
-template <int QT, int KT, int D, int G>
+// PER_RUN: the one-chunk-per-run form (chunk_blocks < 0), a separate instance so that its
+// extra paths leave the balanced form's registers alone.
+template <int QT, int KT, int D, int G, bool PER_RUN>
 __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) void decode_stream_kernel(
     const DecodeArgs a)
 {
@@ -552,7 +560,7 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) voi
     // chunk_blocks < 0: one chunk per run.  The host picks it when every run fits in one
     // minimum chunk, so no run is split, nothing is merged and the merge launch is skipped
     // (small batches, where a launch costs more than the work).  Chunk k is then run k.
-    const bool per_run = a.chunk_blocks < 0;
+    constexpr bool per_run = PER_RUN;
     ChunkMap cm{};
     const Plan pl = per_run ? Plan{0, Pos{NS, 0, 0, 0}} : plan_wave(a, lctx, lane, [&](int64_t U) {
         cm.C = a.chunk_blocks > 0 ? (int64_t)a.chunk_blocks : max((U + NW - 1) / NW, (int64_t)kMinChunkBlocks);
@@ -567,33 +575,45 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) voi
     // A block of B = 16 << ub tokens is 1 << ub units.  Unit `sub` of a block: its K slices are
     // 1 KiB pieces at sub * 1 KiB + c * (B * 64) of the block's tile, its V loads the
     // sub-th run of TILE bytes (the pool layout of include/pagedattn.h).
+    // An 8-token block is one unit whose upper 8 tokens are empty: lanes 32..63 of its K loads
+    // and its V loads past the block's bytes fall outside the window and read nothing.
     const int ub = a.block_size > kUnitTokens ? 1 : 0;
-    const int btile = S::TILE << ub;  // bytes of one (block, kv head) tile
+    const int ush = unit_shift(a.block_size);
+    const int btile = a.block_size * D * S::EB;  // bytes of one (block, kv head) tile
+    const int vwin = btile < S::TILE ? btile : S::TILE;
+    const int kvoff = a.block_size < kUnitTokens && lane >= 32 ? 0x40000000 : lane * 16;
     const int kstride = a.block_size * 64;
     const int64_t block_stride = (int64_t)Hkv * btile;
     const int32_t* tables = a.block_tables;
     const int mbps = a.max_blocks_per_seq;
 
+    if constexpr (per_run) {  // the zero rows of empty sequences, before (and apart from) the stream
+        for (int64_t k = first; k < nchunks; k += NW) {
+            const int s = (int)(k / Hkv), g = (int)(k % Hkv);
+            if (lctx[s] != 0) continue;
+#pragma unroll
+            for (int h = 0; h < G; h++) {
+                const int64_t row = (int64_t)s * a.num_heads + (int64_t)g * G + h;
+#pragma unroll
+                for (int cg = 0; cg < S::CG; cg++) {
+                    if constexpr (QT == kBF16)
+                        static_cast<uint16_t*>(a.out)[row * D + cg * 64 + lane] = 0;
+                    else
+                        static_cast<float*>(a.out)[row * D + cg * 64 + lane] = 0.0f;
+                }
+            }
+        }
+    }
+
     for (int64_t k = first; k < nchunks; k += NW) {
         int n;           // units of this chunk
         Pos p0;          // its first unit
         int64_t u_end;   // list index one past its last unit
-        if (per_run) {
+        if constexpr (per_run) {
             p0 = Pos{(int)(k / Hkv), (int)(k % Hkv), 0, 0};
-            n = nblocks(lctx[p0.s]);
+            n = __builtin_amdgcn_readfirstlane(nunits(lctx[p0.s], ush));  // uniform: keeps loop control scalar
             u_end = n;
-            if (n == 0) {  // empty sequence: zero rows
-#pragma unroll
-                for (int h = 0; h < G; h++) {
-                    const int64_t row = (int64_t)p0.s * a.num_heads + (int64_t)p0.g * G + h;
-#pragma unroll
-                    for (int cg = 0; cg < S::CG; cg++) {
-                        if constexpr (QT == kBF16)
-                            static_cast<uint16_t*>(a.out)[row * D + cg * 64 + lane] = 0;
-                        else
-                            static_cast<float*>(a.out)[row * D + cg * 64 + lane] = 0.0f;
-                    }
-                }
+            if (n == 0) {  // empty sequence: its zero rows were written above
                 continue;
             }
         } else {
@@ -605,11 +625,11 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) voi
 
         // table cursor: the block whose table entry is fetched next (it stops at the chunk's
         // last block, whose entry then feeds the fill-in loads past the end)
-        Cursor tc = cursor_at(p0, lctx);
+        Cursor tc = cursor_at(p0, lctx, ush);
         int tcount = 0;
         auto fetch_entry = [&](int& e, int& nv, int& g, int& sub) {
             e = tables[(int64_t)tc.s * mbps + (tc.j >> ub)];
-            nv = min(kUnitTokens, tc.ctx - tc.j * kUnitTokens);
+            nv = min(1 << ush, tc.ctx - (tc.j << ush));
             g = tc.g;
             sub = tc.j & ub;
             if (tcount + 1 < n) {
@@ -618,7 +638,7 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) voi
             }
         };
         // compute cursor: the block attended next, with its piece's bookkeeping
-        Cursor cc = cursor_at(p0, lctx);
+        Cursor cc = cursor_at(p0, lctx, ush);
         int piece_j0 = cc.j;
 
         // entry ring: physical id, valid tokens, kv head and unit of the block, for units
@@ -729,9 +749,9 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) voi
                     const int sub = ent_sub[i];
                     const int64_t off = (int64_t)phys * block_stride + (int64_t)ent_g[i] * btile;
                     const TileWindow kw(kpool + off + sub * 1024, none ? 0 : btile - sub * 1024);
-                    const TileWindow vw(vpool + off + sub * S::TILE, none ? 0 : S::TILE);
+                    const TileWindow vw(vpool + off + sub * S::TILE, none ? 0 : vwin);
 #pragma unroll
-                    for (int c = 0; c < S::NCH; c++) kb[i][c] = kw.load_stream(lane * 16, c * kstride);
+                    for (int c = 0; c < S::NCH; c++) kb[i][c] = kw.load_stream(kvoff, c * kstride);
 #pragma unroll
                     for (int c = 0; c < S::NCH; c++) vb[i][c] = vw.load_stream(lane * 16 + c * 1024);
                 }
@@ -809,8 +829,12 @@ template <int QT, int KT, int D, int G>
 hipError_t launch_phase_t(int phase, const DecodeArgs& a, hipStream_t stream)
 {
     if ((phase & 1) && a.grid_workgroups > 0) {
-        hipLaunchKernelGGL((decode_stream_kernel<QT, KT, D, G>), dim3((unsigned)a.grid_workgroups),
-                           dim3(kDecodeThreads), (size_t)a.num_seqs * sizeof(int), stream, a);
+        if (a.chunk_blocks < 0)
+            hipLaunchKernelGGL((decode_stream_kernel<QT, KT, D, G, true>), dim3((unsigned)a.grid_workgroups),
+                               dim3(kDecodeThreads), (size_t)a.num_seqs * sizeof(int), stream, a);
+        else
+            hipLaunchKernelGGL((decode_stream_kernel<QT, KT, D, G, false>), dim3((unsigned)a.grid_workgroups),
+                               dim3(kDecodeThreads), (size_t)a.num_seqs * sizeof(int), stream, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

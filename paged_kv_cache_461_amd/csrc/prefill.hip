@@ -110,7 +110,9 @@ __device__ __forceinline__ void ring_schedule()
 // rows 16u .. 16u+15, and its row 4q + j is key 16q + 4u + j (block q, token 4u + j).
 __device__ __forceinline__ int k_lds_row(int b, int o) { return 16 * (o >> 2) + 4 * b + (o & 3); }
 
-template <int KT, int D, int G, int R>
+// B8: the 8-token-block form (bf16 cache only), a separate instance so that its second table
+// entry per unit costs the other block sizes nothing.
+template <int KT, int D, int G, int R, bool B8>
 __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs a)
 {
     using L = PfLds<D>;
@@ -224,15 +226,26 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
     // A block of 16 << ub tokens holds 1 << ub units; unit u of the range is unit u & ub of
     // table entry u >> ub.  Inside a 32-token block's tile, unit `sub` has its K slices at
     // sub * 1 KiB + slice * (B * 64) and its V at sub * TILE_BYTES (include/pagedattn.h).
+    // 8-token blocks (bf16 cache only): unit u is blocks 2u (tokens 0..7) and 2u+1 (8..15).
     const int ub = a.block_size > kUnitTokens ? 1 : 0;
+    constexpr bool b8 = B8;
+    static_assert(!B8 || KT == kBF16, "8-token blocks with a bf16 cache only");
     const int kstride = a.block_size * 64;
+    const int64_t btile = (int64_t)a.block_size * D * EB;  // bytes of one (block, kv head) tile
     const int last_unit = kstop > 0 ? (kstop - 1) >> 4 : 0;
-    int ent[NCH];
+    const int last_b8 = kstop > 0 ? (kstop - 1) >> 3 : 0;
+    int ent[NCH], ent8[B8 ? NCH : 1];  // ent8: the unit's second 8-token block
     auto fetch_entries = [&](int kbase) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < NCH; j++) {
             const int b = __builtin_amdgcn_readfirstlane((tid + kPrefillThreads * j) / CH_PER_TILE);
-            ent[j] = table[min((kbase >> 4) + b, last_unit) >> ub];
+            const int u = (kbase >> 4) + b;
+            if constexpr (b8) {
+                ent[j] = table[min(2 * u, last_b8)];
+                ent8[j] = table[min(2 * u + 1, last_b8)];
+            } else {
+                ent[j] = table[min(u, last_unit) >> ub];
+            }
         }
     };
     auto load = [&](auto set_tag, int kbase) __attribute__((always_inline)) {
@@ -246,10 +259,23 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
             const int phys = __builtin_amdgcn_readfirstlane(ent[j]);
             const bool ok = kbase + 16 * b < kstop && phys >= 0 && (int64_t)phys < a.num_blocks;
             // a block with no valid entry still reads block 0 (the pool has one); store() zeroes it
-            const int sub = ((kbase >> 4) + b) & ub;
-            const int64_t tile = ((int64_t)(ok ? phys : 0) * a.num_kv_heads + g) * (TILE_BYTES << ub);
-            kr[SET][j] = load16(kpool + tile + sub * 1024 + (off >> 10) * kstride + (off & 1023));
-            vr[SET][j] = load16(vpool + tile + sub * TILE_BYTES + off);
+            if constexpr (b8) {
+                const int phys2 = __builtin_amdgcn_readfirstlane(ent8[j]);
+                const bool ok2 = kbase + 16 * b + 8 < kstop && phys2 >= 0 && (int64_t)phys2 < a.num_blocks;
+                const int64_t t1 = ((int64_t)(ok ? phys : 0) * a.num_kv_heads + g) * btile;
+                const int64_t t2 = ((int64_t)(ok2 ? phys2 : 0) * a.num_kv_heads + g) * btile;
+                // K: the piece's token (off >> 6 within its 1 KiB slice) picks the block
+                const int tok = (off & 1023) >> 6;
+                kr[SET][j] = load16(kpool + (tok < 8 ? t1 : t2) + (off >> 10) * kstride + (tok & 7) * 64 + (off & 63));
+                // V: 8-token group og of the unit is block og; the piece is channel (off >> 4) % D
+                const int og = (off >> 4) / D;
+                vr[SET][j] = load16(vpool + (og ? t2 : t1) + (off - og * D * 16));
+            } else {
+                const int sub = ((kbase >> 4) + b) & ub;
+                const int64_t tile = ((int64_t)(ok ? phys : 0) * a.num_kv_heads + g) * btile;
+                kr[SET][j] = load16(kpool + tile + sub * 1024 + (off >> 10) * kstride + (off & 1023));
+                vr[SET][j] = load16(vpool + tile + sub * TILE_BYTES + off);
+            }
             okbits[SET] |= ok ? 1u << j : 0u;
         }
         fetch_entries(kbase + kPfKeys);  // for the next load, one compute phase away
@@ -509,8 +535,16 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a)
 template <int KT, int D, int G>
 hipError_t launch_one(const PrefillArgs& a, int grid, hipStream_t stream)
 {
-    hipLaunchKernelGGL((prefill_kernel<KT, D, G, kPrefillRowTiles>), dim3((unsigned)grid), dim3(kPrefillThreads), 0,
-                       stream, a);
+    if (a.block_size < kUnitTokens) {
+        if constexpr (KT == kBF16)
+            hipLaunchKernelGGL((prefill_kernel<KT, D, G, kPrefillRowTiles, true>), dim3((unsigned)grid),
+                               dim3(kPrefillThreads), 0, stream, a);
+        else
+            return hipErrorInvalidValue;  // rejected by the host checks before this point
+    } else {
+        hipLaunchKernelGGL((prefill_kernel<KT, D, G, kPrefillRowTiles, false>), dim3((unsigned)grid),
+                           dim3(kPrefillThreads), 0, stream, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.num_splits == 1) return e;
     const int64_t n = (int64_t)a.num_query_rows * a.num_heads;

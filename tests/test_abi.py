@@ -74,7 +74,8 @@ def _decode(lib, **kw):
     (dict(Hq=30), ops.PA_ERR_INVALID_ARG),                  # 30 % 8 != 0
     (dict(Hq=24, Hkv=2), ops.PA_ERR_UNSUPPORTED),            # GQA 12
     (dict(D=96), ops.PA_ERR_UNSUPPORTED),
-    (dict(B=8), ops.PA_ERR_UNSUPPORTED),
+    (dict(B=8, cache_dtype=FP8), ops.PA_ERR_UNSUPPORTED),  # fp8 V groups of 8 tokens
+    (dict(B=4), ops.PA_ERR_UNSUPPORTED),
     (dict(B=64), ops.PA_ERR_UNSUPPORTED),
     (dict(B=32, P=48), ops.PA_ERR_INVALID_ARG),              # partition not a multiple of the block
     (dict(q_dtype=F32), ops.PA_ERR_UNSUPPORTED),             # f32 q over a bf16 cache
