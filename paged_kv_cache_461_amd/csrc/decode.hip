@@ -780,48 +780,106 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) voi
     }
 }
 
-// Merge the pieces of one (sequence, query head): weights l_p * 2^(m_p - M).  Also writes
-// the zero rows of empty sequences, which no wave visits.
+// Merge the pieces of one run (sequence s, kv head g), one wave per run: output row h =
+// sum_p w_p o_p / sum_p w_p with w_p = l_p * 2^(m_p - M), M = max_p m_p (flash-decoding's
+// combination of partial softmax results), times v_scale for an fp8 cache.  Lane p holds
+// piece p's (max, sum) for the G heads, so maxima, weights and sums come from one round of
+// loads and two wave reductions; each lane then owns D / 64 channels and reads the pieces'
+// rows UN at a time (up to 64 loads per lane in flight per round trip).  The kernel is
+// latency-bound (a few MB), so the chain of dependent loads is what it is built to keep short:
+// context length and run record, then (max, sum), then rows.  Also writes the zero rows of
+// empty sequences, which no streaming wave visits.
+constexpr int kMergeWaves = 4;  // runs per merge workgroup
+
 template <int QT, int KT, int D, int G>
-__global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a)
+__global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(const DecodeArgs a)
 {
-    const int row_id = blockIdx.x;  // s * Hq + h
-    const int s = row_id / a.num_heads;
-    const int h = row_id % a.num_heads;
-    const int g = h / G, hg = h % G;
-    const int lane = threadIdx.x;
     constexpr int PER = D / 64;
-    float acc[PER];
+    constexpr int UN = G * PER >= 8 ? 64 / (G * PER) : 8;  // pieces whose rows are loaded together
+    const int lane = threadIdx.x & 63;
+    const int64_t run = (int64_t)blockIdx.x * kMergeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (run >= (int64_t)a.num_seqs * a.num_kv_heads) return;
+    const int s = (int)(run / a.num_kv_heads), g = (int)(run % a.num_kv_heads);
+    const int ctx = seq_ctx(a, s);
+    const int64_t k0 = a.run_info[2 * run];
+    const int np = a.run_info[2 * run + 1];
+    float acc[G][PER];
+    float L[G];
 #pragma unroll
-    for (int j = 0; j < PER; j++) acc[j] = 0.0f;
-    float L = 0.0f;
-    if (seq_ctx(a, s) > 0) {
-        const int64_t run = (int64_t)s * a.num_kv_heads + g;
-        const int64_t k0 = a.run_info[2 * run];
-        const int np = a.run_info[2 * run + 1];
+    for (int h = 0; h < G; h++) {
+        L[h] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < PER; j++) acc[h][j] = 0.0f;
+    }
+    if (ctx > 0) {
         // whole run: written by the streaming kernel (the other checks only reject a workspace
         // the streaming kernel has not filled)
         if (np <= 1 || k0 < 0 || run + k0 + np > a.max_pieces) return;
         const int64_t p0 = run + k0;
-        float M = -FLT_MAX;
-        for (int p = 0; p < np; p++) M = __builtin_fmaxf(M, a.ml_part[((p0 + p) * G + hg) * 2]);
-        for (int p = 0; p < np; p++) {
-            const float* ml = a.ml_part + ((p0 + p) * G + hg) * 2;
-            const float wgt = ml[1] * fast_exp2(ml[0] - M);
-            L += wgt;
-            const float* op = a.o_part + ((p0 + p) * G + hg) * D;
+        auto load_ml = [&](int base, float (&m)[G], float (&l)[G]) {
+            const bool valid = base + lane < np;
+            const int64_t p = p0 + (valid ? base + lane : 0);
 #pragma unroll
-            for (int j = 0; j < PER; j++) acc[j] = __builtin_fmaf(wgt, op[lane + 64 * j], acc[j]);
+            for (int h = 0; h < G; h++) {
+                const float2 v = *reinterpret_cast<const float2*>(a.ml_part + (p * G + h) * 2);
+                m[h] = valid ? v.x : -FLT_MAX;
+                l[h] = valid ? v.y : 0.0f;
+            }
+        };
+        float m[G], l[G], M[G];
+        load_ml(0, m, l);
+#pragma unroll
+        for (int h = 0; h < G; h++) M[h] = wave_max(m[h]);
+        for (int base = 64; base < np; base += 64) {  // more than 64 pieces: small partitions
+            float m2[G], l2[G];
+            load_ml(base, m2, l2);
+#pragma unroll
+            for (int h = 0; h < G; h++) M[h] = __builtin_fmaxf(M[h], wave_max(m2[h]));
+        }
+        for (int base = 0; base < np; base += 64) {
+            if (base > 0) load_ml(base, m, l);
+            float w[G];
+#pragma unroll
+            for (int h = 0; h < G; h++) {
+                w[h] = l[h] * fast_exp2(m[h] - M[h]);
+                L[h] += wave_sum(w[h]);
+            }
+            const int n = min(64, np - base);
+            for (int i = 0; i < n; i += UN) {
+                float x[UN][G][PER];
+#pragma unroll
+                for (int u = 0; u < UN; u++) {
+                    const int64_t p = p0 + base + min(i + u, n - 1);  // past the end: re-read, weight 0
+#pragma unroll
+                    for (int h = 0; h < G; h++)
+#pragma unroll
+                        for (int j = 0; j < PER; j++) x[u][h][j] = a.o_part[(p * G + h) * D + lane + 64 * j];
+                }
+#pragma unroll
+                for (int u = 0; u < UN; u++) {
+                    const bool in = i + u < n;
+#pragma unroll
+                    for (int h = 0; h < G; h++) {
+                        const float wt = in ? as_float(__builtin_amdgcn_readlane(as_uint(w[h]), min(i + u, 63))) : 0.0f;
+#pragma unroll
+                        for (int j = 0; j < PER; j++) acc[h][j] = __builtin_fmaf(wt, x[u][h][j], acc[h][j]);
+                    }
+                }
+            }
         }
     }
     const float vs = kIsFp8<KT> ? a.v_scale[g] : 1.0f;
 #pragma unroll
-    for (int j = 0; j < PER; j++) {
-        const float v = L > 0.0f ? acc[j] / L * vs : 0.0f;
-        if constexpr (QT == kBF16)
-            static_cast<uint16_t*>(a.out)[(int64_t)row_id * D + lane + 64 * j] = f32_to_bf16_bits(v);
-        else
-            static_cast<float*>(a.out)[(int64_t)row_id * D + lane + 64 * j] = v;
+    for (int h = 0; h < G; h++) {
+        const int64_t row = (int64_t)s * a.num_heads + (int64_t)g * G + h;
+#pragma unroll
+        for (int j = 0; j < PER; j++) {
+            const float v = L[h] > 0.0f ? acc[h][j] / L[h] * vs : 0.0f;
+            if constexpr (QT == kBF16)
+                static_cast<uint16_t*>(a.out)[row * D + lane + 64 * j] = f32_to_bf16_bits(v);
+            else
+                static_cast<float*>(a.out)[row * D + lane + 64 * j] = v;
+        }
     }
 }
 
@@ -839,10 +897,11 @@ hipError_t launch_phase_t(int phase, const DecodeArgs& a, hipStream_t stream)
         if (e != hipSuccess) return e;
     }
     if ((phase & 2) && a.chunk_blocks >= 0) {  // one chunk per run: nothing to merge
-        const int64_t grid = (int64_t)a.num_seqs * a.num_heads;
+        const int64_t grid = ((int64_t)a.num_seqs * a.num_kv_heads + kMergeWaves - 1) / kMergeWaves;
         if (grid <= 0) return hipSuccess;
         if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((decode_merge_kernel<QT, KT, D, G>), dim3((unsigned)grid), dim3(64), 0, stream, a);
+        hipLaunchKernelGGL((decode_merge_kernel<QT, KT, D, G>), dim3((unsigned)grid), dim3(64 * kMergeWaves), 0,
+                           stream, a);
         return hipGetLastError();
     }
     return hipSuccess;

@@ -167,6 +167,18 @@ __device__ __forceinline__ float wave_max(float x)
     return x;
 }
 
+// Sum over all 64 lanes of a wave (every lane gets it).
+__device__ __forceinline__ float wave_sum(float x)
+{
+    x += dpp_f32<kDppQuadSwap1>(x);
+    x += dpp_f32<kDppQuadSwap2>(x);
+    x += dpp_f32<kDppRowRor4>(x);
+    x += dpp_f32<kDppRowRor8>(x);
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // 16-byte load with the nontemporal hint (global_load_dwordx4 ... nt): for data read once per

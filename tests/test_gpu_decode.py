@@ -325,3 +325,86 @@ def test_fused_append_equals_separate_calls(cache, P, B, short):
                           b.block_size, b.k_scale, b.v_scale)
     assert np.array_equal(raw(kp2), kp_h.view(np.uint8)) and np.array_equal(raw(vp2), vp_h.view(np.uint8))
     assert_close(b, out_to_f64(out2), oracle_attention(b, kp_h, vp_h))
+
+
+def _two_phase(db, kp, vp, partition_size=0):
+    """Reference bits: phase 1 (partials) then the separate merge kernel (phase 2)."""
+    b = db.b
+    ws = ops.decode_workspace(b.num_seqs, b.num_heads, b.num_kv_heads, b.head_dim, b.max_context_len,
+                              b.block_size, partition_size)
+    out = torch.empty_like(db.query)
+    db.decode(kp, vp, partition_size=partition_size, phase=1, out=out, workspace=ws)
+    db.decode(kp, vp, partition_size=partition_size, phase=2, out=out, workspace=ws)
+    return out
+
+
+@pytest.mark.parametrize("cache", [W.BF16, W.FP8_E4M3])
+def test_decode_any_workspace_contents(cache):
+    """Whatever bytes the workspace holds before the call (random, all ones, every byte 0x80,
+    zeros) -- stale run records and partial rows included -- the one-call decode gives the
+    two-phase form's bits, repeated calls on one workspace give the same bits, and an empty
+    sequence among split ones gets zero rows."""
+    b = W.build_batch([100, 900, 2000, 50, 4096, 17, 1500], num_heads=32, num_kv_heads=8, head_dim=128,
+                      q_dtype=W.BF16, cache_dtype=cache, seed=3)
+    kp_h, vp_h = oracle_pool(b, include_new=True)
+    db = DeviceBatch(b)
+    kp, vp = to_dev(kp_h, b.cache_dtype), to_dev(vp_h, b.cache_dtype)
+    want = _two_phase(db, kp, vp)
+    assert_close(b, out_to_f64(want), oracle_attention(b, kp_h, vp_h))
+    ws = ops.decode_workspace(b.num_seqs, b.num_heads, b.num_kv_heads, b.head_dim, b.max_context_len, b.block_size)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    fills = [torch.randint(0, 256, ws.shape, dtype=torch.uint8, generator=g).cuda(),
+             torch.full_like(ws, 0xFF), torch.full_like(ws, 0x80), torch.zeros_like(ws)]
+    for i, fill in enumerate(fills):
+        ws.copy_(fill)
+        for rep in range(3):  # the later calls see what the earlier ones left
+            got = db.decode(kp, vp, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), "fill %d, call %d" % (i, rep)
+    # an empty sequence among split ones (its run record in the workspace is stale)
+    db.ctx = db.ctx.clone()
+    db.ctx[3] = 0
+    want0 = _two_phase(db, kp, vp)
+    for i, fill in enumerate(fills):
+        ws.copy_(fill)
+        got = db.decode(kp, vp, workspace=ws)
+        assert torch.equal(got.view(torch.uint8), want0.view(torch.uint8)), "empty sequence, fill %d" % i
+        assert torch.count_nonzero(got[3].float()) == 0
+
+
+def test_decode_workspace_reused_across_shapes():
+    """One workspace sized for the largest batch serves calls of other shapes in any order (one
+    call's run records land on bytes another call used for partial rows)."""
+    big = W.build_batch([3000, 64, 2500, 129, 4000, 1000, 2222, 17] * 4, num_heads=32, num_kv_heads=8,
+                        head_dim=128, q_dtype=W.BF16, cache_dtype=W.BF16, seed=11)
+    small = W.build_batch([700, 4096, 300], num_heads=16, num_kv_heads=2, head_dim=128, q_dtype=W.BF16,
+                          cache_dtype=W.BF16, seed=12)
+    cases = []
+    for b in (big, small):
+        kp_h, vp_h = oracle_pool(b, include_new=True)
+        db = DeviceBatch(b)
+        kp, vp = to_dev(kp_h, b.cache_dtype), to_dev(vp_h, b.cache_dtype)
+        cases.append((b, db, kp, vp, kp_h, vp_h))
+    n = max(ops.decode_workspace_size(b.num_seqs, b.num_heads, b.num_kv_heads, b.head_dim, b.max_context_len,
+                                      b.block_size, P) for b in (big, small) for P in (0, 32))
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    for b, db, kp, vp, kp_h, vp_h in cases + cases[::-1] + cases:
+        for P in (0, 32):
+            want = _two_phase(db, kp, vp, P)
+            got = db.decode(kp, vp, partition_size=P, workspace=ws)
+            assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), (b.num_seqs, P)
+    for b, db, kp, vp, kp_h, vp_h in cases:
+        assert_close(b, out_to_f64(db.decode(kp, vp, workspace=ws)), oracle_attention(b, kp_h, vp_h))
+
+
+def test_merge_more_than_64_pieces_per_run():
+    """16-token partitions over 4096-token contexts: 256 pieces per run, so the merge walks its
+    (max, sum) pairs in several 64-lane windows."""
+    b = W.build_batch([4096, 1100, 4000], num_heads=8, num_kv_heads=2, head_dim=64, q_dtype=W.F32,
+                      cache_dtype=W.F32, seed=13)
+    kp_h, vp_h = oracle_pool(b, include_new=True)
+    db = DeviceBatch(b)
+    kp, vp = to_dev(kp_h, b.cache_dtype), to_dev(vp_h, b.cache_dtype)
+    got = db.decode(kp, vp, partition_size=16)
+    assert_close(b, out_to_f64(got), oracle_attention(b, kp_h, vp_h))
+    assert torch.equal(got, _two_phase(db, kp, vp, 16))
