@@ -60,8 +60,9 @@ def parse_args():
                    choices=["none", "fp8_chunked_prefill", "fp8_e5m2_chunked_prefill", "llama3_8b_decode",
                             "long_context", "mixed_continuous_batch"],
                    help="second workload measured in the same run and reported under extra_step")
-    p.add_argument("--fused-append", action="store_true",
-                   help="decode rows append their new token inside the decode call (pa_paged_attention_decode_append)")
+    p.add_argument("--separate-append", action="store_true",
+                   help="append every row with pa_kv_cache_write before the decode call; by default the decode "
+                        "rows append their new token inside the decode call (pa_paged_attention_decode_append)")
     p.add_argument("--graph", action="store_true",
                    help="also replay the step from HIP graphs and report it under graph_step")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -117,7 +118,8 @@ def make_batch(name, block_size=16):
 
 
 KERNEL_SOURCES = {
-    "decode": ("decode.hip", "pa_device.hpp", "pa_internal.hpp"),
+    "decode": ("decode_kernel.hpp", "decode.hip", "decode_fused.hip", "kv_store.hpp", "pa_device.hpp",
+               "pa_internal.hpp"),
     "prefill": ("prefill.hip", "pa_device.hpp", "pa_internal.hpp"),
 }
 
@@ -132,9 +134,11 @@ def source_digest(kernel="decode"):
     return h.hexdigest()[:16]
 
 
-def traffic_key(batch):
-    """Counter records are kept per workload, and per block size when it is not 16."""
-    return batch.name if batch.block_size == 16 else "%s/b%d" % (batch.name, batch.block_size)
+def traffic_key(batch, fused=True):
+    """Counter records are kept per workload, per append form (the decode kernel with the fused
+    append, or alone after pa_kv_cache_write) and per block size when it is not 16."""
+    key = batch.name if fused else "%s/separate" % batch.name
+    return key if batch.block_size == 16 else "%s/b%d" % (key, batch.block_size)
 
 
 def stored_traffic(workload, digest, kernel="decode"):
@@ -417,9 +421,10 @@ def measure(batch, dev, layers, steps, warmup, partition_size=0, fused=False, gr
         if fused:
             part_bytes += dec.write_bytes() - 8 * dec.num_rows  # appended rows (no slot ids: the table gives them)
         achieved = part_bytes / (kernels["decode_stream"] * 1e-6) / 1e9
-        res["roofline"] = {"bound": "hbm", "kernel": "decode_stream_kernel", "achieved": round(achieved, 1),
+        res["roofline"] = {"bound": "hbm", "kernel": "decode_stream_kernel" + (" (fused append)" if fused else ""),
+                           "achieved": round(achieved, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                           "traffic": stored_traffic(traffic_key(batch), digest),
+                           "traffic": stored_traffic(traffic_key(batch, fused), digest),
                            "algorithmic_bytes_per_launch": int(part_bytes), "source_digest": digest}
     if Sp:
         pos = [np.arange(c - q, c, dtype=np.int64) for c, q in zip(batch.context_lens[:Sp], ql[:Sp])]
@@ -460,13 +465,13 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     batch = make_batch(args.workload, args.block_size)
-    res, stream = measure(batch, dev, args.layers, args.steps, args.warmup, args.partition_size, args.fused_append,
-                          args.graph)
+    fused = not args.separate_append
+    res, stream = measure(batch, dev, args.layers, args.steps, args.warmup, args.partition_size, fused, args.graph)
     if args.extra_workload != "none" and args.extra_workload != args.workload:
         # The rest of the hot path in the same run: the fp8 cache (in-kernel dequant) and the
         # chunked-prefill kernel, on the mixed step (one layer).
         extra = make_batch(args.extra_workload, args.block_size)
-        xres, _ = measure(extra, dev, 1, args.steps, min(args.warmup, 2), 0, args.fused_append)
+        xres, _ = measure(extra, dev, 1, args.steps, min(args.warmup, 2), 0, fused)
         keep = ("value", "unit", "ms_per_step", "steps", "warmup", "config", "seqs_per_s_per_layer", "step_bytes",
                 "kernels_us", "roofline", "roofline_prefill")
         res["extra_step"] = {k: xres[k] for k in keep if k in xres}

@@ -230,12 +230,13 @@ int32_t pa_paged_attention_chunked_prefill(void* out, const void* query, int32_t
  * new token -- new_key[s] and new_value[s] -- at position context_lens[s] - 1, i.e. slot
  * block_tables[s][(ctx - 1) / block_size] * block_size + (ctx - 1) % block_size, exactly as
  * pa_kv_cache_write would (same bytes, including the fp8 encode); then the decode runs as
- * pa_paged_attention_decode_phase with the same arguments.
+ * pa_paged_attention_decode_phase with the same arguments (the same output bits).
  *   new_key, new_value  device [num_seqs][num_kv_heads][head_dim] in q_dtype (the source dtype
  *                  of the append), 16-byte aligned.
  *   k_pool, v_pool device pools, written at the new tokens' slots.
- * The store is done in phase 1, by the wave that later reads the token's block, so the new
- * token is attended to in the same call.  A new token's block must not be shared with another
+ * Phase 1 does both: the wave that attends the token's block takes the new token from its
+ * input row (encoded as the cache stores it) into the block it has loaded, and stores the row
+ * into the slot, so no wait orders the store before a read.  A new token's block must not be shared with another
  * sequence (the same rule as for pa_kv_cache_write's distinct slots).  Other arguments, errors
  * and the workspace as for pa_paged_attention_decode_phase; phase 2 alone appends nothing.
  */

@@ -1,784 +1,10 @@
-// decode.hip -- PagedAttention decode for gfx950: balanced streaming kernel + merge kernel.
-//
-// The attention of one decode query over its sequence's cache is softmax(q K^T * scale) V
-// (page 1, section 2), read block by block through the sequence's block table (page 1,
-// section 4; page 3, section 2.1), with the G query heads of a GQA group sharing one KV head
-// (page 1, section 10).
-//
-// Work decomposition.  The K/V blocks of every (sequence, kv head) pair -- a "run" -- are
-// laid end to end, sequence-major then kv head, into one list of U units (one unit = one
-// 16-token block of one kv head).  The list is cut into chunks of C units and the waves of a
-// persistent grid take one chunk each, or chunks w, w + NW, ... for a caller-given size (by
-// default C = ceil(U / NW): one chunk per wave, so every wave moves the same number of bytes
-// and the kernel has no tail).  Chunk k runs on XCD k mod 8.
-// A chunk that covers runs r1..r2 attends each covered piece of a run on its own (online
-// softmax state reset per piece) and stores the piece's normalised row and (max, sum) as a
-// partial result; a run covered by one piece writes its output row directly.  The merge
-// kernel combines the pieces of every split run (flash-decoding split-K).  Piece ids are
-// run + chunk, which is one-to-one over non-empty pieces (a later run can only meet a later
-// chunk), so the workspace size depends only on the numbers of runs and chunks.
-//
-// Inside a wave, per 16-token block (pool layout in include/pagedattn.h) NCH K loads and NCH V
-// loads of 16 bytes per lane each read one contiguous 1 KiB slice, with the nontemporal hint
-// (every K/V byte is read once per launch):
-//   QK^T: lane l holds channels of token l/4; bf16/fp8 K is multiplied with bf16 query pairs
-//         (held in VGPRs for the piece) by v_dot2c_f32_bf16 (fp8 first widened exactly to bf16
-//         pairs), fp32 K with FMAs; the 4 lanes of a token finish the dot product with two DPP
-//         quad moves.
-//   softmax: online, in base 2.  The running max is wave-uniform and only moved when a score
-//         exceeds it by more than 8 (then o and l are rescaled), so most blocks skip the
-//         rescale; weights stay below 2^8, and normalisation happens once per piece.
-//   PV:   the block's weights are packed to bf16 pairs (the partner token's weight comes from
-//         the neighbouring quad by one ds_swizzle) and read into scalar registers; each V load
-//         gives every lane one channel of 8 (bf16) or 16 (fp8) consecutive tokens, contracted
-//         with the pairs by v_dot2c_f32_bf16 (fp32: FMAs).  The accumulator is one fp32 per
-//         (channel group, head) per lane.
-// An NST-deep ring of register buffers keeps NST-1 blocks of K and V in flight while one is
-// attended; all loop bounds are wave-uniform, so the waits on the ring stay counted.
-#include <float.h>
-
-#include "kv_store.hpp"
-#include "pa_device.hpp"
-#include "pa_internal.hpp"
+// decode.hip -- PagedAttention decode for gfx950: launchers of the streaming kernel
+// (decode_kernel.hpp; its fused-append instances are in decode_fused.hip) and the merge kernel
+// that combines the pieces of split sequences (flash-decoding split-K).
+#include "decode_kernel.hpp"
 
 namespace pa {
 namespace {
-
-constexpr float kRescaleMargin = 8.0f;  // log2 units: weights are kept <= 2^8
-
-template <int QT, int KT, int D, int G>
-struct Shape {
-    static constexpr int EB = DtypeBytes<KT>::value;
-    static constexpr int W = 64 / EB;      // channels per 64-byte slice
-    static constexpr int NCH = D / W;      // 1 KiB slices per (block, kv head) tile
-    static constexpr int KE = W / 4;       // K channels per lane per slice
-    static constexpr int TPC = 16 / EB;    // V: tokens of one channel per 16-byte piece
-    static constexpr int NQ = kUnitTokens / TPC;  // V: token groups per unit
-    static constexpr int CG = D / 64;      // V: 64-channel groups (one channel per lane)
-    static constexpr int TILE = kUnitTokens * D * EB;  // bytes of one unit (16 tokens, one kv head)
-    static constexpr int QB = DtypeBytes<QT>::value;
-    static constexpr int QBYTES = G * D * QB;  // one GQA group's query rows
-    static_assert(TILE == NCH * 1024, "a tile is a whole number of 1 KiB slices");
-    static_assert(NQ * CG == NCH, "V: one 1 KiB load per (token group, channel group)");
-    static_assert((QT == kF32) == (KT == kF32), "fp32 queries go with an fp32 cache");
-    static_assert(QBYTES % 16 == 0, "query staging in whole 16-byte pieces");
-};
-
-template <int QT, int KT, int D, int G>
-struct Acc {
-    using S = Shape<QT, KT, D, G>;
-    float o[S::CG][G];  // channel cg * 64 + lane
-    float l[G];
-    float m[G];
-};
-
-// The lane's query channels for every slice: the 16 (fp8 cache: 32) bytes of each (slice c,
-// head h) that meet this lane's K elements.  Held in VGPRs for the whole piece.
-template <int QT, int KT, int D, int G>
-struct QRegs {
-    using S = Shape<QT, KT, D, G>;
-    static constexpr int NQW = kIsFp8<KT> ? 8 : 4;  // dwords per (slice, head)
-    uint32_t w[S::NCH][G][NQW];
-};
-
-template <int QT, int KT, int D, int G>
-__device__ __forceinline__ void load_q(QRegs<QT, KT, D, G>& q, const unsigned char* qrow, int kp)
-{
-    using S = Shape<QT, KT, D, G>;
-#pragma unroll
-    for (int c = 0; c < S::NCH; c++)
-#pragma unroll
-        for (int h = 0; h < G; h++) {
-            const unsigned char* src = qrow + (h * D + c * S::W + kp * S::KE) * S::QB;
-#pragma unroll
-            for (int i = 0; i < QRegs<QT, KT, D, G>::NQW; i += 4) {
-                const uint4 v = load16(src + i * 4);
-                q.w[c][h][i] = v.x;
-                q.w[c][h][i + 1] = v.y;
-                q.w[c][h][i + 2] = v.z;
-                q.w[c][h][i + 3] = v.w;
-            }
-        }
-}
-
-// The query kept in the wave's LDS copy instead: the same dwords are read per slice as
-// they are needed.  The copy's LDS offset is made opaque to the compiler once per block --
-// otherwise the loop-invariant reads are hoisted back into VGPRs -- with an empty asm on a
-// scalar register, which (unlike a volatile access) adds no memory wait that would drain the
-// K/V ring.
-struct QLds {
-    const unsigned char* base;
-    int off;
-};
-
-__device__ __forceinline__ int opaque(int x)
-{
-    asm volatile("" : "+s"(x));
-    return x;
-}
-
-template <int QT, int KT, int D, int G>
-__device__ __forceinline__ void q_dwords(const QRegs<QT, KT, D, G>& q, int c, int h, int kp, uint32_t (&qw)[QRegs<QT, KT, D, G>::NQW])
-{
-#pragma unroll
-    for (int i = 0; i < QRegs<QT, KT, D, G>::NQW; i++) qw[i] = q.w[c][h][i];
-    (void)kp;
-}
-
-template <int QT, int KT, int D, int G>
-__device__ __forceinline__ void q_dwords(const QLds& q, int c, int h, int kp, uint32_t (&qw)[QRegs<QT, KT, D, G>::NQW])
-{
-    using S = Shape<QT, KT, D, G>;
-    const unsigned char* p = q.base + q.off + (h * D + c * S::W + kp * S::KE) * S::QB;
-#pragma unroll
-    for (int i = 0; i < QRegs<QT, KT, D, G>::NQW; i += 4) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p + i * 4);
-        qw[i] = v.x;
-        qw[i + 1] = v.y;
-        qw[i + 2] = v.z;
-        qw[i + 3] = v.w;
-    }
-}
-
-// Partial dot products of this lane's K channels with the G query rows.
-template <int QT, int KT, int D, int G, class QSrc>
-__device__ __forceinline__ void qk_slice(const QSrc& q, int kp, int c, const uint4& kv, float (&acc)[G])
-{
-#pragma unroll
-    for (int h = 0; h < G; h++) {
-        uint32_t qw[QRegs<QT, KT, D, G>::NQW];
-        q_dwords<QT, KT, D, G>(q, c, h, kp, qw);
-        if constexpr (KT == kBF16) {
-            acc[h] = dot2_bf16(kv.x, qw[0], acc[h]);
-            acc[h] = dot2_bf16(kv.y, qw[1], acc[h]);
-            acc[h] = dot2_bf16(kv.z, qw[2], acc[h]);
-            acc[h] = dot2_bf16(kv.w, qw[3], acc[h]);
-        } else if constexpr (kIsFp8<KT>) {
-            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, false>(kv.x), qw[0], acc[h]);
-            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, true>(kv.x), qw[1], acc[h]);
-            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, false>(kv.y), qw[2], acc[h]);
-            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, true>(kv.y), qw[3], acc[h]);
-            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, false>(kv.z), qw[4], acc[h]);
-            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, true>(kv.z), qw[5], acc[h]);
-            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, false>(kv.w), qw[6], acc[h]);
-            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, true>(kv.w), qw[7], acc[h]);
-        } else {
-            acc[h] = __builtin_fmaf(as_float(kv.x), as_float(qw[0]), acc[h]);
-            acc[h] = __builtin_fmaf(as_float(kv.y), as_float(qw[1]), acc[h]);
-            acc[h] = __builtin_fmaf(as_float(kv.z), as_float(qw[2]), acc[h]);
-            acc[h] = __builtin_fmaf(as_float(kv.w), as_float(qw[3]), acc[h]);
-        }
-    }
-}
-
-// o[cg] += sum over the TPC tokens of V load c of p[token] * V[token][channel]: the weights
-// are wave-uniform (scalar registers), each lane owns one channel.  bf16 / fp8 weights come
-// as bf16 pairs (tokens 2i, 2i+1) and meet V pairs of the same tokens in v_dot2c_f32_bf16;
-// fp32 uses one FMA per token.
-template <int QT, int KT, int D, int G>
-__device__ __forceinline__ void pv_load(Acc<QT, KT, D, G>& st, int c, const uint4& vv, const uint32_t (&pps)[G][8],
-                                        const float (&ps)[G][16])
-{
-    using S = Shape<QT, KT, D, G>;
-    const int q = c / S::CG, cg = c % S::CG;
-    if constexpr (KT == kBF16) {
-#pragma unroll
-        for (int h = 0; h < G; h++) {
-            st.o[cg][h] = dot2_bf16(vv.x, pps[h][q * 4 + 0], st.o[cg][h]);
-            st.o[cg][h] = dot2_bf16(vv.y, pps[h][q * 4 + 1], st.o[cg][h]);
-            st.o[cg][h] = dot2_bf16(vv.z, pps[h][q * 4 + 2], st.o[cg][h]);
-            st.o[cg][h] = dot2_bf16(vv.w, pps[h][q * 4 + 3], st.o[cg][h]);
-        }
-    } else if constexpr (kIsFp8<KT>) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const uint32_t w = u4_get(vv, i);
-            const uint32_t lo = fp8x2_to_bf16x2<KT, false>(w);
-            const uint32_t hi = fp8x2_to_bf16x2<KT, true>(w);
-#pragma unroll
-            for (int h = 0; h < G; h++) {
-                st.o[cg][h] = dot2_bf16(lo, pps[h][2 * i], st.o[cg][h]);
-                st.o[cg][h] = dot2_bf16(hi, pps[h][2 * i + 1], st.o[cg][h]);
-            }
-        }
-    } else {
-#pragma unroll
-        for (int h = 0; h < G; h++) {
-            st.o[cg][h] = __builtin_fmaf(ps[h][q * 4 + 0], as_float(vv.x), st.o[cg][h]);
-            st.o[cg][h] = __builtin_fmaf(ps[h][q * 4 + 1], as_float(vv.y), st.o[cg][h]);
-            st.o[cg][h] = __builtin_fmaf(ps[h][q * 4 + 2], as_float(vv.z), st.o[cg][h]);
-            st.o[cg][h] = __builtin_fmaf(ps[h][q * 4 + 3], as_float(vv.w), st.o[cg][h]);
-        }
-    }
-}
-
-// Zero the V elements of tokens at or past n_valid in V load c (they may hold anything,
-// including NaN, and 0 * NaN would leak into the sum).
-template <int QT, int KT, int D, int G>
-__device__ __forceinline__ uint4 mask_tail(uint4 v, int c, int n_valid)
-{
-    using S = Shape<QT, KT, D, G>;
-    constexpr int EPD = 4 / S::EB;  // elements (tokens) per dword
-    const int t0 = (c / S::CG) * S::TPC;
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        uint32_t m = 0;
-#pragma unroll
-        for (int e = 0; e < EPD; e++)
-            if (t0 + i * EPD + e < n_valid) m |= (EPD == 1 ? 0xFFFFFFFFu : ((1u << (32 / EPD)) - 1u) << (e * 32 / EPD));
-        w[i] &= m;
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
-template <int QT, int KT, int D, int G, class QSrc>
-__device__ __forceinline__ void attend_block(Acc<QT, KT, D, G>& st, const QSrc& q,
-                                             const uint4 (&kb)[Shape<QT, KT, D, G>::NCH],
-                                             const uint4 (&vb)[Shape<QT, KT, D, G>::NCH], int n_valid, float c2,
-                                             int lane)
-{
-    using S = Shape<QT, KT, D, G>;
-    float acc[G];
-#pragma unroll
-    for (int h = 0; h < G; h++) acc[h] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < S::NCH; c++) qk_slice<QT, KT, D, G>(q, lane & 3, c, kb[c], acc);
-
-    const int tok = lane >> 2;  // this lane's token within the block
-    float s2[G];
-#pragma unroll
-    for (int h = 0; h < G; h++) {
-        s2[h] = quad_sum(acc[h]) * c2;
-        if (n_valid < kUnitTokens) s2[h] = tok < n_valid ? s2[h] : -__builtin_inff();
-    }
-
-    bool need = false;
-#pragma unroll
-    for (int h = 0; h < G; h++) need |= s2[h] > st.m[h] + kRescaleMargin;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-        for (int h = 0; h < G; h++) {
-            const float mn = __builtin_fmaxf(st.m[h], wave_max(s2[h]));
-            const float alpha = fast_exp2(st.m[h] - mn);
-            st.m[h] = mn;
-            st.l[h] *= alpha;
-#pragma unroll
-            for (int cg = 0; cg < S::CG; cg++) st.o[cg][h] *= alpha;
-        }
-    }
-
-    const bool odd = (tok & 1) != 0;
-    uint32_t pps[G][8];  // bf16 weight pairs of tokens (2i, 2i+1), wave-uniform
-    float ps[G][16];     // fp32 weight of token t, wave-uniform
-#pragma unroll
-    for (int h = 0; h < G; h++) {
-        const float mine = fast_exp2(s2[h] - st.m[h]);
-        const float other = swizzle_xor4(mine);  // weight of the other token of the pair
-        // l gathers each pair's weights once per lane; the 8 lanes of a pair are folded at
-        // the end of the piece
-        if constexpr (KT == kF32) {
-            st.l[h] += mine + other;
-#pragma unroll
-            for (int t = 0; t < kUnitTokens; t++) ps[h][t] = as_float(__builtin_amdgcn_readlane(as_uint(mine), 4 * t));
-        } else {
-            const uint32_t pp = pack_bf16x2(odd ? other : mine, odd ? mine : other);
-            st.l[h] = dot2_bf16(pp, kBf16OnePair, st.l[h]);
-#pragma unroll
-            for (int i = 0; i < 8; i++) pps[h][i] = __builtin_amdgcn_readlane(pp, 8 * i);
-        }
-    }
-
-    if (n_valid < kUnitTokens) {
-#pragma unroll
-        for (int c = 0; c < S::NCH; c++) pv_load<QT, KT, D, G>(st, c, mask_tail<QT, KT, D, G>(vb[c], c, n_valid), pps, ps);
-    } else {
-#pragma unroll
-        for (int c = 0; c < S::NCH; c++) pv_load<QT, KT, D, G>(st, c, vb[c], pps, ps);
-    }
-}
-
-// ---- work-list arithmetic ---------------------------------------------------------------
-
-// Context length the kernels use for sequence s: clamped to [0, max_context_len], so a
-// length beyond the caller's bound can never send a table read or a workspace write out of
-// range (the caller's contract is context_lens[s] <= max_context_len).
-__device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int c)
-{
-    return c < 0 ? 0 : (c > a.max_context_len ? a.max_context_len : c);
-}
-
-__device__ __forceinline__ int seq_ctx(const DecodeArgs& a, int s) { return clamp_ctx(a, a.context_lens[s]); }
-
-// Tokens per work unit, as a shift: 16, or 8 for 8-token blocks (one block per unit, the unit's
-// upper half empty).
-__device__ __forceinline__ int unit_shift(int block_size) { return block_size < kUnitTokens ? 3 : 4; }
-__device__ __forceinline__ int nunits(int ctx, int ush) { return (ctx + (1 << ush) - 1) >> ush; }
-
-__device__ __forceinline__ int wave_incl_scan(int x, int lane)
-{
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(x, d, 64);
-        x += lane >= d ? y : 0;
-    }
-    return x;
-}
-
-constexpr int kScanPerLane = 16;  // sequences per lane in one pass over the context lengths
-constexpr int kScanWindow = 64 * kScanPerLane;
-
-struct Pos {
-    int s, g, j;        // run (sequence s, kv head g), block j of the run
-    int64_t run_start;  // unit index of the run's block 0
-};
-
-// The list's total U and the position of unit chunk_start(U), from the clamped context
-// lengths in LDS.  Lane l holds sequences base + 16 l .. base + 16 l + 15 of each
-// 1024-sequence window.
-struct Plan {
-    int64_t U;
-    Pos p;
-};
-
-template <class ChunkStart>
-__device__ __forceinline__ Plan plan_wave(const DecodeArgs& a, const int* lctx, int lane, ChunkStart chunk_start)
-{
-    const int Hkv = a.num_kv_heads, S = a.num_seqs;
-    const int ush = unit_shift(a.block_size);
-    // total
-    int64_t total = 0;
-    for (int base = 0; base < S; base += kScanWindow) {
-        int part = 0;
-#pragma unroll
-        for (int i = 0; i < kScanPerLane; i++) {
-            const int s = base + lane * kScanPerLane + i;
-            part += s < S ? nunits(lctx[s], ush) : 0;
-        }
-        total += __builtin_amdgcn_readlane(wave_incl_scan(part, lane), 63);
-    }
-    Plan pl;
-    pl.U = total * Hkv;
-    const int64_t u0 = chunk_start(pl.U);
-    pl.p.s = S;
-    pl.p.g = pl.p.j = 0;
-    pl.p.run_start = pl.U;
-    if (u0 >= pl.U) return pl;
-    // locate u0
-    int64_t before = 0;
-    for (int base = 0; base < S; base += kScanWindow) {
-        int nb[kScanPerLane];
-        int part = 0;
-#pragma unroll
-        for (int i = 0; i < kScanPerLane; i++) {
-            const int s = base + lane * kScanPerLane + i;
-            nb[i] = s < S ? nunits(lctx[s], ush) : 0;
-            part += nb[i];
-        }
-        const int incl = wave_incl_scan(part, lane);
-        const uint64_t hit = __builtin_amdgcn_ballot_w64(before + (int64_t)incl * Hkv > u0);
-        if (hit) {
-            const int L = __builtin_ctzll(hit);
-            int64_t u = before + (int64_t)(__builtin_amdgcn_readlane(incl, L) - __builtin_amdgcn_readlane(part, L)) * Hkv;
-#pragma unroll
-            for (int i = 0; i < kScanPerLane; i++) {
-                const int n = __builtin_amdgcn_readlane(nb[i], L);
-                const int64_t span = (int64_t)n * Hkv;
-                if (u0 < u + span) {
-                    const int64_t off = u0 - u;
-                    pl.p.s = base + L * kScanPerLane + i;
-                    pl.p.g = (int)(off / n);
-                    pl.p.j = (int)(off % n);
-                    pl.p.run_start = u + (int64_t)pl.p.g * n;
-                    return pl;
-                }
-                u += span;
-            }
-        }
-        before += (int64_t)__builtin_amdgcn_readlane(incl, 63) * Hkv;
-    }
-    return pl;  // not reached
-}
-
-// A position in the work list that moves block by block: (sequence, kv head, block) with
-// the run's context length.  Sequences with no context are skipped.
-struct Cursor {
-    int s, g, j, ctx, nbs;
-    int ush;  // unit_shift of the block size
-    int64_t run_start;
-};
-
-__device__ __forceinline__ Cursor cursor_at(const Pos& p, const int* lctx, int ush)
-{
-    Cursor c;
-    c.ush = ush;
-    c.s = p.s;
-    c.g = p.g;
-    c.j = p.j;
-    c.ctx = lctx[p.s];
-    c.nbs = nunits(c.ctx, c.ush);
-    c.run_start = p.run_start;
-    return c;
-}
-
-__device__ __forceinline__ void cursor_next(Cursor& c, const int* lctx, int num_seqs, int num_kv_heads)
-{
-    if (++c.j < c.nbs) return;
-    c.run_start += c.nbs;
-    c.j = 0;
-    if (++c.g < num_kv_heads) return;
-    c.g = 0;
-    do {
-        ++c.s;
-        c.ctx = c.s < num_seqs ? lctx[c.s] : 0;
-    } while (c.ctx == 0 && c.s < num_seqs);
-    c.nbs = nunits(c.ctx, c.ush);
-}
-
-// Move the cursor to block 0 of the next run (next kv head, or the next non-empty sequence).
-__device__ __forceinline__ void next_run(Cursor& c, const int* lctx, int num_seqs, int num_kv_heads)
-{
-    c.run_start += c.nbs;
-    c.j = 0;
-    if (++c.g < num_kv_heads) return;
-    c.g = 0;
-    do {
-        ++c.s;
-        c.ctx = c.s < num_seqs ? lctx[c.s] : 0;
-    } while (c.ctx == 0 && c.s < num_seqs);
-    c.nbs = nunits(c.ctx, c.ush);
-}
-
-// Fused append: the chunk that holds a run's last block is the only one that reads it, so its
-// wave stores the run's new token (position ctx - 1, source row [s][g] of new_key/new_value)
-// before streaming, with the same piece stores as the append kernel; a workgroup-scope fence
-// then orders those stores before the wave's own loads of the block.  Lanes 0..P-1 store the
-// K row's P 16-byte pieces, lanes P..2P-1 the V row's.
-template <int ST, int CT, int D>
-__device__ __forceinline__ void append_chunk_tokens(const DecodeArgs& a, const int* lctx, const Pos& p0, int64_t u_end,
-                                                    int lane)
-{
-    constexpr int ES = DtypeBytes<ST>::value;
-    constexpr int N = 16 / ES;  // source elements per piece
-    constexpr int P = D / N;    // pieces per source row
-    static_assert(2 * P <= 64, "the K and V rows of a token fit one wave");
-    const int Hkv = a.num_kv_heads, NS = a.num_seqs, B = a.block_size;
-    Cursor c = cursor_at(p0, lctx, unit_shift(B));
-    bool stored = false;
-    while (c.s < NS && c.run_start + c.nbs <= u_end) {  // this run ends inside the chunk
-        const int t = c.ctx - 1;
-        const int phys = a.block_tables[(int64_t)c.s * a.max_blocks_per_seq + t / B];
-        if (lane < 2 * P && phys >= 0 && (int64_t)phys < a.num_blocks) {
-            const int kv = lane / P, piece = lane % P;
-            const unsigned char* src = static_cast<const unsigned char*>(kv ? a.new_value : a.new_key) +
-                                       (((int64_t)c.s * Hkv + c.g) * D + piece * N) * ES;
-            const int64_t tile = ((int64_t)phys * Hkv + c.g) * B * D;
-            unsigned char* pool = static_cast<unsigned char*>(kv ? a.v_pool : a.k_pool);
-            const float sc = kIsFp8<CT> && ST != CT ? (kv ? a.v_scale : a.k_scale)[c.g] : 1.0f;
-            store_kv_piece<ST, CT>(load16(src), pool, tile, piece * N, t % B, kv, D, B, sc);
-        }
-        stored = true;
-        next_run(c, lctx, NS, Hkv);
-    }
-    if (stored) __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-}
-
-// ---- the streaming kernel ---------------------------------------------------------------
-
-// Per (cache dtype): where the query lives and how deep the K/V ring is.  Measured on the
-// Llama-3-8B-shaped bf16 batch: query in VGPRs with a 2-deep ring beats query in LDS with a
-// 3-deep ring (118 vs 121 us); an fp32 query does not fit in VGPRs beside the ring.
-template <int KT>
-struct Variant {
-    static constexpr bool kQueryInLds = KT == kF32;
-    static constexpr int kDepth = kQueryInLds ? 3 : 2;
-};
-
-// Chunks of the unit list: chunk k = units [k*C, (k+1)*C).
-struct ChunkMap {
-    int64_t C;
-    __device__ int64_t start(int64_t k) const { return k * C; }
-    __device__ int64_t size(int64_t) const { return C; }
-    __device__ int64_t of_unit(int64_t u) const { return u / C; }
-};
-
-// Occupancy of the streaming kernel, chosen per variant from measurements on MI355X (stream
-// kernel alone, Llama-shaped batch with the variant's heads):
-//   3 waves per SIMD (at most 168 VGPRs, no spills) where that measured faster: fp8 with G <= 4
-//     (70.3 -> 66.4 us at D 128) and D 64 with G <= 4 (bf16: 60.0 -> 55.5 us);
-//   2 forced for bf16 D 128 G 8, which otherwise takes 296 registers and runs one wave per
-//     SIMD (157 -> 139 us despite a few spills), and for fp8 G 8 (it fits 256 registers);
-//   otherwise the compiler's choice: 2 waves per SIMD for most variants (bf16 G 1 / 2 measured
-//     slower at 3), one for fp32 D 128, which measured slower when forced to 2 with spills.
-// The persistent grid has max(2, this) waves per SIMD.
-template <int KT, int D, int G>
-constexpr int stream_min_waves()
-{
-    if constexpr (KT == kF32) return 1;
-    else if constexpr (KT == kBF16) return D == 64 && G <= 4 ? 3 : D == 128 && G == 8 ? 2 : 1;
-    else return G <= 4 ? 3 : 2;
-}
-
-template <int KT, int D, int G>
-constexpr int stream_waves_per_simd()
-{
-    return stream_min_waves<KT, D, G>() > 2 ? stream_min_waves<KT, D, G>() : 2;
-}
-
-// PER_RUN: the one-chunk-per-run form (chunk_blocks < 0), a separate instance so that its
-// extra paths leave the balanced form's registers alone.
-template <int QT, int KT, int D, int G, bool PER_RUN>
-__global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) void decode_stream_kernel(
-    const DecodeArgs a)
-{
-    using S = Shape<QT, KT, D, G>;
-    constexpr bool QL = Variant<KT>::kQueryInLds;
-    constexpr int NST = Variant<KT>::kDepth;
-    const int lane = threadIdx.x & 63;
-    const int wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t NW = (int64_t)gridDim.x * kDecodeWaves;
-    const int64_t w = (int64_t)blockIdx.x * kDecodeWaves + wave_in_wg;
-    const int Hkv = a.num_kv_heads, NS = a.num_seqs;
-
-    __shared__ __align__(16) unsigned char q_lds[QL ? kDecodeWaves * S::QBYTES : 16];
-    extern __shared__ int lctx[];  // clamped context length of every sequence
-
-    // All cursor moves read context lengths from LDS, so inside the stream the only global
-    // loads are the ring's K/V loads and one block-table entry per step, a fixed count per
-    // step that keeps every wait on the ring exact.
-    for (int i = threadIdx.x; i < NS; i += kDecodeThreads) lctx[i] = seq_ctx(a, i);
-    __syncthreads();
-
-    // Chunk size: one chunk of ceil(U / NW) units per wave (at least kMinChunkBlocks), or the
-    // caller's chunk size with chunks dealt round-robin to the waves.  Workgroups are dealt to
-    // the 8 XCDs round-robin; the wave's first chunk is chosen so that chunk k runs on XCD
-    // k mod 8, which gives every XCD the same mix of sequences, kv heads and block ranges (with
-    // 4 consecutive chunks per workgroup, an XCD would see a fixed part of every run).
-    const int64_t first = (gridDim.x & 7) == 0
-                              ? 8 * kDecodeWaves * (int64_t)(blockIdx.x >> 3) + 8 * wave_in_wg + (blockIdx.x & 7)
-                              : w;
-    // chunk_blocks < 0: one chunk per run.  The host picks it when every run fits in one
-    // minimum chunk, so no run is split, nothing is merged and the merge launch is skipped
-    // (small batches, where a launch costs more than the work).  Chunk k is then run k.
-    constexpr bool per_run = PER_RUN;
-    ChunkMap cm{};
-    const Plan pl = per_run ? Plan{0, Pos{NS, 0, 0, 0}} : plan_wave(a, lctx, lane, [&](int64_t U) {
-        cm.C = a.chunk_blocks > 0 ? (int64_t)a.chunk_blocks : max((U + NW - 1) / NW, (int64_t)kMinChunkBlocks);
-        return cm.start(first);
-    });
-    const int64_t U = pl.U;
-    const int64_t nchunks =
-        per_run ? (int64_t)NS * Hkv : (U > 0 ? min(cm.of_unit(U - 1) + 1, a.max_chunks) : 0);
-
-    const unsigned char* kpool = static_cast<const unsigned char*>(a.k_pool);
-    const unsigned char* vpool = static_cast<const unsigned char*>(a.v_pool);
-    // A block of B = 16 << ub tokens is 1 << ub units.  Unit `sub` of a block: its K slices are
-    // 1 KiB pieces at sub * 1 KiB + c * (B * 64) of the block's tile, its V loads the
-    // sub-th run of TILE bytes (the pool layout of include/pagedattn.h).
-    // An 8-token block is one unit whose upper 8 tokens are empty: lanes 32..63 of its K loads
-    // and its V loads past the block's bytes fall outside the window and read nothing.
-    const int ub = a.block_size > kUnitTokens ? 1 : 0;
-    const int ush = unit_shift(a.block_size);
-    const int btile = a.block_size * D * S::EB;  // bytes of one (block, kv head) tile
-    const int vwin = btile < S::TILE ? btile : S::TILE;
-    const int kvoff = a.block_size < kUnitTokens && lane >= 32 ? 0x40000000 : lane * 16;
-    const int kstride = a.block_size * 64;
-    const int64_t block_stride = (int64_t)Hkv * btile;
-    const int32_t* tables = a.block_tables;
-    const int mbps = a.max_blocks_per_seq;
-
-    if constexpr (per_run) {  // the zero rows of empty sequences, before (and apart from) the stream
-        for (int64_t k = first; k < nchunks; k += NW) {
-            const int s = (int)(k / Hkv), g = (int)(k % Hkv);
-            if (lctx[s] != 0) continue;
-#pragma unroll
-            for (int h = 0; h < G; h++) {
-                const int64_t row = (int64_t)s * a.num_heads + (int64_t)g * G + h;
-#pragma unroll
-                for (int cg = 0; cg < S::CG; cg++) {
-                    if constexpr (QT == kBF16)
-                        static_cast<uint16_t*>(a.out)[row * D + cg * 64 + lane] = 0;
-                    else
-                        static_cast<float*>(a.out)[row * D + cg * 64 + lane] = 0.0f;
-                }
-            }
-        }
-    }
-
-    for (int64_t k = first; k < nchunks; k += NW) {
-        int n;           // units of this chunk
-        Pos p0;          // its first unit
-        int64_t u_end;   // list index one past its last unit
-        if constexpr (per_run) {
-            p0 = Pos{(int)(k / Hkv), (int)(k % Hkv), 0, 0};
-            n = __builtin_amdgcn_readfirstlane(nunits(lctx[p0.s], ush));  // uniform: keeps loop control scalar
-            u_end = n;
-            if (n == 0) {  // empty sequence: its zero rows were written above
-                continue;
-            }
-        } else {
-            n = (int)min(cm.size(k), U - cm.start(k));  // >= 1
-            p0 = k == first ? pl.p : plan_wave(a, lctx, lane, [&](int64_t) { return cm.start(k); }).p;
-            u_end = cm.start(k) + n;
-        }
-        if (a.new_key != nullptr) append_chunk_tokens<QT, KT, D>(a, lctx, p0, u_end, lane);
-
-        // table cursor: the block whose table entry is fetched next (it stops at the chunk's
-        // last block, whose entry then feeds the fill-in loads past the end)
-        Cursor tc = cursor_at(p0, lctx, ush);
-        int tcount = 0;
-        auto fetch_entry = [&](int& e, int& nv, int& g, int& sub) {
-            e = tables[(int64_t)tc.s * mbps + (tc.j >> ub)];
-            nv = min(1 << ush, tc.ctx - (tc.j << ush));
-            g = tc.g;
-            sub = tc.j & ub;
-            if (tcount + 1 < n) {
-                cursor_next(tc, lctx, NS, Hkv);
-                ++tcount;
-            }
-        };
-        // compute cursor: the block attended next, with its piece's bookkeeping
-        Cursor cc = cursor_at(p0, lctx, ush);
-        int piece_j0 = cc.j;
-
-        // entry ring: physical id, valid tokens, kv head and unit of the block, for units
-        // t .. t+NST-1
-        int ent[NST], ent_nv[NST], ent_g[NST], ent_sub[NST];
-#pragma unroll
-        for (int i = 0; i < NST; i++) fetch_entry(ent[i], ent_nv[i], ent_g[i], ent_sub[i]);
-
-        auto query_row = [&](const Cursor& c) {
-            return static_cast<const unsigned char*>(a.query) + ((int64_t)c.s * a.num_heads + (int64_t)c.g * G) * D * S::QB;
-        };
-        QRegs<QT, KT, D, G> qr;
-        const int q_off = wave_in_wg * S::QBYTES;
-        auto load_query = [&](const Cursor& c) {
-            if constexpr (QL) {
-#pragma unroll
-                for (int off = 0; off < S::QBYTES; off += 1024)
-                    if (off + lane * 16 < S::QBYTES)
-                        *reinterpret_cast<uint4*>(q_lds + q_off + off + lane * 16) = load16(query_row(c) + off + lane * 16);
-            } else {
-                load_q<QT, KT, D, G>(qr, query_row(c), lane & 3);
-            }
-        };
-        load_query(cc);
-        float c2 = a.scale_log2 * (kIsFp8<KT> ? a.k_scale[cc.g] : 1.0f);
-
-        Acc<QT, KT, D, G> st;
-        auto reset = [&]() {
-#pragma unroll
-            for (int h = 0; h < G; h++) {
-                st.m[h] = -FLT_MAX;
-                st.l[h] = 0.0f;
-#pragma unroll
-                for (int cg = 0; cg < S::CG; cg++) st.o[cg][h] = 0.0f;
-            }
-        };
-        reset();
-
-        // ---- end of a piece: fold the 8 token-pair lane groups of l, then write the row (a
-        // run covered whole) or the partial result ----
-        auto finish_piece = [&]() {
-#pragma unroll
-            for (int h = 0; h < G; h++) {
-                float x = st.l[h];
-                x += dpp_f32<kDppRowRor8>(x);
-                x += swizzle_xor16(x);
-                x += __shfl_xor(x, 32, 64);
-                st.l[h] = x;
-            }
-            const int64_t run = (int64_t)cc.s * Hkv + cc.g;
-            const bool first = piece_j0 == 0, whole = first && cc.j == cc.nbs - 1;
-            if (first && lane == 0 && !per_run) {
-                // every run with blocks is entered at its block 0 by exactly one wave, which
-                // records the chunk range covering it for the merge
-                const int64_t k_last = cm.of_unit(cc.run_start + cc.nbs - 1);
-                a.run_info[2 * run] = (int32_t)k;
-                a.run_info[2 * run + 1] = (int32_t)(k_last - k + 1);
-            }
-            const int64_t piece = run + k;
-            if (whole) {
-                const float vs = kIsFp8<KT> ? a.v_scale[cc.g] : 1.0f;
-#pragma unroll
-                for (int h = 0; h < G; h++) {
-                    const float f = st.l[h] > 0.0f ? vs / st.l[h] : 0.0f;
-                    const int64_t row = (int64_t)cc.s * a.num_heads + (int64_t)cc.g * G + h;
-#pragma unroll
-                    for (int cg = 0; cg < S::CG; cg++) {
-                        const float v = st.o[cg][h] * f;
-                        if constexpr (QT == kBF16)
-                            static_cast<uint16_t*>(a.out)[row * D + cg * 64 + lane] = f32_to_bf16_bits(v);
-                        else
-                            static_cast<float*>(a.out)[row * D + cg * 64 + lane] = v;
-                    }
-                }
-            } else if (piece < a.max_pieces) {
-#pragma unroll
-                for (int h = 0; h < G; h++) {
-                    const float f = st.l[h] > 0.0f ? 1.0f / st.l[h] : 0.0f;
-                    float* op = a.o_part + (piece * G + h) * D;
-#pragma unroll
-                    for (int cg = 0; cg < S::CG; cg++) op[cg * 64 + lane] = st.o[cg][h] * f;
-                    if (lane == 0) {
-                        a.ml_part[(piece * G + h) * 2] = st.m[h];
-                        a.ml_part[(piece * G + h) * 2 + 1] = st.l[h];
-                    }
-                }
-            }
-        };
-
-        // ---- the stream: step t issues block t into ring slot t % NST (blocks past the end
-        // re-read the chunk's last block and are never attended), refills the entry ring with
-        // block t + NST, and attends block t - (NST - 1) ----
-        uint4 kb[NST][S::NCH], vb[NST][S::NCH];
-        int kv_nv[NST];
-        for (int t0 = 0; t0 < n + NST - 1; t0 += NST) {
-#pragma unroll
-            for (int i = 0; i < NST; i++) {
-                const int t = t0 + i;
-                {
-                    // A step past the chunk's end, or a block id outside the pool, loads through
-                    // an empty buffer window: the loads return zeros without touching memory,
-                    // and the instruction stream (hence every wait count) stays the same.
-                    int phys = __builtin_amdgcn_readfirstlane(ent[i]);
-                    const bool bad = phys < 0 || (int64_t)phys >= a.num_blocks;
-                    phys = bad ? 0 : phys;
-                    kv_nv[i] = bad ? 0 : ent_nv[i];
-                    const bool none = bad || t >= n;
-                    const int sub = ent_sub[i];
-                    const int64_t off = (int64_t)phys * block_stride + (int64_t)ent_g[i] * btile;
-                    const TileWindow kw(kpool + off + sub * 1024, none ? 0 : btile - sub * 1024);
-                    const TileWindow vw(vpool + off + sub * S::TILE, none ? 0 : vwin);
-#pragma unroll
-                    for (int c = 0; c < S::NCH; c++) kb[i][c] = kw.load_stream(kvoff, c * kstride);
-#pragma unroll
-                    for (int c = 0; c < S::NCH; c++) vb[i][c] = vw.load_stream(lane * 16 + c * 1024);
-                }
-                fetch_entry(ent[i], ent_nv[i], ent_g[i], ent_sub[i]);
-
-                const int ta = t - (NST - 1);
-                if (ta >= 0 && ta < n) {
-                    const int j = (i + 1) % NST;  // the slot issued NST-1 steps ago
-                    if (ta > 0 && cc.j == 0) {       // a new run: start its piece
-                        load_query(cc);
-                        c2 = a.scale_log2 * (kIsFp8<KT> ? a.k_scale[cc.g] : 1.0f);
-                        reset();
-                        piece_j0 = 0;
-                    }
-                    if constexpr (QL) {
-                        const QLds qo{q_lds, opaque(q_off)};
-                        attend_block<QT, KT, D, G>(st, qo, kb[j], vb[j], kv_nv[j], c2, lane);
-                    } else {
-                        attend_block<QT, KT, D, G>(st, qr, kb[j], vb[j], kv_nv[j], c2, lane);
-                    }
-                    if (cc.j == cc.nbs - 1 || ta == n - 1) finish_piece();
-                    if (ta < n - 1) cursor_next(cc, lctx, NS, Hkv);
-                }
-            }
-        }
-    }
-}
 
 // Merge the pieces of one run (sequence s, kv head g), one wave per run: output row h =
 // sum_p w_p o_p / sum_p w_p with w_p = l_p * 2^(m_p - M), M = max_p m_p (flash-decoding's
@@ -887,13 +113,16 @@ template <int QT, int KT, int D, int G>
 hipError_t launch_phase_t(int phase, const DecodeArgs& a, hipStream_t stream)
 {
     if ((phase & 1) && a.grid_workgroups > 0) {
-        if (a.chunk_blocks < 0)
-            hipLaunchKernelGGL((decode_stream_kernel<QT, KT, D, G, true>), dim3((unsigned)a.grid_workgroups),
-                               dim3(kDecodeThreads), (size_t)a.num_seqs * sizeof(int), stream, a);
+        const dim3 grid((unsigned)a.grid_workgroups), block(kDecodeThreads);
+        const size_t lds = (size_t)a.num_seqs * sizeof(int);
+        hipError_t e = hipSuccess;
+        if (a.new_key != nullptr)
+            e = launch_decode_stream_fused(QT, KT, D, G, a, stream);
+        else if (a.chunk_blocks < 0)
+            hipLaunchKernelGGL((decode_stream_kernel<QT, KT, D, G, true, false>), grid, block, lds, stream, a);
         else
-            hipLaunchKernelGGL((decode_stream_kernel<QT, KT, D, G, false>), dim3((unsigned)a.grid_workgroups),
-                               dim3(kDecodeThreads), (size_t)a.num_seqs * sizeof(int), stream, a);
-        const hipError_t e = hipGetLastError();
+            hipLaunchKernelGGL((decode_stream_kernel<QT, KT, D, G, false, false>), grid, block, lds, stream, a);
+        if (e == hipSuccess) e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if ((phase & 2) && a.chunk_blocks >= 0) {  // one chunk per run: nothing to merge

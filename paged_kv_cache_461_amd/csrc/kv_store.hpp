@@ -1,8 +1,8 @@
 // kv_store.hpp -- store one 16-byte piece of a new token's K or V row into its pool slot.
 //
-// Shared by the append kernel and by the decode kernel's fused append, so both write the same
-// bytes.  Each decode step stores the new token's K/V in the cache (page 1, section 1, the
-// prefill/decode diagram) at its slot, the physical block from the sequence's block table and
+// The append kernel stores with store_kv_piece; the decode kernel's fused append encodes with
+// encode_elem, so both write the same bytes.  Each decode step stores the new token's K/V in
+// the cache (page 1, section 1, the prefill/decode diagram) at its slot, the physical block from the sequence's block table and
 // the offset inside it (page 1, section 4).  Layouts are those of include/pagedattn.h: a K
 // piece lands contiguously inside one 64-byte channel slice of the (block, kv head) tile; a V
 // piece is spread over its channels' token groups, so V is written with element-sized stores
@@ -15,6 +15,29 @@
 #include "pa_device.hpp"
 
 namespace pa {
+
+// Element i of a 16-byte source piece in the cache's encoding (the low EC bytes of the result):
+// the same bits for the same dtype; for an fp8 cache, x / scale in binary32 (round to nearest
+// even) converted with saturation.
+template <int ST, int CT>
+__device__ __forceinline__ uint32_t encode_elem(const uint32_t (&words)[4], int i, float scale)
+{
+    constexpr int ES = DtypeBytes<ST>::value;
+    if constexpr (ST == CT) {
+        if constexpr (ES == 4)
+            return words[i];
+        else
+            return (words[i / 2] >> (16 * (i % 2))) & 0xFFFFu;
+    } else {
+        static_assert(kIsFp8<CT>, "conversions go to fp8 only");
+        float x;
+        if constexpr (ST == kBF16)
+            x = bf16_bits_to_f32((words[i / 2] >> (16 * (i % 2))) & 0xFFFFu);
+        else
+            x = as_float(words[i]);
+        return f32_to_fp8<CT>(__fdiv_rn(x, scale));
+    }
+}
 
 // src: the piece's 16 source bytes (source elements d0 .. d0 + N - 1 of the row).
 // pool: the K or V pool (kv = 0 or 1); tile: element offset of the (block, kv head) tile;
@@ -50,14 +73,7 @@ __device__ __forceinline__ void store_kv_piece(const uint4 raw, unsigned char* p
         static_assert(kIsFp8<CT>, "conversions go to fp8 only");
         uint32_t codes[N];
 #pragma unroll
-        for (int i = 0; i < N; i++) {
-            float x;
-            if constexpr (ST == kBF16)
-                x = bf16_bits_to_f32((words[i / 2] >> (16 * (i % 2))) & 0xFFFFu);
-            else
-                x = as_float(words[i]);
-            codes[i] = f32_to_fp8<CT>(__fdiv_rn(x, scale));
-        }
+        for (int i = 0; i < N; i++) codes[i] = encode_elem<ST, CT>(words, i, scale);
         if (kv == 0) {
             unsigned char* dst = pool + slice + (int64_t)o * W + d0 % W;
             if constexpr (N == 8) {

@@ -104,6 +104,10 @@ int decode_waves_per_simd(int q_dtype, int cache_dtype, int head_dim, int gqa);
 hipError_t launch_decode(int phase, int q_dtype, int cache_dtype, int head_dim, int gqa,
                          const DecodeArgs& a, hipStream_t stream);
 
+// The streaming kernel's fused-append instances (a.new_key set), one launch.
+hipError_t launch_decode_stream_fused(int q_dtype, int cache_dtype, int head_dim, int gqa, const DecodeArgs& a,
+                                      hipStream_t stream);
+
 // grid = num_seqs * num_kv_heads * row_blocks * num_splits workgroups.
 hipError_t launch_prefill(int cache_dtype, int head_dim, int gqa, const PrefillArgs& a, int64_t grid,
                           hipStream_t stream);

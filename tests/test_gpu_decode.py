@@ -304,8 +304,10 @@ def _fused(db, k_pool, v_pool, partition_size=0):
     (W.BF16, 0, 8, False), (W.F32, 16, 8, True)])
 def test_fused_append_equals_separate_calls(cache, P, B, short):
     """pa_paged_attention_decode_append writes the same pool bytes as pa_kv_cache_write and
-    returns the same output bits as the decode that follows it; both match the oracle.  short:
-    contexts <= 128, so the automatic split is one chunk per (sequence, kv head)."""
+    returns the same output bits as the decode that follows it; both match the oracle.  The
+    contexts put the new token alone in a block (1, 17), in a block's last slot (16) and
+    mid-block.  short: contexts <= 128, so the automatic split is one chunk per (sequence, kv
+    head)."""
     q = W.F32 if cache == W.F32 else W.BF16
     ctx = [1, 16, 17, 40, 100, 127, 128] if short else [1, 16, 17, 40, 333, 1000, 2048]
     b = W.build_batch(ctx, num_heads=16, num_kv_heads=4, head_dim=128, q_dtype=q, cache_dtype=cache, seed=21,
