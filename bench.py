@@ -60,9 +60,9 @@ def parse_args():
                    choices=["none", "fp8_chunked_prefill", "fp8_e5m2_chunked_prefill", "llama3_8b_decode",
                             "long_context", "mixed_continuous_batch"],
                    help="second workload measured in the same run and reported under extra_step")
-    p.add_argument("--separate-append", action="store_true",
-                   help="append every row with pa_kv_cache_write before the decode call; by default the decode "
-                        "rows append their new token inside the decode call (pa_paged_attention_decode_append)")
+    p.add_argument("--fused-append", action="store_true",
+                   help="decode rows append their new token inside the decode call (pa_paged_attention_decode_append) "
+                        "instead of pa_kv_cache_write before it")
     p.add_argument("--graph", action="store_true",
                    help="also replay the step from HIP graphs and report it under graph_step")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -134,10 +134,10 @@ def source_digest(kernel="decode"):
     return h.hexdigest()[:16]
 
 
-def traffic_key(batch, fused=True):
-    """Counter records are kept per workload, per append form (the decode kernel with the fused
-    append, or alone after pa_kv_cache_write) and per block size when it is not 16."""
-    key = batch.name if fused else "%s/separate" % batch.name
+def traffic_key(batch, fused=False):
+    """Counter records are kept per workload, per append form (the decode kernel alone after
+    pa_kv_cache_write, or with the fused append) and per block size when it is not 16."""
+    key = "%s/fused" % batch.name if fused else batch.name
     return key if batch.block_size == 16 else "%s/b%d" % (key, batch.block_size)
 
 
@@ -465,7 +465,7 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     batch = make_batch(args.workload, args.block_size)
-    fused = not args.separate_append
+    fused = args.fused_append
     res, stream = measure(batch, dev, args.layers, args.steps, args.warmup, args.partition_size, fused, args.graph)
     if args.extra_workload != "none" and args.extra_workload != args.workload:
         # The rest of the hot path in the same run: the fp8 cache (in-kernel dequant) and the

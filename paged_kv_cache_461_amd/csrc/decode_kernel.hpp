@@ -773,8 +773,11 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) voi
                     phys = bad ? 0 : phys;
                     kv_nv[i] = bad ? 0 : ent_nv[i];
                     const bool none = bad || t >= n;
-                    const int sub = ent_sub[i];
-                    const int64_t off = (int64_t)phys * block_stride + (int64_t)ent_g[i] * btile;
+                    // kv head and unit are wave-uniform; saying so keeps the buffer descriptors
+                    // in SGPRs (otherwise every load is wrapped in a readfirstlane loop)
+                    const int sub = __builtin_amdgcn_readfirstlane(ent_sub[i]);
+                    const int gu = __builtin_amdgcn_readfirstlane(ent_g[i]);
+                    const int64_t off = (int64_t)phys * block_stride + (int64_t)gu * btile;
                     kv_koff[i] = off + sub * 1024;
                     kv_voff[i] = off + sub * S::TILE;
                     const TileWindow kw(kpool + off + sub * 1024, none ? 0 : btile - sub * 1024);
