@@ -284,6 +284,11 @@ def measure(batch, dev, layers, steps, warmup, partition_size=0, fused=False, gr
                                             num_kv_heads=Hkv, scale=batch.scale, block_size=B, k_scale=ks,
                                             v_scale=vs, workspace=pf_ws, stream=cur[0])
 
+    # sequences sharing leading blocks: the decode call gets the shared-block hint (cached loads
+    # for those blocks), as a prefix cache's host side would pass it
+    counts = batch.shared_block_counts()[Sp:]
+    shared = torch.from_numpy(counts).to(dev) if counts.any() and not fused else None
+
     def decode(r, phase=3):
         kp, vp, (nk, nv, _), q, ks, vs = pools[r % len(pools)]
         common = dict(max_context_len=dec_max_ctx, num_kv_heads=Hkv, scale=batch.scale, block_size=B, k_scale=ks,
@@ -292,7 +297,8 @@ def measure(batch, dev, layers, steps, warmup, partition_size=0, fused=False, gr
             ops.paged_attention_decode_append(outs[r % len(pools)][Rp:], q[Rp:], nk[Rp:].view(Sd, Hkv, D),
                                               nv[Rp:].view(Sd, Hkv, D), kp, vp, tables[Sp:], ctx[Sp:], **common)
         else:
-            ops.paged_attention_decode(outs[r % len(pools)][Rp:], q[Rp:], kp, vp, tables[Sp:], ctx[Sp:], **common)
+            ops.paged_attention_decode(outs[r % len(pools)][Rp:], q[Rp:], kp, vp, tables[Sp:], ctx[Sp:],
+                                       shared_blocks=shared, **common)
 
     def step(i):
         if Rw:
@@ -403,6 +409,7 @@ def measure(batch, dev, layers, steps, warmup, partition_size=0, fused=False, gr
             "num_blocks": batch.num_blocks, "layers_cycled": layers,
             "partition_size": "auto (equal chunks per wave)" if P == 0 else P,
             "append": "fused into the decode call" if fused and Sd else "pa_kv_cache_write",
+            "shared_block_hint": shared is not None,
         },
         "frac_of_hbm_peak": round(value * 1e3 / HBM_PEAK_GBS, 4),
         "seqs_per_s_per_layer": round(S / (ms_per_step * 1e-3), 1),

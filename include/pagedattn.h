@@ -225,6 +225,31 @@ int32_t pa_paged_attention_chunked_prefill(void* out, const void* query, int32_t
                                            size_t workspace_bytes, void* stream);
 
 /*
+ * pa_paged_attention_decode_phase with a hint about blocks shared between sequences (prefix
+ * sharing through identical leading block ids, as a prefix cache produces):
+ *   shared_blocks  device int32 [num_seqs], or NULL (= pa_paged_attention_decode_phase): block j
+ *                  of sequence s with j < shared_blocks[s] is read with the default cache policy,
+ *                  so the sequence's other readers of that block can find it cached; every other
+ *                  block is read once per call and streamed past the caches.  The hint changes
+ *                  only the loads' cache policy: the output is the same, bit for bit, for any
+ *                  values (an inaccurate hint only costs time).  The host knows the counts from
+ *                  its block refcounts (the leading blocks with refcount > 1).
+ * num_seqs must be <= 8192 when shared_blocks is given (the counts are staged in LDS beside the
+ * context lengths).  Other arguments, errors and the workspace as for
+ * pa_paged_attention_decode_phase.
+ */
+int32_t pa_paged_attention_decode_shared(int32_t phase, void* out, const void* query, int32_t q_dtype,
+                                         const void* k_pool, const void* v_pool, int64_t num_blocks,
+                                         int32_t cache_dtype, const int32_t* block_tables,
+                                         int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                         const int32_t* shared_blocks, int32_t max_context_len,
+                                         int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t block_size, float scale,
+                                         const float* k_scale, const float* v_scale,
+                                         int32_t partition_size, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
+/*
  * Decode with the step's append fused in (one launch instead of pa_kv_cache_write followed by
  * pa_paged_attention_decode_phase).  Every sequence s with context_lens[s] >= 1 first stores its
  * new token -- new_key[s] and new_value[s] -- at position context_lens[s] - 1, i.e. slot

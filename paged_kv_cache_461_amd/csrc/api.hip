@@ -289,7 +289,8 @@ namespace {
 int32_t decode_call(int32_t phase, void* out, const void* query, int32_t q_dtype, const void* new_key,
                     const void* new_value, const void* k_pool, const void* v_pool, int64_t num_blocks,
                     int32_t cache_dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                    const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+                    const int32_t* context_lens, const int32_t* shared_blocks, int32_t max_context_len,
+                    int32_t num_seqs, int32_t num_heads,
                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale, const float* k_scale,
                     const float* v_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
                     void* stream)
@@ -304,6 +305,9 @@ int32_t decode_call(int32_t phase, void* out, const void* query, int32_t q_dtype
     if (num_seqs > pa::kMaxDecodeSeqs)
         return fail(PA_ERR_UNSUPPORTED, "num_seqs %d above %d (context lengths are staged in LDS)", num_seqs,
                     pa::kMaxDecodeSeqs);
+    if (shared_blocks && num_seqs > pa::kMaxDecodeSeqsShared)
+        return fail(PA_ERR_UNSUPPORTED, "num_seqs %d above %d with shared-block counts (staged in LDS beside the "
+                    "context lengths)", num_seqs, pa::kMaxDecodeSeqsShared);
     if ((int64_t)max_blocks_per_seq * block_size < max_context_len)
         return fail(PA_ERR_INVALID_ARG, "max_context_len %d exceeds the table capacity %d x %d", max_context_len,
                     max_blocks_per_seq, block_size);
@@ -346,6 +350,7 @@ int32_t decode_call(int32_t phase, void* out, const void* query, int32_t q_dtype
     a.block_tables = block_tables;
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.context_lens = context_lens;
+    a.shared_blocks = shared_blocks;
     a.max_context_len = max_context_len;
     a.num_seqs = num_seqs;
     a.num_heads = num_heads;
@@ -381,9 +386,24 @@ int32_t pa_paged_attention_decode_phase(int32_t phase, void* out, const void* qu
                                         size_t workspace_bytes, void* stream)
 {
     return decode_call(phase, out, query, q_dtype, nullptr, nullptr, k_pool, v_pool, num_blocks, cache_dtype,
-                       block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_heads,
+                       block_tables, max_blocks_per_seq, context_lens, nullptr, max_context_len, num_seqs, num_heads,
                        num_kv_heads, head_dim, block_size, scale, k_scale, v_scale, partition_size, workspace,
                        workspace_bytes, stream);
+}
+
+int32_t pa_paged_attention_decode_shared(int32_t phase, void* out, const void* query, int32_t q_dtype,
+                                         const void* k_pool, const void* v_pool, int64_t num_blocks,
+                                         int32_t cache_dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                         const int32_t* context_lens, const int32_t* shared_blocks,
+                                         int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+                                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                                         const float* k_scale, const float* v_scale, int32_t partition_size,
+                                         void* workspace, size_t workspace_bytes, void* stream)
+{
+    return decode_call(phase, out, query, q_dtype, nullptr, nullptr, k_pool, v_pool, num_blocks, cache_dtype,
+                       block_tables, max_blocks_per_seq, context_lens, shared_blocks, max_context_len, num_seqs,
+                       num_heads, num_kv_heads, head_dim, block_size, scale, k_scale, v_scale, partition_size,
+                       workspace, workspace_bytes, stream);
 }
 
 int32_t pa_paged_attention_decode_append(int32_t phase, void* out, const void* query, int32_t q_dtype,
@@ -399,7 +419,7 @@ int32_t pa_paged_attention_decode_append(int32_t phase, void* out, const void* q
         return fail(PA_ERR_INVALID_ARG, "null new_key / new_value");
     return decode_call(phase, out, query, q_dtype, num_seqs > 0 ? new_key : nullptr,
                        num_seqs > 0 ? new_value : nullptr, k_pool, v_pool, num_blocks, cache_dtype, block_tables,
-                       max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_heads, num_kv_heads,
+                       max_blocks_per_seq, context_lens, nullptr, max_context_len, num_seqs, num_heads, num_kv_heads,
                        head_dim, block_size, scale, k_scale, v_scale, partition_size, workspace, workspace_bytes,
                        stream);
 }

@@ -114,12 +114,14 @@ hipError_t launch_phase_t(int phase, const DecodeArgs& a, hipStream_t stream)
 {
     if ((phase & 1) && a.grid_workgroups > 0) {
         const dim3 grid((unsigned)a.grid_workgroups), block(kDecodeThreads);
-        const size_t lds = (size_t)a.num_seqs * sizeof(int);
+        const size_t lds = (size_t)a.num_seqs * sizeof(int) * (a.shared_blocks ? 2 : 1);
         hipError_t e = hipSuccess;
         if (a.new_key != nullptr)
             e = launch_decode_stream_fused(QT, KT, D, G, a, stream);
-        else if (a.chunk_blocks < 0)
+        else if (a.chunk_blocks < 0)  // short contexts: the shared-block hint is not used
             hipLaunchKernelGGL((decode_stream_kernel<QT, KT, D, G, true, false>), grid, block, lds, stream, a);
+        else if (a.shared_blocks != nullptr)
+            hipLaunchKernelGGL((decode_stream_kernel<QT, KT, D, G, false, false, true>), grid, block, lds, stream, a);
         else
             hipLaunchKernelGGL((decode_stream_kernel<QT, KT, D, G, false, false>), grid, block, lds, stream, a);
         if (e == hipSuccess) e = hipGetLastError();

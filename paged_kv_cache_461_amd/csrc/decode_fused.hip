@@ -10,7 +10,7 @@ template <int QT, int KT, int D, int G>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream)
 {
     const dim3 grid((unsigned)a.grid_workgroups), block(kDecodeThreads);
-    const size_t lds = (size_t)a.num_seqs * sizeof(int);
+    const size_t lds = (size_t)a.num_seqs * sizeof(int) * (a.shared_blocks ? 2 : 1);
     if (a.chunk_blocks < 0)
         hipLaunchKernelGGL((decode_stream_kernel<QT, KT, D, G, true, true>), grid, block, lds, stream, a);
     else

@@ -541,9 +541,10 @@ constexpr int stream_waves_per_simd()
     return stream_min_waves<KT, D, G>() > 2 ? stream_min_waves<KT, D, G>() : 2;
 }
 
-// PER_RUN: the one-chunk-per-run form (chunk_blocks < 0); FUSED: the fused append (new_key set).
-// Separate instances, so that their extra paths leave the plain balanced form's registers alone.
-template <int QT, int KT, int D, int G, bool PER_RUN, bool FUSED>
+// PER_RUN: the one-chunk-per-run form (chunk_blocks < 0); FUSED: the fused append (new_key set);
+// HINT: cached loads for the leading blocks a.shared_blocks marks as shared.  Separate instances,
+// so that their extra paths leave the plain balanced form's registers alone.
+template <int QT, int KT, int D, int G, bool PER_RUN, bool FUSED, bool HINT = false>
 __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) void decode_stream_kernel(
     const DecodeArgs a)
 {
@@ -564,6 +565,10 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) voi
     // loads are the ring's K/V loads and one block-table entry per step, a fixed count per
     // step that keeps every wait on the ring exact.
     for (int i = threadIdx.x; i < NS; i += kDecodeThreads) lctx[i] = seq_ctx(a, i);
+    // shared-block counts, when given, follow the context lengths
+    constexpr bool hint = HINT;
+    if (hint)
+        for (int i = threadIdx.x; i < NS; i += kDecodeThreads) lctx[NS + i] = a.shared_blocks[i];
     __syncthreads();
 
     // Chunk size: one chunk of ceil(U / NW) units per wave (at least kMinChunkBlocks), or the
@@ -643,11 +648,12 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) voi
         // last block, whose entry then feeds the fill-in loads past the end)
         Cursor tc = cursor_at(p0, lctx, ush);
         int tcount = 0;
-        auto fetch_entry = [&](int& e, int& nv, int& g, int& sub) {
+        auto fetch_entry = [&](int& e, int& nv, int& g, int& sub, int& cached) {
             e = tables[(int64_t)tc.s * mbps + (tc.j >> ub)];
             nv = min(1 << ush, tc.ctx - (tc.j << ush));
             g = tc.g;
             sub = tc.j & ub;
+            if constexpr (hint) cached = (tc.j >> ub) < lctx[NS + tc.s];
             if (tcount + 1 < n) {
                 cursor_next(tc, lctx, NS, Hkv);
                 ++tcount;
@@ -659,9 +665,9 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) voi
 
         // entry ring: physical id, valid tokens, kv head and unit of the block, for units
         // t .. t+NST-1
-        int ent[NST], ent_nv[NST], ent_g[NST], ent_sub[NST];
+        int ent[NST], ent_nv[NST], ent_g[NST], ent_sub[NST], ent_cached[NST] = {};
 #pragma unroll
-        for (int i = 0; i < NST; i++) fetch_entry(ent[i], ent_nv[i], ent_g[i], ent_sub[i]);
+        for (int i = 0; i < NST; i++) fetch_entry(ent[i], ent_nv[i], ent_g[i], ent_sub[i], ent_cached[i]);
 
         auto query_row = [&](const Cursor& c) {
             return static_cast<const unsigned char*>(a.query) + ((int64_t)c.s * a.num_heads + (int64_t)c.g * G) * D * S::QB;
@@ -782,12 +788,21 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) voi
                     kv_voff[i] = off + sub * S::TILE;
                     const TileWindow kw(kpool + off + sub * 1024, none ? 0 : btile - sub * 1024);
                     const TileWindow vw(vpool + off + sub * S::TILE, none ? 0 : vwin);
+                    // a block shared with other sequences keeps the default cache policy, so its
+                    // other readers find it cached; the rest are read once and streamed (nt)
+                    if (hint && __builtin_amdgcn_readfirstlane(ent_cached[i])) {
 #pragma unroll
-                    for (int c = 0; c < S::NCH; c++) kb[i][c] = kw.load_stream(kvoff, c * kstride);
+                        for (int c = 0; c < S::NCH; c++) kb[i][c] = kw.load_cached(kvoff, c * kstride);
 #pragma unroll
-                    for (int c = 0; c < S::NCH; c++) vb[i][c] = vw.load_stream(lane * 16 + c * 1024);
+                        for (int c = 0; c < S::NCH; c++) vb[i][c] = vw.load_cached(lane * 16 + c * 1024);
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < S::NCH; c++) kb[i][c] = kw.load_stream(kvoff, c * kstride);
+#pragma unroll
+                        for (int c = 0; c < S::NCH; c++) vb[i][c] = vw.load_stream(lane * 16 + c * 1024);
+                    }
                 }
-                fetch_entry(ent[i], ent_nv[i], ent_g[i], ent_sub[i]);
+                fetch_entry(ent[i], ent_nv[i], ent_g[i], ent_sub[i], ent_cached[i]);
 
                 const int ta = t - (NST - 1);
                 if (ta >= 0 && ta < n) {

@@ -206,6 +206,13 @@ struct TileWindow {
         const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, offset, soffset, kBufferNontemporal);
         return make_uint4(v.x, v.y, v.z, v.w);
     }
+    // the same load with the default cache policy: for bytes that other waves read again
+    // (blocks shared between sequences)
+    __device__ __forceinline__ uint4 load_cached(int offset, int soffset = 0) const
+    {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, offset, soffset, 0);
+        return make_uint4(v.x, v.y, v.z, v.w);
+    }
     static constexpr int kBufferNontemporal = 2;  // the cache-policy bit printed as "nt"
 };
 

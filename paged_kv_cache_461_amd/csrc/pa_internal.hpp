@@ -33,6 +33,7 @@ constexpr int kSimds = 1024;         // 256 CUs x 4 SIMDs
 constexpr int kStreamWavesMax = 3 * kSimds;  // largest persistent grid (3 waves per SIMD)
 constexpr int kMinChunkBlocks = 8;   // smallest automatic chunk, in (block, kv head) units
 constexpr int kMaxDecodeSeqs = 16384;  // context lengths of a call are staged in 64 KiB of LDS
+constexpr int kMaxDecodeSeqsShared = 8192;  // ... and the shared-block counts beside them
 
 struct DecodeArgs {
     void* out;
@@ -45,6 +46,8 @@ struct DecodeArgs {
     const int32_t* block_tables;
     int32_t max_blocks_per_seq;
     const int32_t* context_lens;
+    const int32_t* shared_blocks;  // [S] leading blocks of each sequence shared with other
+                                   // sequences (read with cached loads), or null
     int32_t max_context_len;  // context lengths are clamped to this bound
     int32_t num_seqs;
     int32_t num_heads;

@@ -35,7 +35,7 @@ EXPORTS = (
     "pa_paged_attention_decode", "pa_paged_attention_decode_phase", "pa_kv_bytes_per_token",
     "pa_pool_bytes", "pa_probe_tile_read", "pa_status_string", "pa_last_error",
     "pa_chunked_prefill_workspace_size", "pa_paged_attention_chunked_prefill", "pa_paged_attention_decode_append",
-    "pa_copy_blocks", "pa_bm_create", "pa_bm_destroy", "pa_bm_add_sequence", "pa_bm_append_token", "pa_bm_fork",
+    "pa_paged_attention_decode_shared", "pa_copy_blocks", "pa_bm_create", "pa_bm_destroy", "pa_bm_add_sequence", "pa_bm_append_token", "pa_bm_fork",
     "pa_bm_free_sequence", "pa_bm_block_table", "pa_bm_refcount", "pa_bm_get_stats",
 )
 
@@ -66,6 +66,8 @@ def library():
         lib.pa_paged_attention_decode.argtypes = dec
         lib.pa_paged_attention_decode_phase.restype = I32
         lib.pa_paged_attention_decode_phase.argtypes = [I32] + dec
+        lib.pa_paged_attention_decode_shared.restype = I32
+        lib.pa_paged_attention_decode_shared.argtypes = [I32] + dec[:10] + [P] + dec[10:]
         lib.pa_paged_attention_decode_append.restype = I32
         lib.pa_paged_attention_decode_append.argtypes = [I32, P, P, I32, P, P] + dec[3:]
         lib.pa_chunked_prefill_workspace_size.restype = I64
@@ -187,9 +189,11 @@ def decode_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_context_le
 
 def paged_attention_decode(out, query, k_pool, v_pool, block_tables, context_lens, *, max_context_len,
                            num_kv_heads, scale, block_size=16, k_scale=None, v_scale=None, partition_size=0,
-                           workspace=None, phase=3, stream=None):
+                           workspace=None, phase=3, stream=None, shared_blocks=None):
     """One query row per sequence over its paged context (pa_paged_attention_decode[_phase]).
-    query/out: [S][Hq][D]; block_tables: int32 [S][max_blocks]; context_lens: int32 [S]."""
+    query/out: [S][Hq][D]; block_tables: int32 [S][max_blocks]; context_lens: int32 [S].
+    shared_blocks: optional int32 [S], the leading blocks of each sequence that other sequences
+    share (pa_paged_attention_decode_shared: those are read with cached loads)."""
     for n, t in (("out", out), ("query", query), ("k_pool", k_pool), ("v_pool", v_pool)):
         _dev(n, t)
     _dev("block_tables", block_tables, torch.int32)
@@ -204,6 +208,16 @@ def paged_attention_decode(out, query, k_pool, v_pool, block_tables, context_len
         raise ValueError("block_tables must be [num_seqs][max_blocks] and context_lens [num_seqs]")
     nb = num_pool_blocks(k_pool, num_kv_heads, D, block_size)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if shared_blocks is not None:
+        _dev("shared_blocks", shared_blocks, torch.int32)
+        if shared_blocks.numel() != S:
+            raise ValueError("shared_blocks must be [num_seqs]")
+        _check(library().pa_paged_attention_decode_shared(
+            int(phase), _ptr(out), _ptr(query), dtype_code(query), _ptr(k_pool), _ptr(v_pool), nb,
+            dtype_code(k_pool), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), _ptr(shared_blocks),
+            int(max_context_len), S, Hq, num_kv_heads, D, block_size, float(scale), _ptr(k_scale), _ptr(v_scale),
+            int(partition_size), _ptr(workspace), ws_bytes, _stream(stream)))
+        return out
     _check(library().pa_paged_attention_decode_phase(
         int(phase), _ptr(out), _ptr(query), dtype_code(query), _ptr(k_pool), _ptr(v_pool), nb, dtype_code(k_pool),
         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), int(max_context_len), S, Hq, num_kv_heads, D,

@@ -307,6 +307,21 @@ class PagedBatch:
             b += 2 * 4 * self.num_kv_heads
         return int(b)
 
+    def shared_block_counts(self) -> np.ndarray:
+        """int32 [S]: the leading blocks of each sequence whose refcount is above 1 -- the blocks
+        it shares with other sequences, as a prefix cache's host side knows them (the hint that
+        pa_paged_attention_decode_shared takes)."""
+        B = self.block_size
+        counts = np.zeros(self.num_seqs, np.int32)
+        if self.refcount.size == 0:
+            return counts
+        for s in range(self.num_seqs):
+            nb = -(-int(self.context_lens[s]) // B)
+            row = self.block_tables[s, :nb]
+            shared = self.refcount[row] > 1
+            counts[s] = nb if shared.all() else int(np.argmin(shared))
+        return counts
+
     def write_bytes(self) -> int:
         """Algorithmic bytes of appending this step's new rows: read K,V rows in the source
         dtype, write them in the cache dtype, read the slot ids."""

@@ -102,6 +102,34 @@ def test_decode_rejects_before_launch(lib, kw, status):
     assert lib.pa_last_error() != b""
 
 
+def _decode_shared(lib, shared=FAKE, **kw):
+    a = dict(phase=3, out=FAKE, query=FAKE, q_dtype=BF16, k_pool=FAKE, v_pool=FAKE, num_blocks=100,
+             cache_dtype=BF16, block_tables=FAKE, mbps=256, context_lens=FAKE, max_ctx=4096, S=64, Hq=32, Hkv=8,
+             D=128, B=16, scale=0.088, k_scale=None, v_scale=None, P=0, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.pa_paged_attention_decode_shared(
+        a["phase"], a["out"], a["query"], a["q_dtype"], a["k_pool"], a["v_pool"], a["num_blocks"], a["cache_dtype"],
+        a["block_tables"], a["mbps"], a["context_lens"], shared, a["max_ctx"], a["S"], a["Hq"], a["Hkv"], a["D"],
+        a["B"], a["scale"], a["k_scale"], a["v_scale"], a["P"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(S=8193), ops.PA_ERR_UNSUPPORTED),                  # counts staged beside the lengths
+    (dict(shared=None, S=8193), ops.PA_ERR_WORKSPACE),        # no counts: the plain limit applies
+    (dict(out=None), ops.PA_ERR_INVALID_ARG),
+    (dict(D=96), ops.PA_ERR_UNSUPPORTED),
+    (dict(ws=None, ws_bytes=0), ops.PA_ERR_WORKSPACE),
+])
+def test_decode_shared_rejects_before_launch(lib, kw, status):
+    """pa_paged_attention_decode_shared checks its arguments as the phase call does, plus the
+    smaller sequence limit that staging the shared-block counts in LDS imposes."""
+    assert _decode_shared(lib, **kw) == status
+
+
+def test_decode_shared_empty_batch_is_ok_without_launch(lib):
+    assert _decode_shared(lib, S=0, out=None, query=None, shared=None) == ops.PA_OK
+
+
 def test_decode_accepts_32_token_blocks(lib):
     """Block size 32 passes the host checks (with a table long enough for it); the call then
     stops at the workspace check, before any launch."""

@@ -410,3 +410,30 @@ def test_merge_more_than_64_pieces_per_run():
     got = db.decode(kp, vp, partition_size=16)
     assert_close(b, out_to_f64(got), oracle_attention(b, kp_h, vp_h))
     assert torch.equal(got, _two_phase(db, kp, vp, 16))
+
+
+@pytest.mark.parametrize("cache,B", [(W.BF16, 16), (W.FP8_E4M3, 16), (W.BF16, 32), (W.F32, 8)])
+def test_shared_block_hint_changes_nothing_but_cache_policy(cache, B):
+    """Sequences sharing a 256-token prefix through identical block ids: the decode with the
+    shared-block hint (cached loads for the shared leading blocks) gives the same bits as without
+    it, for the true counts and for wrong ones (all blocks, none, negative), and matches the
+    oracle."""
+    q = W.F32 if cache == W.F32 else W.BF16
+    ctx = [300, 900, 257, 2000, 1500, 700, 420, 64]
+    b = W.build_batch(ctx, num_heads=16, num_kv_heads=4, head_dim=128, q_dtype=q, cache_dtype=cache, seed=31,
+                      block_size=B, shared_prefix_len=256, sharing=[0, 1, 3, 4, 5, 6])
+    kp_h, vp_h = oracle_pool(b, include_new=True)
+    db = DeviceBatch(b)
+    kp, vp = to_dev(kp_h, b.cache_dtype), to_dev(vp_h, b.cache_dtype)
+    counts = b.shared_block_counts()
+    assert counts.max() == 256 // B and counts[2] == 0 and counts[7] == 0
+    base = db.decode(kp, vp)
+    assert_close(b, out_to_f64(base), oracle_attention(b, kp_h, vp_h))
+    ws = ops.decode_workspace(b.num_seqs, b.num_heads, b.num_kv_heads, b.head_dim, b.max_context_len, b.block_size)
+    for hint in (counts, np.full_like(counts, 1 << 20), np.zeros_like(counts), np.full_like(counts, -5)):
+        out = torch.empty_like(db.query)
+        ops.paged_attention_decode(out, db.query, kp, vp, db.tables, db.ctx, max_context_len=b.max_context_len,
+                                   num_kv_heads=b.num_kv_heads, scale=b.scale, block_size=b.block_size,
+                                   k_scale=db.k_scale, v_scale=db.v_scale, workspace=ws,
+                                   shared_blocks=torch.from_numpy(hint).cuda())
+        assert torch.equal(out.view(torch.uint8), base.view(torch.uint8)), hint[:4]

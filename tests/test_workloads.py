@@ -98,3 +98,11 @@ def test_bf16_rounding_is_nearest_even():
     x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 65504.0], np.float32)
     got = W.bf16_bits_to_f32(W.f32_to_bf16_bits(x))
     assert list(got) == [1.0, 1.0, 1.0 + 2 ** -6, -2.5, 65536.0]
+
+
+def test_shared_block_counts_follow_refcounts():
+    """The shared-block hint: sharing sequences report the prefix's blocks, the others none."""
+    b = W.build_batch([300, 900, 257, 2000], num_heads=8, num_kv_heads=2, head_dim=64, seed=4,
+                      shared_prefix_len=256, sharing=[0, 1, 3])
+    assert b.shared_block_counts().tolist() == [16, 16, 0, 16]
+    assert W.build_batch([40, 50], num_heads=8, num_kv_heads=2, head_dim=64).shared_block_counts().tolist() == [0, 0]
