@@ -198,7 +198,8 @@ def oracle_sampled_rows(batch, picks):
 
 def device_step(batch, db, k_pool, v_pool, partition_size=0):
     """The step as bench.py launches it: chunked prefill for the sequences with several rows
-    (they come first), decode for the rest, into one output tensor."""
+    (they come first), decode for the rest, into one output tensor; the decode gets the
+    shared-block hint when sequences share leading blocks."""
     ql = batch.query_lens
     Sp = int(np.argmax(ql == 1)) if (ql == 1).any() else len(ql)
     Rp = int(ql[:Sp].sum())
@@ -216,8 +217,10 @@ def device_step(batch, db, k_pool, v_pool, partition_size=0):
         dmax = int(b.context_lens[Sp:].max())
         ws = ops.decode_workspace(b.num_seqs - Sp, b.num_heads, b.num_kv_heads, b.head_dim, dmax, b.block_size,
                                   partition_size)
+        counts = b.shared_block_counts()[Sp:]
+        shared = torch.from_numpy(counts).cuda() if counts.any() else None
         ops.paged_attention_decode(out[Rp:], db.query[Rp:], k_pool, v_pool, db.tables[Sp:], db.ctx[Sp:],
                                    max_context_len=dmax, num_kv_heads=b.num_kv_heads, scale=b.scale,
                                    block_size=b.block_size, k_scale=db.k_scale, v_scale=db.v_scale,
-                                   partition_size=partition_size, workspace=ws)
+                                   partition_size=partition_size, workspace=ws, shared_blocks=shared)
     return out

@@ -60,10 +60,12 @@ def test_long_context_full_partition_sweep():
 
 
 def test_mixed_continuous_batch_full():
-    """256 log-normal contexts up to 32768, 64 sharing a 2048-token prefix (same physical blocks)."""
+    """256 log-normal contexts up to 32768, 64 sharing a 2048-token prefix (same physical blocks),
+    decoded with the shared-block hint as the benchmark runs it."""
     b = W.mixed_continuous_batch()
     seqs = set(sample_seqs(b))
     seqs.update(int(s) for s in b.sharing[:2])
+    assert b.shared_block_counts().max() == 2048 // b.block_size
     full_step_and_check(b, [(s, 0) for s in sorted(seqs)])
 
 
