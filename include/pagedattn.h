@@ -225,8 +225,9 @@ int32_t pa_paged_attention_chunked_prefill(void* out, const void* query, int32_t
                                            size_t workspace_bytes, void* stream);
 
 /*
- * pa_paged_attention_decode_phase with a hint about blocks shared between sequences (prefix
- * sharing through identical leading block ids, as a prefix cache produces):
+ * pa_paged_attention_decode_phase with a hint about blocks shared between sequences: sequences
+ * that share a prefix hold the same physical blocks in their tables (page 1, section 4; page 2,
+ * the PagedAttention section), so every sharer reads those blocks:
  *   shared_blocks  device int32 [num_seqs], or NULL (= pa_paged_attention_decode_phase): block j
  *                  of sequence s with j < shared_blocks[s] is read with the default cache policy,
  *                  so the sequence's other readers of that block can find it cached; every other
