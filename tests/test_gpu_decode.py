@@ -437,3 +437,22 @@ def test_shared_block_hint_changes_nothing_but_cache_policy(cache, B):
                                    k_scale=db.k_scale, v_scale=db.v_scale, workspace=ws,
                                    shared_blocks=torch.from_numpy(hint).cuda())
         assert torch.equal(out.view(torch.uint8), base.view(torch.uint8)), hint[:4]
+
+
+def test_shared_block_hint_short_contexts():
+    """Contexts of at most 128 tokens take the one-chunk-per-run form, which ignores the hint:
+    the same bits with and without it."""
+    b = W.build_batch([100, 120, 64, 128], num_heads=32, num_kv_heads=8, head_dim=128, q_dtype=W.BF16,
+                      cache_dtype=W.BF16, seed=41, shared_prefix_len=32, sharing=[0, 1, 3])
+    kp_h, vp_h = oracle_pool(b, include_new=True)
+    db = DeviceBatch(b)
+    kp, vp = to_dev(kp_h, b.cache_dtype), to_dev(vp_h, b.cache_dtype)
+    base = db.decode(kp, vp)
+    assert_close(b, out_to_f64(base), oracle_attention(b, kp_h, vp_h))
+    counts = b.shared_block_counts()
+    assert counts.tolist() == [2, 2, 0, 2]
+    out = torch.empty_like(db.query)
+    ops.paged_attention_decode(out, db.query, kp, vp, db.tables, db.ctx, max_context_len=b.max_context_len,
+                               num_kv_heads=b.num_kv_heads, scale=b.scale, block_size=b.block_size,
+                               shared_blocks=torch.from_numpy(counts).cuda())
+    assert torch.equal(out.view(torch.uint8), base.view(torch.uint8))
