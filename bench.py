@@ -170,14 +170,14 @@ def fill_pools(batch, layers, dev):
     pools = []
     for layer in range(layers):
         lb = dataclasses.replace(batch, layer=layer)
-        if batch.cache_dtype in W.FP8_DTYPES:
-            lb.k_scale, lb.v_scale = W.fp8_calibration_scales(batch.num_kv_heads, batch.head_dim, batch.seed, layer,
+        if batch.cache_dtype in W.QUANT_DTYPES:
+            lb.k_scale, lb.v_scale = W.quant_calibration_scales(batch.num_kv_heads, batch.head_dim, batch.seed, layer,
                                                               batch.src_dtype, cache_dtype=batch.cache_dtype,
                                                               granularity=batch.fp8_scale)
         ks = None if lb.k_scale is None else torch.from_numpy(lb.k_scale).to(dev)
         vs = None if lb.v_scale is None else torch.from_numpy(lb.v_scale).to(dev)
         # fp8 pools are zeroed as bytes, then typed (E5M2 pools must carry the float8_e5m2 type)
-        zdt = torch.uint8 if batch.cache_dtype in W.FP8_DTYPES else tdt
+        zdt = torch.uint8 if batch.cache_dtype in W.QUANT_DTYPES else tdt
         kp = torch.zeros(batch.pool_elems, dtype=zdt, device=dev).view(tdt)
         vp = torch.zeros(batch.pool_elems, dtype=zdt, device=dev).view(tdt)
         for k, v, slots in lb.history_chunks():

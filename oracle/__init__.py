@@ -7,8 +7,8 @@ product package.  The arithmetic lives in ``pa_oracle.c`` (plain C99, float64, c
 with gcc -O2, no fast-math); this module only builds it and marshals numpy arrays.
 
 Element types are passed as numpy arrays of their raw bits: fp32 as ``float32``, bf16 as
-``uint16`` and OCP fp8 E4M3 / E5M2 as ``uint8``.  Dtype codes: 0 fp32, 1 bf16, 2 fp8 e4m3,
-3 fp8 e5m2.
+``uint16``, OCP fp8 E4M3 / E5M2 and INT8 (two's complement) as ``uint8``.  Dtype codes: 0 fp32,
+1 bf16, 2 fp8 e4m3, 3 fp8 e5m2, 4 int8.
 
 Pins (tests/test_oracle_*.py check this module against what the pages and mathematics fix):
   * attention == torch scaled_dot_product_attention in float64 on the contiguous
@@ -22,6 +22,8 @@ Pins (tests/test_oracle_*.py check this module against what the pages and mathem
     round-to-nearest-even cast wherever that cast does not overflow, saturation to 448
     above it, and round trip on every finite code;
   * E5M2: the same three pins against torch.float8_e5m2 (saturation at 57344);
+  * INT8: encode == numpy's binary32 division then round-half-even (numpy.rint), saturated to
+    [-127, 127], over every bf16 pattern at several scales; decode == the int8 view of the byte;
   * KV bytes per token == 131072 for 32 layers x 8 kv heads x 128 x bf16.
 """
 from __future__ import annotations
@@ -33,8 +35,8 @@ import threading
 
 import numpy as np
 
-F32, BF16, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3
-_NP_OF = {F32: np.float32, BF16: np.uint16, FP8_E4M3: np.uint8, FP8_E5M2: np.uint8}
+F32, BF16, FP8_E4M3, FP8_E5M2, INT8 = 0, 1, 2, 3, 4
+_NP_OF = {F32: np.float32, BF16: np.uint16, FP8_E4M3: np.uint8, FP8_E5M2: np.uint8, INT8: np.uint8}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "pa_oracle.c")
@@ -84,6 +86,14 @@ def _bind(lib):
     lib.oracle_e5m2_encode_array.argtypes = [P, P, L]
     lib.oracle_e5m2_decode_array.restype = None
     lib.oracle_e5m2_decode_array.argtypes = [P, P, L]
+    lib.oracle_int8_to_double.restype = D
+    lib.oracle_int8_to_double.argtypes = [ctypes.c_uint8]
+    lib.oracle_int8_encode.restype = ctypes.c_uint8
+    lib.oracle_int8_encode.argtypes = [ctypes.c_float]
+    lib.oracle_int8_encode_array.restype = None
+    lib.oracle_int8_encode_array.argtypes = [P, P, L]
+    lib.oracle_int8_decode_array.restype = None
+    lib.oracle_int8_decode_array.argtypes = [P, P, L]
     lib.oracle_kv_bytes_per_token.restype = L
     lib.oracle_kv_bytes_per_token.argtypes = [I, I, I, I]
     return lib
@@ -159,6 +169,25 @@ def e5m2_encode(y) -> np.ndarray:
     y = np.ascontiguousarray(y, dtype=np.float32)
     out = np.empty(y.shape, dtype=np.uint8)
     lib.oracle_e5m2_encode_array(_ptr(y), _ptr(out), y.size)
+    return out
+
+
+def int8_to_float64(codes) -> np.ndarray:
+    """Integer value of each INT8 code byte (two's complement)."""
+    lib = _load()
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    lib.oracle_int8_decode_array(_ptr(c), _ptr(out), c.size)
+    return out
+
+
+def int8_encode(y) -> np.ndarray:
+    """Round binary32 values to INT8 code bytes (nearest integer, ties to even, saturating at
+    +-127, NaN -> 0)."""
+    lib = _load()
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.empty(y.shape, dtype=np.uint8)
+    lib.oracle_int8_encode_array(_ptr(y), _ptr(out), y.size)
     return out
 
 

@@ -18,7 +18,13 @@
  *   - the KV cache may be stored as 8-bit floats, e4m3 preferred over e5m2 (which can drift
  *     numerically on long sequences), with
  *     per-tensor or per-head scales                          (page 1, section 15; page 2,
- *     "quantisation"; page 3, section 2.4).
+ *     "quantisation"; page 3, section 2.4);
+ *   - or as 8-bit integers: a tuning step brings the KV cache from 16-bit floats down to INT8
+ *     (page 4, section 4.5, step 4; page 2, "quantisation", which names KV-cache quantisation
+ *     beside weight and activation quantisation).  The pages give no encoding; the reading
+ *     taken here is the plain symmetric one: one fp32 scale per (layer, kv head), the stored
+ *     code is the nearest integer (ties to even) to fl32(x / scale), saturated to [-127, 127]
+ *     (NaN stores 0), and the cached value is code * scale.
  * Each decode step produces the new token's K/V and stores it in the cache, and the new
  * query attends over all stored positions including that one (page 1, section 1, the
  * prefill/decode diagram).
@@ -44,7 +50,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8_E4M3 = 2, OR_FP8_E5M2 = 3 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8_E4M3 = 2, OR_FP8_E5M2 = 3, OR_INT8 = 4 };
 
 enum {
     OR_OK = 0,
@@ -61,6 +67,7 @@ static int elem_bytes(int dtype)
     case OR_BF16: return 2;
     case OR_FP8_E4M3: return 1;
     case OR_FP8_E5M2: return 1;
+    case OR_INT8: return 1;
     default: return 0;
     }
 }
@@ -187,7 +194,30 @@ uint8_t oracle_e5m2_encode(float y)
     return sign | (uint8_t)nearest_code(a, 0x7b, oracle_e5m2_to_double);
 }
 
+/* INT8 cache code: a two's-complement byte c; its value (before the scale) is the integer c. */
+double oracle_int8_to_double(uint8_t c) { return (double)(int8_t)c; }
+
+/* Nearest integer to a binary32 value, ties to the even integer, saturated to [-127, 127]
+ * (the symmetric range: +x and -x get opposite codes); NaN stores 0.  Written out: n is the
+ * integer part below y, r = y - n is exact (|y| < 127 has at most 24 significant bits), and
+ * r > 1/2, or r = 1/2 with n odd, rounds up. */
+uint8_t oracle_int8_encode(float y)
+{
+    if (isnan(y)) return 0;
+    if (y >= 127.0f) return 127;
+    if (y <= -127.0f) return (uint8_t)(int8_t)-127;
+    double a = (double)y;
+    double f = floor(a);
+    double r = a - f;
+    long n = (long)f;
+    if (r > 0.5 || (r == 0.5 && n % 2 != 0)) n += 1;
+    return (uint8_t)(int8_t)n;
+}
+
 static int is_fp8(int dtype) { return dtype == OR_FP8_E4M3 || dtype == OR_FP8_E5M2; }
+
+/* A quantised cache (fp8 or INT8): codes times a per-head scale. */
+static int is_quant(int dtype) { return is_fp8(dtype) || dtype == OR_INT8; }
 
 static double load_elem(const unsigned char* base, int64_t idx, int dtype)
 {
@@ -200,6 +230,7 @@ static double load_elem(const unsigned char* base, int64_t idx, int dtype)
     }
     case OR_FP8_E4M3: return oracle_e4m3_to_double(base[idx]);
     case OR_FP8_E5M2: return oracle_e5m2_to_double(base[idx]);
+    case OR_INT8: return oracle_int8_to_double(base[idx]);
     default: return NAN;
     }
 }
@@ -208,9 +239,9 @@ static double load_elem(const unsigned char* base, int64_t idx, int dtype)
 
 /* For every token i with slot_mapping[i] >= 0 the token goes to physical block
  * slot / block_size at offset slot % block_size, for every kv head and channel.  Same
- * source and cache dtype: the element's bits are copied.  fp32/bf16 source into an E4M3 (E5M2)
- * cache: the stored code is e4m3(fl32(x / scale[h])) (e5m2(...)) -- one IEEE binary32 division
- * by that head's scale, then the rounding above. */
+ * source and cache dtype: the element's bits are copied.  fp32/bf16 source into an E4M3 (E5M2,
+ * INT8) cache: the stored code is e4m3(fl32(x / scale[h])) (e5m2(...), int8(...)) -- one IEEE
+ * binary32 division by that head's scale, then the rounding above. */
 int oracle_kv_cache_write(const void* key, const void* value, int src_dtype,
                           void* k_pool, void* v_pool, int cache_dtype, int64_t num_blocks,
                           const int64_t* slot_mapping, int64_t num_tokens,
@@ -219,9 +250,9 @@ int oracle_kv_cache_write(const void* key, const void* value, int src_dtype,
 {
     int es = elem_bytes(src_dtype), ec = elem_bytes(cache_dtype);
     if (!es || !ec) return OR_ERR_DTYPE;
-    if (is_fp8(src_dtype)) return OR_ERR_DTYPE;
-    if (src_dtype != cache_dtype && !is_fp8(cache_dtype)) return OR_ERR_DTYPE;
-    if (is_fp8(cache_dtype) && (!k_scale || !v_scale)) return OR_ERR_ARG;
+    if (is_quant(src_dtype)) return OR_ERR_DTYPE;
+    if (src_dtype != cache_dtype && !is_quant(cache_dtype)) return OR_ERR_DTYPE;
+    if (is_quant(cache_dtype) && (!k_scale || !v_scale)) return OR_ERR_ARG;
     if (!layout_ok(head_dim, block_size, cache_dtype)) return OR_ERR_ARG;
     const unsigned char* src[2] = {(const unsigned char*)key, (const unsigned char*)value};
     unsigned char* dst[2] = {(unsigned char*)k_pool, (unsigned char*)v_pool};
@@ -251,7 +282,9 @@ int oracle_kv_cache_write(const void* key, const void* value, int src_dtype,
                             x = (float)bf16_bits_to_double(bb);
                         }
                         float y = x / scl[kv][h]; /* binary32 division, round to nearest */
-                        dst[kv][di] = cache_dtype == OR_FP8_E4M3 ? oracle_e4m3_encode(y) : oracle_e5m2_encode(y);
+                        dst[kv][di] = cache_dtype == OR_FP8_E4M3   ? oracle_e4m3_encode(y)
+                                      : cache_dtype == OR_FP8_E5M2 ? oracle_e5m2_encode(y)
+                                                                   : oracle_int8_encode(y);
                     }
                 }
             }
@@ -296,7 +329,7 @@ static int attend_row(const job_t* J, int s, int64_t row, int i, int q_len, int 
     if (n <= 0) return OR_OK;
     if ((n + B - 1) / B > J->mbps) return OR_ERR_BOUNDS;
     double ks = 1.0, vs = 1.0;
-    if (is_fp8(J->cache_dtype)) {
+    if (is_quant(J->cache_dtype)) {
         ks = (double)J->k_scale[g];
         vs = (double)J->v_scale[g];
     }
@@ -379,10 +412,10 @@ int oracle_paged_attention(double* out, const void* query, int q_dtype,
                            int num_heads, int num_kv_heads, int head_dim, int block_size,
                            double scale, const float* k_scale, const float* v_scale, int nthreads)
 {
-    if (!elem_bytes(q_dtype) || is_fp8(q_dtype) || !elem_bytes(cache_dtype)) return OR_ERR_DTYPE;
+    if (!elem_bytes(q_dtype) || is_quant(q_dtype) || !elem_bytes(cache_dtype)) return OR_ERR_DTYPE;
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads) return OR_ERR_ARG;
     if (!layout_ok(head_dim, block_size, cache_dtype)) return OR_ERR_ARG;
-    if (is_fp8(cache_dtype) && (!k_scale || !v_scale)) return OR_ERR_ARG;
+    if (is_quant(cache_dtype) && (!k_scale || !v_scale)) return OR_ERR_ARG;
     if (num_seqs == 0) return OR_OK;
     for (int s = 0; s < num_seqs; s++)
         if (cu_q[s + 1] < cu_q[s]) return OR_ERR_ARG;
@@ -452,4 +485,14 @@ void oracle_e5m2_encode_array(const float* y, uint8_t* codes, int64_t n)
 void oracle_e5m2_decode_array(const uint8_t* codes, double* out, int64_t n)
 {
     for (int64_t i = 0; i < n; i++) out[i] = oracle_e5m2_to_double(codes[i]);
+}
+
+void oracle_int8_encode_array(const float* y, uint8_t* codes, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) codes[i] = oracle_int8_encode(y[i]);
+}
+
+void oracle_int8_decode_array(const uint8_t* codes, double* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = oracle_int8_to_double(codes[i]);
 }

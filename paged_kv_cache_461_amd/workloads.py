@@ -2,7 +2,8 @@
 
 This module is shared by the tests, the benchmark and the smoke check, and by both sides of
 a parity comparison.  It generates inputs only: sequence lengths, block allocation with
-refcounts, block tables, slot mappings, random token values and fp8 calibration scales.  It
+refcounts, block tables, slot mappings, random token values and the calibration scales of a
+quantised (fp8 / INT8) cache.  It
 contains none of the attention or quantisation arithmetic.  It imports nothing from the
 HIP binding or from the oracle.
 
@@ -13,7 +14,7 @@ Every random draw comes from ``numpy.random.default_rng`` seeded with a tuple
   stream 101  per-(layer, sequence) token K/V values  (positions after a shared prefix)
   stream 102  per-layer shared-prefix K/V values
   stream 103  query rows
-  stream 104  fp8 calibration batch
+  stream 104  calibration batch of a quantised (fp8 / INT8) cache's scales
 
 Values are N(0, 1) drawn in float32, then rounded to the cache source dtype (bf16 with
 round-to-nearest-even).  The workload shapes follow the pages' running example of a
@@ -27,16 +28,19 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-F32, BF16, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3
-DTYPE_NAMES = {F32: "f32", BF16: "bf16", FP8_E4M3: "fp8_e4m3", FP8_E5M2: "fp8_e5m2"}
-ELEM_BYTES = {F32: 4, BF16: 2, FP8_E4M3: 1, FP8_E5M2: 1}
-RAW_NP = {F32: np.float32, BF16: np.uint16, FP8_E4M3: np.uint8, FP8_E5M2: np.uint8}
-POISON = {F32: np.float32(np.nan), BF16: np.uint16(0x7FC0), FP8_E4M3: np.uint8(0x7F), FP8_E5M2: np.uint8(0x7F)}
+F32, BF16, FP8_E4M3, FP8_E5M2, INT8 = 0, 1, 2, 3, 4
+DTYPE_NAMES = {F32: "f32", BF16: "bf16", FP8_E4M3: "fp8_e4m3", FP8_E5M2: "fp8_e5m2", INT8: "int8"}
+ELEM_BYTES = {F32: 4, BF16: 2, FP8_E4M3: 1, FP8_E5M2: 1, INT8: 1}
+RAW_NP = {F32: np.float32, BF16: np.uint16, FP8_E4M3: np.uint8, FP8_E5M2: np.uint8, INT8: np.uint8}
+# Unused slots are filled with a value no append writes: NaN, or the INT8 code -128 (0x80).
+POISON = {F32: np.float32(np.nan), BF16: np.uint16(0x7FC0), FP8_E4M3: np.uint8(0x7F), FP8_E5M2: np.uint8(0x7F),
+          INT8: np.uint8(0x80)}
 FP8_DTYPES = (FP8_E4M3, FP8_E5M2)
+QUANT_DTYPES = (FP8_E4M3, FP8_E5M2, INT8)  # caches of codes times a per-head scale
 
-FP8_E4M3_MAX = 448.0  # largest finite OCP E4M3 value, used only to size calibration scales
-FP8_E5M2_MAX = 57344.0  # largest finite OCP E5M2 value, likewise
-FP8_MAX = {FP8_E4M3: FP8_E4M3_MAX, FP8_E5M2: FP8_E5M2_MAX}
+# Largest code magnitude of each quantised format, used only to size calibration scales: the
+# largest finite OCP E4M3 / E5M2 values and the symmetric INT8 range.
+QUANT_MAX = {FP8_E4M3: 448.0, FP8_E5M2: 57344.0, INT8: 127.0}
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -135,9 +139,10 @@ class PagedBatch:
     shared_prefix_len: int = 0
     sharing: np.ndarray = field(default_factory=lambda: np.zeros(0, dtype=np.int64))
     refcount: np.ndarray = field(default_factory=lambda: np.zeros(0, dtype=np.int32))
-    k_scale: np.ndarray | None = None  # float32 [Hkv] for an fp8 cache
+    k_scale: np.ndarray | None = None  # float32 [Hkv] for a quantised (fp8 / INT8) cache
     v_scale: np.ndarray | None = None
-    fp8_scale: str = "head"  # fp8 scale granularity: "head" or "tensor" (one value repeated per head)
+    fp8_scale: str = "head"  # quantised-cache scale granularity: "head" or "tensor" (one value repeated
+                             # per head)
 
     # -- shapes ------------------------------------------------------------------------
     @property
@@ -297,13 +302,13 @@ class PagedBatch:
 
     def decode_bytes(self, unique: bool = True) -> int:
         """Algorithmic bytes of one attention call: KV + query + output + tables + lengths
-        (+ fp8 scales)."""
+        (+ the scales of a quantised cache)."""
         eq = ELEM_BYTES[self.q_dtype]
         nblk = (self.context_lens.astype(np.int64) + self.block_size - 1) // self.block_size
         b = self.kv_read_bytes(unique)
         b += self.num_rows * self.num_heads * self.head_dim * 2 * eq
         b += int(nblk.sum()) * 4 + self.num_seqs * 4
-        if self.cache_dtype in FP8_DTYPES:
+        if self.cache_dtype in QUANT_DTYPES:
             b += 2 * 4 * self.num_kv_heads
         return int(b)
 
@@ -333,14 +338,14 @@ class PagedBatch:
 def build_batch(context_lens, *, num_heads, num_kv_heads, head_dim, block_size=16, q_dtype=BF16,
                 cache_dtype=BF16, src_dtype=None, seed=0, query_lens=None, shared_prefix_len=0,
                 sharing=(), num_blocks=None, pool_slack=0.10, max_blocks_per_seq=None, layer=0,
-                name="custom", fp8_calibration_tokens=4096, fp8_scale="head") -> PagedBatch:
+                name="custom", quant_calibration_tokens=4096, fp8_scale="head") -> PagedBatch:
     ctx = np.asarray(context_lens, dtype=np.int32)
     S = ctx.shape[0]
     ql = np.ones(S, np.int32) if query_lens is None else np.asarray(query_lens, np.int32)
     if np.any(ql > np.maximum(ctx, 0)) or np.any(ql < 0):
         raise ValueError("query_lens must lie in [0, context_len]")
     if src_dtype is None:
-        src_dtype = q_dtype if cache_dtype in FP8_DTYPES else cache_dtype
+        src_dtype = q_dtype if cache_dtype in QUANT_DTYPES else cache_dtype
     B = block_size
     sharing = np.asarray(sorted(set(int(s) for s in sharing)), dtype=np.int64)
     if shared_prefix_len % B:
@@ -380,27 +385,28 @@ def build_batch(context_lens, *, num_heads, num_kv_heads, head_dim, block_size=1
                        context_lens=ctx, query_lens=ql, block_tables=tables, num_blocks=num_blocks,
                        seed=seed, layer=layer, shared_prefix_len=shared_prefix_len if len(sharing) else 0,
                        sharing=sharing, refcount=alloc.refcount.copy(), fp8_scale=fp8_scale)
-    if cache_dtype in FP8_DTYPES:
-        batch.k_scale, batch.v_scale = fp8_calibration_scales(
-            num_kv_heads, head_dim, seed, layer, src_dtype, fp8_calibration_tokens, cache_dtype, fp8_scale)
+    if cache_dtype in QUANT_DTYPES:
+        batch.k_scale, batch.v_scale = quant_calibration_scales(
+            num_kv_heads, head_dim, seed, layer, src_dtype, quant_calibration_tokens, cache_dtype, fp8_scale)
     return batch
 
 
-def fp8_calibration_scales(num_kv_heads, head_dim, seed, layer, src_dtype, tokens=4096, cache_dtype=FP8_E4M3,
-                           granularity="head"):
-    """fp8 scales for one layer: amax over a seeded calibration batch of K (resp. V) rows
-    drawn like the workload, divided by the format's largest finite value, as float32.
+def quant_calibration_scales(num_kv_heads, head_dim, seed, layer, src_dtype, tokens=4096, cache_dtype=FP8_E4M3,
+                             granularity="head"):
+    """Scales of a quantised cache for one layer: amax over a seeded calibration batch of K
+    (resp. V) rows drawn like the workload, divided by the format's largest code magnitude
+    (448 E4M3, 57344 E5M2, 127 INT8), as float32.
     granularity "head" takes the amax per kv head; "tensor" takes one amax over all heads and
     repeats it per head (a per-tensor scale)."""
     if granularity not in ("head", "tensor"):
-        raise ValueError("fp8 scale granularity must be 'head' or 'tensor'")
+        raise ValueError("scale granularity must be 'head' or 'tensor'")
     rng = np.random.default_rng([seed, 104, layer])
     cal = rng.standard_normal((tokens, 2, num_kv_heads, head_dim), dtype=np.float32)
     cal = raw_to_f32(to_raw(cal, src_dtype), src_dtype)
     amax = np.abs(cal).max(axis=(0, 3))  # [2][Hkv]
     if granularity == "tensor":
         amax = np.repeat(amax.max(axis=1, keepdims=True), num_kv_heads, axis=1)
-    sc = (amax.astype(np.float64) / FP8_MAX[cache_dtype]).astype(np.float32)
+    sc = (amax.astype(np.float64) / QUANT_MAX[cache_dtype]).astype(np.float32)
     return np.ascontiguousarray(sc[0]), np.ascontiguousarray(sc[1])
 
 

@@ -35,13 +35,24 @@ MUTANTS = {
     "e5m2_bias_off_by_one": ("v = ldexp((double)(4 + m), e - 17);", "v = ldexp((double)(4 + m), e - 16);"),
     "e5m2_inf_read_as_nan": ("v = m ? NAN : INFINITY;", "v = NAN;"),
     "e5m2_no_saturation": ("if (a >= 57344.0) return sign | 0x7b;", "if (a >= 61440.0) return sign | 0x7c;"),
-    "e5m2_cache_encoded_as_e4m3": ("cache_dtype == OR_FP8_E4M3 ? oracle_e4m3_encode(y) : oracle_e5m2_encode(y)",
-                                   "oracle_e4m3_encode(y)"),
+    "e5m2_cache_encoded_as_e4m3": ("cache_dtype == OR_FP8_E5M2 ? oracle_e5m2_encode(y)",
+                                   "cache_dtype == OR_FP8_E5M2 ? oracle_e4m3_encode(y)"),
     "e5m2_cache_read_as_e4m3": ("case OR_FP8_E5M2: return oracle_e5m2_to_double(base[idx]);",
                                 "case OR_FP8_E5M2: return oracle_e4m3_to_double(base[idx]);"),
     "fp8_multiply_not_divide": ("float y = x / scl[kv][h];", "float y = x * scl[kv][h];"),
     "softmax_denominator_dropped": ("for (int dd = 0; dd < D; dd++) out[dd] /= den;", ""),
     "kv_bytes_missing_factor_2": ("head_dim * 2 * elem_bytes(dtype)", "head_dim * elem_bytes(dtype)"),
+    "int8_tie_away": ("if (r > 0.5 || (r == 0.5 && n % 2 != 0)) n += 1;", "if (r >= 0.5) n += 1;"),
+    "int8_saturate_at_128": ("if (y <= -127.0f) return (uint8_t)(int8_t)-127;",
+                             "if (y <= -128.0f) return (uint8_t)(int8_t)-128;"),
+    "int8_nan_to_max": ("if (isnan(y)) return 0;", "if (isnan(y)) return 127;"),
+    "int8_truncate": ("double f = floor(a);", "double f = trunc(a);"),
+    "int8_read_unsigned": ("double oracle_int8_to_double(uint8_t c) { return (double)(int8_t)c; }",
+                           "double oracle_int8_to_double(uint8_t c) { return (double)c; }"),
+    "int8_cache_encoded_as_e4m3": ("                                                                   : oracle_int8_encode(y);",
+                                   "                                                                   : oracle_e4m3_encode(y);"),
+    "int8_cache_read_as_e4m3": ("case OR_INT8: return oracle_int8_to_double(base[idx]);",
+                                "case OR_INT8: return oracle_e4m3_to_double(base[idx]);"),
 }
 
 
@@ -59,6 +70,10 @@ def _checks():
     yield lambda: pins.test_e5m2_encode_matches_torch_rne(8.7e-5)
     yield lambda: pins.test_e5m2_round_trip_and_ties()
     yield lambda: pins.test_kv_size_closed_forms()
+    yield lambda: pins.test_int8_decode_table_is_twos_complement()
+    yield lambda: pins.test_int8_encode_exhaustive_over_bf16(4.5 / 127.0)
+    yield lambda: pins.test_int8_round_trip_and_ties()
+    yield lambda: pins.test_decode_equals_sdpa(pins.CASES[9])
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))

@@ -8,6 +8,8 @@
 * closed-form special cases of softmax attention;
 * the OCP E4M3 and E5M2 codecs against torch.float8_e4m3fn / torch.float8_e5m2 and their
   defining constants;
+* the INT8 codec against numpy's binary32 division and round-half-even (numpy.rint) with
+  saturation to [-127, 127], over every bf16 pattern;
 * the KV-size closed forms (page 1, section 2.1; page 3, section 2.1).
 """
 import json
@@ -53,12 +55,28 @@ FP8_CODEC = {W.FP8_E4M3: (oracle.e4m3_encode, oracle.e4m3_to_float64),
              W.FP8_E5M2: (oracle.e5m2_encode, oracle.e5m2_to_float64)}
 
 
+def int8_reference_codes(y):
+    """INT8 codes of binary32 values y without the oracle: round half to even (numpy.rint),
+    saturate to [-127, 127], NaN -> 0; returned as the integer values (float64)."""
+    y = np.asarray(y, dtype=np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        c = np.clip(np.rint(y), -127.0, 127.0)
+    return np.where(np.isnan(y), 0.0, c)
+
+
 def stored_values(batch, s):
     """float64 K, V of sequence s as the cache holds them ([ctx][Hkv][D]), computed without
     the oracle's layout: fp32/bf16 rows are stored exactly; fp8 rows are the E4M3 (E5M2) code
-    of fl32(x / scale) times the scale."""
+    of fl32(x / scale) times the scale; INT8 rows the rounded integer of fl32(x / scale) (by
+    numpy, not the oracle) times the scale."""
     k, v = batch.token_values(s)
     k, v = k.astype(np.float64), v.astype(np.float64)
+    if batch.cache_dtype == W.INT8:
+        out = []
+        for x, sc in ((k, batch.k_scale), (v, batch.v_scale)):
+            y = (x.astype(np.float32) / sc[None, :, None]).astype(np.float32)
+            out.append(int8_reference_codes(y) * sc[None, :, None].astype(np.float64))
+        return out
     if batch.cache_dtype in FP8_CODEC:
         encode, decode = FP8_CODEC[batch.cache_dtype]
         out = []
@@ -103,6 +121,8 @@ CASES = [
     ([33, 18], 4, 1, 64, 16, W.F32, W.FP8_E4M3),
     ([70, 3, 129], 8, 2, 128, 16, W.BF16, W.FP8_E5M2),
     ([21, 48], 4, 2, 64, 16, W.F32, W.FP8_E5M2),
+    ([60, 2, 131], 8, 2, 128, 16, W.BF16, W.INT8),
+    ([19, 40], 4, 1, 64, 16, W.F32, W.INT8),
 ]
 
 
@@ -117,7 +137,7 @@ def test_decode_equals_sdpa(case):
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
 
 
-@pytest.mark.parametrize("cd", [W.BF16, W.FP8_E4M3, W.F32])
+@pytest.mark.parametrize("cd", [W.BF16, W.FP8_E4M3, W.F32, W.INT8])
 def test_chunked_prefill_equals_sdpa_causal(cd):
     qd = W.F32 if cd == W.F32 else W.BF16
     batch = W.build_batch([70, 1, 40, 16], num_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
@@ -155,7 +175,7 @@ def relabel(batch, kp, vp, perm):
     return kp2, vp2, tables2
 
 
-@pytest.mark.parametrize("cd", [W.F32, W.BF16, W.FP8_E4M3])
+@pytest.mark.parametrize("cd", [W.F32, W.BF16, W.FP8_E4M3, W.INT8])
 def test_physical_block_permutation_is_exact(cd):
     qd = W.F32 if cd == W.F32 else W.BF16
     batch = W.build_batch([17, 33, 64, 100], num_heads=8, num_kv_heads=2, head_dim=64,
@@ -398,10 +418,44 @@ def test_e5m2_round_trip_and_ties():
     assert np.array_equal(got, want)
 
 
+# ---- INT8 codec ----------------------------------------------------------------------------------
+
+def test_int8_decode_table_is_twos_complement():
+    codes = np.arange(256, dtype=np.uint8)
+    assert np.array_equal(oracle.int8_to_float64(codes), codes.view(np.int8).astype(np.float64))
+    assert oracle.int8_to_float64(np.array([0x7F, 0x80, 0xFF, 0x01], np.uint8)).tolist() == [127, -128, -1, 1]
+
+
+@pytest.mark.parametrize("scale", [1.0, 4.5 / 127.0, 0.0103125, 3.0, 2.0 ** -12, 1.0 / 127.0])
+def test_int8_encode_exhaustive_over_bf16(scale):
+    """Every bf16 pattern x: code == saturate(rint(fl32(x / scale))) computed by numpy (binary32
+    division, round half to even), NaN -> 0, infinities -> +-127."""
+    x = _all_bf16_as_f32()
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        y = (x / np.float32(scale)).astype(np.float32)
+    ours = oracle.int8_encode(y).view(np.int8).astype(np.float64)
+    assert np.array_equal(ours, int8_reference_codes(y))
+    assert np.all(ours[np.isnan(y)] == 0)
+    assert np.all(ours[np.isinf(y)] == np.where(np.signbit(y[np.isinf(y)]), -127, 127))
+
+
+def test_int8_round_trip_and_ties():
+    codes = np.arange(-127, 128).astype(np.int8).view(np.uint8)
+    vals = oracle.int8_to_float64(codes).astype(np.float32)
+    assert np.array_equal(oracle.int8_encode(vals), codes)
+    # halfway points go to the even integer, on both sides of zero; beyond +-127 saturate
+    k = np.arange(-127, 127)
+    got = oracle.int8_encode((k + 0.5).astype(np.float32)).view(np.int8).astype(np.int64)
+    assert np.array_equal(got, np.where(k % 2 == 0, k, k + 1))
+    assert oracle.int8_encode(np.array([127.4, 127.5, 300.0, -127.5, -128.0, -1e30], np.float32)).view(
+        np.int8).tolist() == [127, 127, 127, -127, -127, -127]
+
+
 # ---- layout and sizes ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype,d,b", [(W.F32, 64, 16), (W.BF16, 128, 16), (W.FP8_E4M3, 128, 16),
-                                       (W.BF16, 64, 4), (W.FP8_E4M3, 64, 2), (W.F32, 128, 32)])
+                                       (W.BF16, 64, 4), (W.FP8_E4M3, 64, 2), (W.F32, 128, 32),
+                                       (W.INT8, 128, 16)])
 def test_layout_is_a_bijection_with_contiguous_tiles(dtype, d, b):
     nb, hkv = 3, 2
     bb, hh, tt, dd = np.meshgrid(np.arange(nb), np.arange(hkv), np.arange(b), np.arange(d), indexing="ij")
@@ -416,7 +470,7 @@ def test_layout_is_a_bijection_with_contiguous_tiles(dtype, d, b):
 def test_kv_size_closed_forms():
     with open(os.path.join(GOLDEN, "kv_size_closed_forms.json")) as fh:
         g = json.load(fh)
-    codes = {"bf16": W.BF16, "fp8_e4m3": W.FP8_E4M3, "f32": W.F32}
+    codes = {"bf16": W.BF16, "fp8_e4m3": W.FP8_E4M3, "f32": W.F32, "int8": W.INT8}
     for c in g["cases"]:
         assert oracle.kv_bytes_per_token(c["layers"], c["kv_heads"], c["head_dim"], codes[c["dtype"]]) \
             == c["bytes_per_token"]
@@ -426,3 +480,4 @@ def test_kv_size_closed_forms():
     assert oracle.kv_bytes_per_token(32, 8, 128, W.BF16) / oracle.kv_bytes_per_token(32, 32, 128, W.BF16) \
         == g["gqa_32q_8kv_fraction"]
     assert oracle.kv_bytes_per_token(32, 8, 128, W.FP8_E4M3) * 2 == per_tok
+    assert oracle.kv_bytes_per_token(32, 8, 128, W.INT8) * 2 == per_tok  # FP16 -> INT8 halves the cache

@@ -67,11 +67,11 @@ def test_e5m2_per_tensor_scales():
     head; per-head scales of the same calibration batch are each at most that value."""
     b = W.WORKLOADS["fp8_e5m2_chunked_prefill"]()
     assert b.cache_dtype == W.FP8_E5M2 and b.fp8_scale == "tensor"
-    head_k, head_v = W.fp8_calibration_scales(b.num_kv_heads, b.head_dim, b.seed, b.layer, b.src_dtype,
+    head_k, head_v = W.quant_calibration_scales(b.num_kv_heads, b.head_dim, b.seed, b.layer, b.src_dtype,
                                               cache_dtype=W.FP8_E5M2, granularity="head")
     assert np.all(b.k_scale == head_k.max()) and np.all(b.v_scale == head_v.max())
     assert len(set(head_k.tolist())) > 1
-    e4_k, _ = W.fp8_calibration_scales(b.num_kv_heads, b.head_dim, b.seed, b.layer, b.src_dtype)
+    e4_k, _ = W.quant_calibration_scales(b.num_kv_heads, b.head_dim, b.seed, b.layer, b.src_dtype)
     np.testing.assert_allclose(head_k.astype(np.float64) * 57344.0, e4_k.astype(np.float64) * 448.0, rtol=1e-6)
 
 
