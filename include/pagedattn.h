@@ -128,9 +128,11 @@ int64_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t nu
  *                  ceil(context_lens[s] / block_size) are never read.
  *   context_lens   device int32 [num_seqs]; a sequence with 0 positions gets zeros.
  *   max_context_len  host bound on context_lens (sizes the launch and the workspace).
- *   scale          softmax scale applied to q.k (1/sqrt(head_dim) for standard attention).
+ *   scale          softmax scale applied to q.k (1/sqrt(head_dim) for standard attention);
+ *                  positive and finite, else PA_ERR_INVALID_ARG.
  *   k_scale, v_scale device fp32 [num_kv_heads] for an fp8 cache (the stored code times
- *                  the scale is the cached value), else NULL.
+ *                  the scale is the cached value), else NULL.  Exactly num_kv_heads values are
+ *                  read from each; a per-tensor scale is passed repeated per head.
  *   partition_size 0 = automatic, else a multiple of block_size.  The work is the list of
  *                  every (sequence, kv head) pair's units (16 tokens, or one 8-token block)
  *                  laid end to end; it is cut into chunks of partition_size tokens' units

@@ -321,7 +321,8 @@ int32_t decode_call(int32_t phase, void* out, const void* query, int32_t q_dtype
         return fail(PA_ERR_INVALID_ARG, "query and pools must be 16-byte aligned");
     if (is_fp8(cache_dtype) && (!k_scale || !v_scale))
         return fail(PA_ERR_INVALID_ARG, "an fp8 cache needs k_scale and v_scale");
-    if (!(scale == scale)) return fail(PA_ERR_INVALID_ARG, "scale is NaN");
+    if (!(scale > 0.0f && scale <= 3.402823466e38f))
+        return fail(PA_ERR_INVALID_ARG, "scale %g: the softmax scale must be positive and finite", (double)scale);
     if ((new_key == nullptr) != (new_value == nullptr))
         return fail(PA_ERR_INVALID_ARG, "new_key and new_value must both be given");
     if (new_key && (!aligned16(new_key) || !aligned16(new_value)))
@@ -479,7 +480,8 @@ int32_t pa_paged_attention_chunked_prefill(void* out, const void* query, int32_t
         return fail(PA_ERR_INVALID_ARG, "query, out and pools must be 16-byte aligned");
     if (is_fp8(cache_dtype) && (!k_scale || !v_scale))
         return fail(PA_ERR_INVALID_ARG, "an fp8 cache needs k_scale and v_scale");
-    if (!(scale == scale)) return fail(PA_ERR_INVALID_ARG, "scale is NaN");
+    if (!(scale > 0.0f && scale <= 3.402823466e38f))
+        return fail(PA_ERR_INVALID_ARG, "scale %g: the softmax scale must be positive and finite", (double)scale);
     const PrefillPlan pl = plan_prefill(num_query_rows, num_seqs, max_query_len, num_heads, num_kv_heads, head_dim,
                                         max_context_len, partition_size);
     if (pl.grid > 0x7FFFFFFF)

@@ -138,6 +138,14 @@ def _dev(name, t, dtype=None):
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
 
 
+def _check_scales(pool, k_scale, v_scale, num_kv_heads):
+    """The kernels read k_scale[g] and v_scale[g] for every kv head g of a quantised cache: both must
+    hold num_kv_heads values (a per-tensor scale is passed repeated per head)."""
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if t is not None and t.numel() != num_kv_heads:
+            raise ValueError("%s must hold one fp32 value per kv head (%d), got %d" % (name, num_kv_heads, t.numel()))
+
+
 def _stream(stream):
     if stream is None:
         return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -161,6 +169,7 @@ def kv_cache_write(key, value, k_pool, v_pool, slot_mapping, *, num_kv_heads, he
     _dev("slot_mapping", slot_mapping, torch.int64)
     _dev("k_scale", k_scale, torch.float32)
     _dev("v_scale", v_scale, torch.float32)
+    _check_scales(k_pool, k_scale, v_scale, num_kv_heads)
     nb = num_pool_blocks(k_pool, num_kv_heads, head_dim, block_size)
     T = slot_mapping.numel()
     if key.numel() != T * num_kv_heads * head_dim or value.shape != key.shape:
@@ -200,6 +209,7 @@ def paged_attention_decode(out, query, k_pool, v_pool, block_tables, context_len
     _dev("context_lens", context_lens, torch.int32)
     _dev("k_scale", k_scale, torch.float32)
     _dev("v_scale", v_scale, torch.float32)
+    _check_scales(k_pool, k_scale, v_scale, num_kv_heads)
     _dev("workspace", workspace)
     if query.dim() != 3 or out.shape != query.shape or out.dtype != query.dtype:
         raise ValueError("query and out must both be [num_seqs][num_heads][head_dim] of one dtype")
@@ -257,6 +267,7 @@ def paged_attention_chunked_prefill(out, query, cu_query_lens, k_pool, v_pool, b
     _dev("context_lens", context_lens, torch.int32)
     _dev("k_scale", k_scale, torch.float32)
     _dev("v_scale", v_scale, torch.float32)
+    _check_scales(k_pool, k_scale, v_scale, num_kv_heads)
     _dev("workspace", workspace)
     if query.dim() != 3 or out.shape != query.shape or out.dtype != query.dtype:
         raise ValueError("query and out must both be [num_query_rows][num_heads][head_dim] of one dtype")
@@ -286,6 +297,7 @@ def paged_attention_decode_append(out, query, new_key, new_value, k_pool, v_pool
     _dev("context_lens", context_lens, torch.int32)
     _dev("k_scale", k_scale, torch.float32)
     _dev("v_scale", v_scale, torch.float32)
+    _check_scales(k_pool, k_scale, v_scale, num_kv_heads)
     _dev("workspace", workspace)
     if query.dim() != 3 or out.shape != query.shape or out.dtype != query.dtype:
         raise ValueError("query and out must both be [num_seqs][num_heads][head_dim] of one dtype")

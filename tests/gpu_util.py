@@ -153,49 +153,6 @@ def assert_close(batch, got: np.ndarray, ref: np.ndarray, rows=None):
     return worst
 
 
-def oracle_sampled_rows(batch, picks):
-    """Oracle outputs for a few rows of a full-size batch, computed one by one.
-
-    picks: list of (sequence s, row i of its q_len rows).  Each pick becomes its own decode
-    sequence over ctx' = context_lens[s] - q_len + i + 1 positions (row i of a chunk is the
-    decode of its position).  The oracle writes only those sequences' tokens, through its own
-    append, into a compact pool holding just their blocks (relabelled 0..n-1, which leaves
-    attention unchanged).  Returns (ref [len(picks)][Hq][D] float64, used physical ids in
-    compact order, compact K pool, compact V pool) -- the pools start zeroed."""
-    B, Hkv, D = batch.block_size, batch.num_kv_heads, batch.head_dim
-    seqs = sorted({s for s, _ in picks})
-    nblk = {s: (int(batch.context_lens[s]) + B - 1) // B for s in seqs}
-    used = np.unique(np.concatenate([batch.block_tables[s, :nblk[s]] for s in seqs])).astype(np.int64)
-    remap = {int(b): k for k, b in enumerate(used)}
-    tables = {s: np.array([remap[int(b)] for b in batch.block_tables[s, :nblk[s]]], dtype=np.int64) for s in seqs}
-    tile = Hkv * B * D
-    dt = W.RAW_NP[batch.cache_dtype]
-    kp = np.zeros(len(used) * tile, dtype=dt)
-    vp = np.zeros(len(used) * tile, dtype=dt)
-    for s in seqs:
-        ctx = int(batch.context_lens[s])
-        k, v = batch.token_raw(s, 0, ctx)
-        t = np.arange(ctx, dtype=np.int64)
-        slots = tables[s][t // B] * B + t % B
-        oracle.kv_cache_write(k, v, batch.src_dtype, kp, vp, batch.cache_dtype, slots, Hkv, D, B, batch.k_scale,
-                              batch.v_scale)
-    q_all = batch.query_raw()
-    cu = batch.cu_query_lens
-    mb = max(nblk.values())
-    vt = np.zeros((len(picks), mb), dtype=np.int32)
-    vctx = np.zeros(len(picks), dtype=np.int32)
-    rows = []
-    for n, (s, i) in enumerate(picks):
-        ql = int(batch.query_lens[s])
-        vt[n, :nblk[s]] = tables[s]
-        vctx[n] = int(batch.context_lens[s]) - ql + i + 1
-        rows.append(int(cu[s]) + i)
-    ref = oracle.paged_attention(np.ascontiguousarray(q_all[rows]), batch.q_dtype, kp, vp, batch.cache_dtype, vt,
-                                 vctx, batch.num_heads, Hkv, D, B, batch.scale, k_scale=batch.k_scale,
-                                 v_scale=batch.v_scale)
-    return ref, used, kp, vp
-
-
 def device_step(batch, db, k_pool, v_pool, partition_size=0):
     """The step as bench.py launches it: chunked prefill for the sequences with several rows
     (they come first), decode for the rest, into one output tensor; the decode gets the

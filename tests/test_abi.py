@@ -91,6 +91,9 @@ def _decode(lib, **kw):
     (dict(phase=4), ops.PA_ERR_INVALID_ARG),
     (dict(query=FAKE + 8), ops.PA_ERR_INVALID_ARG),          # misaligned
     (dict(scale=float("nan")), ops.PA_ERR_INVALID_ARG),
+    (dict(scale=0.0), ops.PA_ERR_INVALID_ARG),               # the softmax scale must be positive
+    (dict(scale=-0.088), ops.PA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), ops.PA_ERR_INVALID_ARG),
     (dict(num_blocks=0), ops.PA_ERR_INVALID_ARG),            # empty pool
     (dict(S=16385), ops.PA_ERR_UNSUPPORTED),                 # more sequences than LDS holds
     (dict(ws=None, ws_bytes=0), ops.PA_ERR_WORKSPACE),       # split-K needs workspace
@@ -234,6 +237,9 @@ def _prefill(lib, **kw):
     (dict(num_blocks=0), ops.PA_ERR_INVALID_ARG),
     (dict(out=FAKE + 2), ops.PA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), ops.PA_ERR_INVALID_ARG),
+    (dict(scale=0.0), ops.PA_ERR_INVALID_ARG),                      # the softmax scale must be positive
+    (dict(scale=-1.0), ops.PA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), ops.PA_ERR_INVALID_ARG),
     (dict(ws=None, ws_bytes=0), ops.PA_ERR_WORKSPACE),              # 128 row blocks -> split keys
     (dict(ws=FAKE + 64, ws_bytes=1 << 30), ops.PA_ERR_WORKSPACE),
 ])
@@ -309,3 +315,4 @@ def test_copy_blocks_rejects_before_launch(lib):
     assert lib.pa_copy_blocks(None, FAKE, 10, 4096, FAKE, 1, None) == ops.PA_ERR_INVALID_ARG
     assert lib.pa_copy_blocks(FAKE + 8, FAKE, 10, 4096, FAKE, 1, None) == ops.PA_ERR_INVALID_ARG
     assert P is not None
+

@@ -214,7 +214,7 @@ def test_kv_write_bit_exact_whole_pool(src, cache):
     slots[rng.random(T) < 0.1] = -1
     vals = rng.standard_normal((2, T, hkv, d)).astype(np.float32) * 3
     key, value = W.to_raw(vals[0], src), W.to_raw(vals[1], src)
-    fmax = W.FP8_MAX.get(cache, 1.0)
+    fmax = W.QUANT_MAX.get(cache, 1.0)
     ks = (np.abs(vals[0]).max(axis=(0, 2)) / fmax * 0.5).astype(np.float32)   # forces some saturation
     vs = (np.abs(vals[1]).max(axis=(0, 2)) / fmax * 1.3).astype(np.float32)
     fp8 = cache in W.FP8_DTYPES
@@ -456,3 +456,21 @@ def test_shared_block_hint_short_contexts():
                                num_kv_heads=b.num_kv_heads, scale=b.scale, block_size=b.block_size,
                                shared_blocks=torch.from_numpy(counts).cuda())
     assert torch.equal(out.view(torch.uint8), base.view(torch.uint8))
+
+
+@pytest.mark.parametrize("n,lo,hi,P,hkv,D", [
+    (3000, 1, 2000, 0, 2, 128),     # several 1024-sequence scan windows, automatic split
+    (3000, 1, 2000, 256, 2, 128),   # the same batch with fixed partitions
+    (16384, 129, 300, 0, 2, 64),    # the most sequences a call takes: 64 KiB of staged lengths
+])
+def test_many_sequences_balanced_split(n, lo, hi, P, hkv, D):
+    """More than 1024 sequences on the balanced (split) path: the prologue scans the staged
+    context lengths in several 1024-sequence windows to find each wave's first unit; at 16384
+    sequences the staged lengths take 64 KiB of LDS per workgroup, so fewer workgroups of the
+    persistent grid are resident at once.  Every row is compared with the oracle."""
+    rng = np.random.default_rng([n, lo, hi, P])
+    ctx = rng.integers(lo, hi + 1, size=n)
+    b = W.build_batch(ctx, num_heads=4 * hkv, num_kv_heads=hkv, head_dim=D, q_dtype=W.BF16, cache_dtype=W.BF16,
+                      seed=n + P)
+    print("many-sequence case: %d seqs, ctx %d..%d, P %d" % (n, ctx.min(), ctx.max(), P), flush=True)
+    step_and_compare(b, partition_size=P)
