@@ -279,6 +279,33 @@ int32_t pa_paged_attention_decode_append(int32_t phase, void* out, const void* q
                                          int32_t partition_size, void* workspace,
                                          size_t workspace_bytes, void* stream);
 
+/*
+ * Decode that allocates nothing and takes no workspace, for callers that cannot allocate device
+ * memory at all: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It equals pa_paged_attention_decode (phase 3, the same kernels, the same output
+ * bits) with the split-K partial results held in a static device array inside the library:
+ * pa_decode_noalloc_max_workspace() bytes (64 MiB) per GPU, reserved when the library's code is
+ * loaded on that GPU and held until the process ends.  The first call on a device looks the
+ * array's address up (hipGetSymbolAddress); no call allocates.
+ *   Arguments as for pa_paged_attention_decode, without workspace and workspace_bytes.
+ *   Returns PA_ERR_WORKSPACE, before any GPU work, when these arguments need more than that many
+ *   bytes of workspace (pa_decode_workspace_size(...) gives an upper bound of the need).
+ * All calls on one GPU share the array, whose contents are left from the last call: two calls
+ * that overlap on one GPU (different streams or host threads without ordering) race and give
+ * undefined results.  Calls ordered on one stream are safe.
+ */
+int32_t pa_paged_attention_decode_noalloc(void* out, const void* query, int32_t q_dtype,
+                                          const void* k_pool, const void* v_pool, int64_t num_blocks,
+                                          int32_t cache_dtype, const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                          int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+                                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                          float scale, const float* k_scale, const float* v_scale,
+                                          int32_t partition_size, void* stream);
+
+/* Bytes of the static scratch array pa_paged_attention_decode_noalloc uses per GPU. */
+int64_t pa_decode_noalloc_max_workspace(void);
+
 /* KV bytes one token occupies over num_layers layers: layers x kv_heads x head_dim x 2 (K and
  * V) x element bytes (page 1, section 2.1: 131072 for 32 x 8 x 128 bf16).  -1 on bad input. */
 int64_t pa_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim,

@@ -2,10 +2,12 @@
 //
 // Host-side validation, workspace sizing and kernel dispatch.  Every argument check
 // happens before anything is enqueued; the library allocates nothing and keeps no state
-// beyond a per-thread error message.
+// beyond a per-thread error message and, for the no-allocation decode, the device address of
+// each GPU's static scratch array.
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/pagedattn.h"
@@ -283,6 +285,54 @@ int64_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t nu
 
 }  // extern "C"
 
+// ---- decode without a caller workspace -------------------------------------------------------
+//
+// For callers that cannot allocate (code under graph capture, tight serving loops): the split-K
+// partial results live in this file-scope device array instead of a caller workspace.  Every
+// GPU the library runs on holds its own copy until the process ends.  In host code the array's
+// name is only a stand-in; its device address is looked up once per device with
+// hipGetSymbolAddress (with that device current) and that address is what the kernels get.
+// Every call on one GPU shares the array: calls that overlap on one GPU (two streams, two
+// threads) race.  The kernels need no part of it zeroed (the merge reads only what the
+// streaming kernel of the same call wrote), so nothing is cleared between calls.
+
+namespace {
+
+constexpr int64_t kNoAllocScratchBytes = 64ll << 20;  // 64 MiB per GPU
+constexpr int kMaxScratchDevices = 64;
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+// Device address of this device's scratch, looked up on the first call on the device.
+int32_t scratch_for_current_device(void** ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(PA_ERR_UNSUPPORTED, "device %d (the scratch table covers devices 0..%d)", dev,
+                    kMaxScratchDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return PA_OK;
+}
+
+}  // namespace
+
 namespace {
 
 // Decode, with the fused append when new_key is not null.
@@ -293,7 +343,7 @@ int32_t decode_call(int32_t phase, void* out, const void* query, int32_t q_dtype
                     int32_t num_seqs, int32_t num_heads,
                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale, const float* k_scale,
                     const float* v_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
-                    void* stream)
+                    void* stream, bool use_scratch = false)
 {
     if (phase < 1 || phase > 3) return fail(PA_ERR_INVALID_ARG, "phase %d (1, 2 or 3)", phase);
     int32_t st = check_decode_shape(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
@@ -331,6 +381,15 @@ int32_t decode_call(int32_t phase, void* out, const void* query, int32_t q_dtype
         (int64_t)pa::kSimds * pa::decode_waves_per_simd(q_dtype, cache_dtype, head_dim, num_heads / num_kv_heads);
     const DecodePlan pl = plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
                                       partition_size, stream_waves);
+    if (use_scratch) {  // the no-allocation form: this GPU's static scratch array is the workspace
+        if (pl.total > kNoAllocScratchBytes)
+            return fail(PA_ERR_WORKSPACE, "this decode needs %lld bytes of split-K scratch, above the %lld bytes the "
+                        "no-allocation entry point holds per GPU (use pa_paged_attention_decode with a workspace)",
+                        (long long)pl.total, (long long)kNoAllocScratchBytes);
+        const int32_t sst = scratch_for_current_device(&workspace);
+        if (sst != PA_OK) return sst;
+        workspace_bytes = (size_t)kNoAllocScratchBytes;
+    }
     if (pl.total > 0) {
         if (!workspace || (int64_t)workspace_bytes < pl.total)
             return fail(PA_ERR_WORKSPACE, "workspace %zu bytes at %p, need %lld", workspace_bytes, workspace,
@@ -423,6 +482,22 @@ int32_t pa_paged_attention_decode_append(int32_t phase, void* out, const void* q
                        max_blocks_per_seq, context_lens, nullptr, max_context_len, num_seqs, num_heads, num_kv_heads,
                        head_dim, block_size, scale, k_scale, v_scale, partition_size, workspace, workspace_bytes,
                        stream);
+}
+
+int64_t pa_decode_noalloc_max_workspace(void) { return kNoAllocScratchBytes; }
+
+int32_t pa_paged_attention_decode_noalloc(void* out, const void* query, int32_t q_dtype, const void* k_pool,
+                                          const void* v_pool, int64_t num_blocks, int32_t cache_dtype,
+                                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
+                                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t block_size, float scale, const float* k_scale,
+                                          const float* v_scale, int32_t partition_size, void* stream)
+{
+    return decode_call(3, out, query, q_dtype, nullptr, nullptr, k_pool, v_pool, num_blocks, cache_dtype,
+                       block_tables, max_blocks_per_seq, context_lens, nullptr, max_context_len, num_seqs, num_heads,
+                       num_kv_heads, head_dim, block_size, scale, k_scale, v_scale, partition_size, nullptr, 0, stream,
+                       true);
 }
 
 int32_t pa_paged_attention_decode(void* out, const void* query, int32_t q_dtype, const void* k_pool,

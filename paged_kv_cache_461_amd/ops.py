@@ -37,6 +37,7 @@ EXPORTS = (
     "pa_chunked_prefill_workspace_size", "pa_paged_attention_chunked_prefill", "pa_paged_attention_decode_append",
     "pa_paged_attention_decode_shared", "pa_copy_blocks", "pa_bm_create", "pa_bm_destroy", "pa_bm_add_sequence", "pa_bm_append_token", "pa_bm_fork",
     "pa_bm_free_sequence", "pa_bm_block_table", "pa_bm_refcount", "pa_bm_get_stats",
+    "pa_paged_attention_decode_noalloc", "pa_decode_noalloc_max_workspace",
 )
 
 
@@ -68,6 +69,10 @@ def library():
         lib.pa_paged_attention_decode_phase.argtypes = [I32] + dec
         lib.pa_paged_attention_decode_shared.restype = I32
         lib.pa_paged_attention_decode_shared.argtypes = [I32] + dec[:10] + [P] + dec[10:]
+        lib.pa_paged_attention_decode_noalloc.restype = I32
+        lib.pa_paged_attention_decode_noalloc.argtypes = dec[:20] + [P]
+        lib.pa_decode_noalloc_max_workspace.restype = I64
+        lib.pa_decode_noalloc_max_workspace.argtypes = []
         lib.pa_paged_attention_decode_append.restype = I32
         lib.pa_paged_attention_decode_append.argtypes = [I32, P, P, I32, P, P] + dec[3:]
         lib.pa_chunked_prefill_workspace_size.restype = I64
@@ -234,6 +239,36 @@ def paged_attention_decode(out, query, k_pool, v_pool, block_tables, context_len
         block_size, float(scale), _ptr(k_scale), _ptr(v_scale), int(partition_size), _ptr(workspace), ws_bytes,
         _stream(stream)))
     return out
+
+
+def paged_attention_decode_noalloc(out, query, k_pool, v_pool, block_tables, context_lens, *, max_context_len,
+                                   num_kv_heads, scale, block_size=16, k_scale=None, v_scale=None, partition_size=0,
+                                   stream=None):
+    """pa_paged_attention_decode without a workspace: the library's static per-GPU scratch holds
+    the split-K partial results (pa_paged_attention_decode_noalloc).  Calls that overlap on one
+    GPU race."""
+    for n, t in (("out", out), ("query", query), ("k_pool", k_pool), ("v_pool", v_pool)):
+        _dev(n, t)
+    _dev("block_tables", block_tables, torch.int32)
+    _dev("context_lens", context_lens, torch.int32)
+    _dev("k_scale", k_scale, torch.float32)
+    _dev("v_scale", v_scale, torch.float32)
+    if query.dim() != 3 or out.shape != query.shape or out.dtype != query.dtype:
+        raise ValueError("query and out must both be [num_seqs][num_heads][head_dim] of one dtype")
+    S, Hq, D = query.shape
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables must be [num_seqs][max_blocks] and context_lens [num_seqs]")
+    _check_scales(k_pool, k_scale, v_scale, num_kv_heads)
+    nb = num_pool_blocks(k_pool, num_kv_heads, D, block_size)
+    _check(library().pa_paged_attention_decode_noalloc(
+        _ptr(out), _ptr(query), dtype_code(query), _ptr(k_pool), _ptr(v_pool), nb, dtype_code(k_pool),
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), int(max_context_len), S, Hq, num_kv_heads, D,
+        block_size, float(scale), _ptr(k_scale), _ptr(v_scale), int(partition_size), _stream(stream)))
+    return out
+
+
+def decode_noalloc_max_workspace() -> int:
+    return int(library().pa_decode_noalloc_max_workspace())
 
 
 def chunked_prefill_workspace_size(num_query_rows, num_seqs, max_query_len, num_heads, num_kv_heads, head_dim,

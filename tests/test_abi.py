@@ -316,3 +316,42 @@ def test_copy_blocks_rejects_before_launch(lib):
     assert lib.pa_copy_blocks(FAKE + 8, FAKE, 10, 4096, FAKE, 1, None) == ops.PA_ERR_INVALID_ARG
     assert P is not None
 
+def _noalloc(lib, **kw):
+    a = dict(out=FAKE, query=FAKE, q_dtype=BF16, k_pool=FAKE, v_pool=FAKE, num_blocks=100, cache_dtype=BF16,
+             block_tables=FAKE, mbps=256, context_lens=FAKE, max_ctx=4096, S=64, Hq=32, Hkv=8, D=128, B=16,
+             scale=0.088, k_scale=None, v_scale=None, P=0, stream=None)
+    a.update(kw)
+    return lib.pa_paged_attention_decode_noalloc(
+        a["out"], a["query"], a["q_dtype"], a["k_pool"], a["v_pool"], a["num_blocks"], a["cache_dtype"],
+        a["block_tables"], a["mbps"], a["context_lens"], a["max_ctx"], a["S"], a["Hq"], a["Hkv"], a["D"], a["B"],
+        a["scale"], a["k_scale"], a["v_scale"], a["P"], a["stream"])
+
+
+def test_noalloc_scratch_limit(lib):
+    assert lib.pa_decode_noalloc_max_workspace() == 64 << 20
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=None), ops.PA_ERR_INVALID_ARG),
+    (dict(D=96), ops.PA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), ops.PA_ERR_INVALID_ARG),
+    (dict(cache_dtype=FP8), ops.PA_ERR_INVALID_ARG),               # fp8 without scales
+    (dict(S=4096, Hq=64, Hkv=8), ops.PA_ERR_WORKSPACE),              # needs more than the 64 MiB scratch
+    (dict(S=16, P=16, max_ctx=32768, mbps=2048), ops.PA_ERR_WORKSPACE),  # 16-token partitions of 32 K tokens
+])
+def test_noalloc_rejects_before_any_gpu_call(lib, kw, status):
+    """Argument and size errors of the no-allocation decode come back before the scratch array's
+    address is looked up, so they need no device."""
+    assert _noalloc(lib, **kw) == status
+    assert lib.pa_last_error() != b""
+
+
+def test_noalloc_empty_batch_is_ok(lib):
+    assert _noalloc(lib, S=0, out=None, query=None) == ops.PA_OK
+
+
+def test_noalloc_limit_covers_the_benchmark_decodes(lib):
+    """The 64 MiB scratch holds the split-K workspace of every decode batch the benchmark times
+    (the workspace size is an upper bound of the no-allocation call's need)."""
+    for S, maxctx in ((64, 4096), (16, 8192), (256, 32768), (128, 8192)):
+        assert 0 < lib.pa_decode_workspace_size(S, 32, 8, 128, 16, maxctx, 0) <= 64 << 20
