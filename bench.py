@@ -1,26 +1,28 @@
 #!/usr/bin/env python3
-"""Benchmark of one paged decode step on one MI355X (gfx950).
+"""Benchmark of the paged-KV hot path on one MI355X (gfx950).
 
 A step is the whole hot path over one batch: the paged KV append of every sequence's new
-token (pa_kv_cache_write) followed by PagedAttention decode of every sequence's query row
-over its paged context (pa_paged_attention_decode: the per-partition attention kernel, then
-the split-K merge kernel).  Inputs are seeded synthetic data of the Llama-3-8B-shaped decode
-layer (64 sequences, contexts uniform in [512, 4096], 32 query / 8 KV heads, head dim 128,
-bf16, 16-token blocks, pool = used blocks + 10%); they are resident in HBM before timing.
-Several layers' pools (same block tables, different values) are cycled through so that no
-step finds the previous step's KV in the 256 MB last-level cache.
+token (pa_kv_cache_write), then PagedAttention over every sequence's paged context: chunked
+prefill (pa_paged_attention_chunked_prefill, bf16 matrix cores) for sequences with a prompt
+chunk, decode (pa_paged_attention_decode: the streaming kernel, then the split-K merge kernel)
+for the single-row ones.  Inputs are seeded synthetic data; they are resident in HBM before
+timing.  Several layers' pools (same block tables, different values) are cycled through so
+that no step finds the previous step's KV in the 256 MB last-level cache.
 
-With --workload fp8_chunked_prefill the step is the mixed one: append of the 512 chunk rows
-and the 128 decode tokens into an fp8 cache, chunked prefill of the chunk
-(pa_paged_attention_chunked_prefill, bf16 matrix cores) and decode of the 128 sequences;
-`roofline_prefill` then reports the chunk kernel against the bf16 MFMA peak.
+The headline is the Llama-3-8B-shaped decode layer (64 sequences, contexts uniform in
+[512, 4096], 32 query / 8 KV heads, head dim 128, bf16, 16-token blocks).  The same run also
+measures, under `workloads`, the tiny fp32 step (launch latency, eager and HIP-graph replay),
+the long-context batch (16 x 8192, partition sweep auto / 256 / 512 / 1024, four layers'
+pools), the continuous-batching mixed batch (256 log-normal contexts, 64 sharing a
+2048-token prefix) and the fp8 step (512-row chunk + 128 decode rows over an E4M3 cache).
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--layers L] [--partition-size P]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--extra LIST|none]
 
-Prints one JSON line.  `value` is algorithmic bytes of the step (KV read + query/output +
-tables + append traffic) over the measured step time, in TB/s; `roofline` reports the decode
-attention kernel alone, timed with HIP events on its stream; `cpu_baseline` times the CPU
-float64 oracle on the same batch (one layer) on this host's cores.
+Prints one JSON line.  `value` is the step's algorithmic bytes (KV read + query/output +
+tables + append traffic) over the measured step time, in TB/s; `step_us` gives the median
+and p10/p90 of single steps; `roofline` reports the decode streaming kernel and
+`roofline_decode_call` the whole decode call (streaming + merge); `cpu_baseline` times the
+CPU float64 oracle on the same batch (one layer) on this host's cores, and on one core.
 """
 from __future__ import annotations
 
@@ -43,32 +45,45 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
+# Workloads measured beside the headline by default, with the layer pools each cycles and the
+# partition sizes its decode is timed at (the first is the step's).
+EXTRA_DEFAULT = ("tiny_fp32", "long_context", "mixed_continuous_batch", "fp8_chunked_prefill")
+LAYERS = {"tiny_fp32": 2, "llama3_8b_decode": 2, "long_context": 4, "mixed_continuous_batch": 2,
+          "fp8_chunked_prefill": 2, "fp8_e5m2_chunked_prefill": 2, "int8_chunked_prefill": 2}
+PARTITIONS = {"long_context": (0, 256, 512, 1024)}
+WORKLOAD_NAMES = ("llama3_8b_decode", "long_context", "mixed_continuous_batch", "fp8_chunked_prefill",
+                  "fp8_e5m2_chunked_prefill", "int8_chunked_prefill", "tiny_fp32")
+
 
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="llama3_8b_decode",
-                   choices=["llama3_8b_decode", "long_context", "mixed_continuous_batch", "fp8_chunked_prefill",
-                            "fp8_e5m2_chunked_prefill", "tiny_fp32"])
-    p.add_argument("--layers", type=int, default=2, help="layer pools cycled through (>= 2)")
-    p.add_argument("--partition-size", type=int, default=0, help="split-K partition (0 = library's choice)")
+    p.add_argument("--workload", default="llama3_8b_decode", choices=WORKLOAD_NAMES)
+    p.add_argument("--layers", type=int, default=0, help="layer pools cycled through (0 = the workload's default)")
+    p.add_argument("--partition-size", type=int, default=-1,
+                   help="split-K partition of the headline decode (0 = library's choice; default: the workload's "
+                        "sweep, auto first)")
     p.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32],
-                   help="tokens per KV block of the pools (both workloads)")
-    p.add_argument("--extra-workload", default="fp8_chunked_prefill",
-                   choices=["none", "fp8_chunked_prefill", "fp8_e5m2_chunked_prefill", "llama3_8b_decode",
-                            "long_context", "mixed_continuous_batch"],
-                   help="second workload measured in the same run and reported under extra_step")
+                   help="tokens per KV block of the pools (every workload)")
+    p.add_argument("--extra", default=",".join(EXTRA_DEFAULT),
+                   help="comma-separated workloads measured in the same run and reported under `workloads`, "
+                        "or 'none'")
+    p.add_argument("--per-step", type=int, default=50, help="single steps timed for the median / p10 / p90")
     p.add_argument("--fused-append", action="store_true",
                    help="decode rows append their new token inside the decode call (pa_paged_attention_decode_append) "
                         "instead of pa_kv_cache_write before it")
     p.add_argument("--graph", action="store_true",
-                   help="also replay the step from HIP graphs and report it under graph_step")
+                   help="also replay the headline step from HIP graphs and report it under graph_step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device copy (HBM counter calibration) and exit")
     return p.parse_args()
+
+
+def log(msg):
+    print("# " + msg, file=sys.stderr, flush=True)
 
 
 def copy_probe():
@@ -118,7 +133,7 @@ def make_batch(name, block_size=16):
 
 
 KERNEL_SOURCES = {
-    "decode": ("decode_kernel.hpp", "decode.hip", "decode_fused.hip", "kv_store.hpp", "pa_device.hpp",
+    "decode": ("decode_kernel.hpp", "decode_launch.hpp", "decode.hip", "kv_store.hpp", "pa_device.hpp",
                "pa_internal.hpp"),
     "prefill": ("prefill.hip", "pa_device.hpp", "pa_internal.hpp"),
 }
@@ -141,10 +156,10 @@ def traffic_key(batch, fused=False):
     return key if batch.block_size == 16 else "%s/b%d" % (key, batch.block_size)
 
 
-def stored_traffic(workload, digest, kernel="decode"):
+def stored_traffic(key, digest, kernel="decode"):
     """HBM bytes per launch of `kernel` from the committed counter runs, if they were taken on
     the current kernel sources for this workload; else None."""
-    key = workload if kernel == "decode" else "%s/%s" % (workload, kernel)
+    key = key if kernel == "decode" else "%s/%s" % (key, kernel)
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh).get(key)
@@ -155,50 +170,61 @@ def stored_traffic(workload, digest, kernel="decode"):
     return rec.get("hbm_bytes_per_launch")
 
 
+def derived_layer(t):
+    """Another layer's pool from layer 0's on the device: every value with its sign flipped (bf16,
+    fp32 and fp8 codes: the sign bit; INT8 codes: negated).  Same shape and magnitudes, different
+    values, at its own address -- which is all the layer cycling needs."""
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return (t.view(torch.int16) ^ -32768).view(torch.bfloat16)
+    if t.dtype == torch.float32:
+        return (t.view(torch.int32) ^ -(1 << 31)).view(torch.float32)
+    if t.dtype == torch.int8:
+        return torch.neg(t)
+    return (t.view(torch.uint8) ^ 0x80).view(t.dtype)
+
+
 def fill_pools(batch, layers, dev):
-    """Device K/V pools for each layer (same tables, per-layer values), history written by
-    the library's append; returns the pools and, for layer 0, the raw history chunks'
-    generator arguments (regenerated on demand for the CPU baseline)."""
+    """Device K/V pools for each layer: layer 0's history written by the library's append from
+    the seeded generator, layers 1.. derived from it on the device (derived_layer).  Each entry:
+    (k_pool, v_pool, (new K rows, new V rows, slots), query, k_scale, v_scale)."""
     import torch
 
     from paged_kv_cache_461_amd import ops
     from paged_kv_cache_461_amd import workloads as W
 
     tdt = {W.BF16: torch.bfloat16, W.F32: torch.float32, W.FP8_E4M3: torch.uint8,
-           W.FP8_E5M2: torch.float8_e5m2}[batch.cache_dtype]
+           W.FP8_E5M2: torch.float8_e5m2, W.INT8: torch.int8}[batch.cache_dtype]
     sdt = {W.BF16: torch.bfloat16, W.F32: torch.float32}[batch.src_dtype]
-    pools = []
-    for layer in range(layers):
-        lb = dataclasses.replace(batch, layer=layer)
-        if batch.cache_dtype in W.QUANT_DTYPES:
-            lb.k_scale, lb.v_scale = W.quant_calibration_scales(batch.num_kv_heads, batch.head_dim, batch.seed, layer,
-                                                              batch.src_dtype, cache_dtype=batch.cache_dtype,
-                                                              granularity=batch.fp8_scale)
-        ks = None if lb.k_scale is None else torch.from_numpy(lb.k_scale).to(dev)
-        vs = None if lb.v_scale is None else torch.from_numpy(lb.v_scale).to(dev)
-        # fp8 pools are zeroed as bytes, then typed (E5M2 pools must carry the float8_e5m2 type)
-        zdt = torch.uint8 if batch.cache_dtype in W.QUANT_DTYPES else tdt
-        kp = torch.zeros(batch.pool_elems, dtype=zdt, device=dev).view(tdt)
-        vp = torch.zeros(batch.pool_elems, dtype=zdt, device=dev).view(tdt)
-        for k, v, slots in lb.history_chunks():
-            kt = torch.from_numpy(k.view(np.int16) if k.dtype == np.uint16 else k).to(dev).view(sdt)
-            vt = torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).to(dev).view(sdt)
-            ops.kv_cache_write(kt, vt, kp, vp, torch.from_numpy(slots).to(dev), num_kv_heads=batch.num_kv_heads,
-                               head_dim=batch.head_dim, block_size=batch.block_size, k_scale=ks, v_scale=vs)
-        k, v, slots = lb.new_tokens()
-        new = (torch.from_numpy(k.view(np.int16) if k.dtype == np.uint16 else k).to(dev).view(sdt),
-               torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).to(dev).view(sdt),
-               torch.from_numpy(slots).to(dev))
-        q = lb.query_raw()
-        qt = torch.from_numpy(q.view(np.int16) if q.dtype == np.uint16 else q).to(dev).view(sdt)
-        pools.append((kp, vp, new, qt, ks, vs))
+
+    def dev_src(a):
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev).view(sdt)
+
+    ks = None if batch.k_scale is None else torch.from_numpy(batch.k_scale).to(dev)
+    vs = None if batch.v_scale is None else torch.from_numpy(batch.v_scale).to(dev)
+    # 8-bit pools are zeroed as bytes, then typed (E5M2 and INT8 pools carry their torch type)
+    zdt = torch.uint8 if batch.cache_dtype in W.QUANT_DTYPES else tdt
+    kp = torch.zeros(batch.pool_elems, dtype=zdt, device=dev).view(tdt)
+    vp = torch.zeros(batch.pool_elems, dtype=zdt, device=dev).view(tdt)
+    for k, v, slots in batch.history_chunks():
+        ops.kv_cache_write(dev_src(k), dev_src(v), kp, vp, torch.from_numpy(slots).to(dev),
+                           num_kv_heads=batch.num_kv_heads, head_dim=batch.head_dim, block_size=batch.block_size,
+                           k_scale=ks, v_scale=vs)
+    k, v, slots = batch.new_tokens()
+    new = (dev_src(k), dev_src(v), torch.from_numpy(slots).to(dev))
+    q = dev_src(batch.query_raw())
+    pools = [(kp, vp, new, q, ks, vs)]
+    for _ in range(1, layers):
+        pools.append((derived_layer(kp), derived_layer(vp), new, q, ks, vs))
     torch.cuda.synchronize()
     return pools
 
 
-def cpu_baseline(batch, min_seconds=1.5):
+def cpu_baseline(batch, min_seconds=10.0):
     """The CPU float64 oracle on the same step (one layer): append of the new tokens, then
-    decode of every sequence's query row.  Host pool built by the oracle's own append."""
+    attention of every query row; host pool built by the oracle's own append.  Repeated on all
+    host cores to >= min_seconds of work, then run once on one core."""
     import oracle
 
     kp, vp = batch.empty_pool(poison=False)
@@ -212,41 +238,56 @@ def cpu_baseline(batch, min_seconds=1.5):
     k, v, slots = batch.new_tokens()
     q = batch.query_raw()
     cu = None if batch.is_decode else batch.cu_query_lens
-    cores = len(os.sched_getaffinity(0))
-    runs, t0 = 0, time.perf_counter()
-    while runs == 0 or time.perf_counter() - t0 < min_seconds:  # repeat to >= min_seconds of wall time
+
+    def step(threads):
         append(k, v, slots)
         oracle.paged_attention(q, batch.q_dtype, kp, vp, batch.cache_dtype, batch.block_tables,
                                batch.context_lens, batch.num_heads, batch.num_kv_heads, batch.head_dim,
                                batch.block_size, batch.scale, cu_query_lens=cu, k_scale=batch.k_scale,
-                               v_scale=batch.v_scale, nthreads=cores)
+                               v_scale=batch.v_scale, nthreads=threads)
+
+    cores = len(os.sched_getaffinity(0))
+    runs, t0 = 0, time.perf_counter()
+    while runs == 0 or time.perf_counter() - t0 < min_seconds:
+        step(cores)
         runs += 1
     dt = (time.perf_counter() - t0) / runs
+    t1 = time.perf_counter()
+    step(1)
+    dt1 = time.perf_counter() - t1
     step_bytes = batch.decode_bytes() + batch.write_bytes()
     return {"value": step_bytes / dt / 1e12, "unit": "TB/s", "cores": cores, "kind": "oracle",
             "sample": "the whole %s step for one layer (%d appended rows, %d query rows x %d heads over %d "
-                      "sequences), %d runs" % (batch.name, batch.num_rows, batch.num_rows, batch.num_heads,
-                                               batch.num_seqs, runs),
-            "seconds_per_step": dt, "seqs_per_s_per_layer": batch.num_seqs / dt}
+                      "sequences), %d runs on %d threads (%.1f s), then one run on 1 thread" % (
+                          batch.name, batch.num_rows, batch.num_rows, batch.num_heads, batch.num_seqs, runs, cores,
+                          dt * runs),
+            "seconds_per_step": dt, "seqs_per_s_per_layer": batch.num_seqs / dt,
+            "one_core": {"value": step_bytes / dt1 / 1e12, "unit": "TB/s", "cores": 1, "seconds_per_step": dt1,
+                         "seqs_per_s_per_layer": batch.num_seqs / dt1}}
 
 
-def measure(batch, dev, layers, steps, warmup, partition_size=0, fused=False, graph=False):
-    """Fill the pools, time `steps` steps after `warmup` untimed ones, then time each kernel of
-    the step alone; returns the result fields for this workload.  fused: decode rows append
-    their new token inside the decode call (pa_paged_attention_decode_append); otherwise every
-    new row goes through pa_kv_cache_write first.  graph: also time the step captured in HIP
-    graphs (one per layer pool) and replayed."""
+def _pct(xs, p):
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), p))
+
+
+def measure(batch, dev, layers, steps, warmup, partitions=(0,), fused=False, graph=False, per_step=50):
+    """Fill the pools; time `steps` steps after `warmup` untimed ones (events only at the two
+    ends of the region); time `per_step` single steps for the distribution; then time each kernel
+    of the step alone.  partitions: the decode's partition sizes, the first one the step's; the
+    others are timed as a sweep.  fused: decode rows append their new token inside the decode
+    call; otherwise every new row goes through pa_kv_cache_write first.  graph: also replay the
+    step from HIP graphs (one per layer pool)."""
     import torch
 
     from paged_kv_cache_461_amd import ops
+    from paged_kv_cache_461_amd import workloads as W
 
     S, Hq, Hkv, D, B = batch.num_seqs, batch.num_heads, batch.num_kv_heads, batch.head_dim, batch.block_size
-    print("# workload %s: %d seqs, ctx %d..%d, pool %.1f MB x2 per layer, %d layers" % (
-        batch.name, S, batch.context_lens.min(), batch.context_lens.max(), batch.pool_bytes / 1e6, layers),
-        file=sys.stderr, flush=True)
+    log("workload %s: %d seqs, ctx %d..%d, pool %.1f MB x2 per layer, %d layers" % (
+        batch.name, S, batch.context_lens.min(), batch.context_lens.max(), batch.pool_bytes / 1e6, layers))
     t0 = time.time()
     pools = fill_pools(batch, layers, dev)
-    print("# pools filled in %.1f s" % (time.time() - t0), file=sys.stderr, flush=True)
+    log("pools filled in %.1f s" % (time.time() - t0))
 
     # Rows of sequences with more than one query row go to the chunked-prefill call; the
     # decode sequences (one row each) follow them and go to the decode call.
@@ -257,10 +298,11 @@ def measure(batch, dev, layers, steps, warmup, partition_size=0, fused=False, gr
     tables = torch.from_numpy(batch.block_tables).to(dev)
     ctx = torch.from_numpy(batch.context_lens).to(dev)
     cu = torch.from_numpy(batch.cu_query_lens).to(dev)
-    P = partition_size
     Sd = S - Sp
     dec_max_ctx = int(batch.context_lens[Sp:].max()) if Sd else 0
-    ws = ops.decode_workspace(Sd, Hq, Hkv, D, dec_max_ctx, B, P, device=dev) if Sd else None
+    wss = {P: (ops.decode_workspace(Sd, Hq, Hkv, D, dec_max_ctx, B, P, device=dev) if Sd else None)
+           for P in partitions}
+    part = [partitions[0]]  # the partition the step uses
     pf_max_q = int(ql[:Sp].max()) if Sp else 0
     pf_max_ctx = int(batch.context_lens[:Sp].max()) if Sp else 0
     pf_ws = ops.chunked_prefill_workspace(Rp, Sp, pf_max_q, Hq, Hkv, D, pf_max_ctx, B, 0, device=dev) if Sp else None
@@ -291,8 +333,9 @@ def measure(batch, dev, layers, steps, warmup, partition_size=0, fused=False, gr
 
     def decode(r, phase=3):
         kp, vp, (nk, nv, _), q, ks, vs = pools[r % len(pools)]
+        P = part[0]
         common = dict(max_context_len=dec_max_ctx, num_kv_heads=Hkv, scale=batch.scale, block_size=B, k_scale=ks,
-                      v_scale=vs, partition_size=P, workspace=ws, phase=phase, stream=cur[0])
+                      v_scale=vs, partition_size=P, workspace=wss[P], phase=phase, stream=cur[0])
         if fused:
             ops.paged_attention_decode_append(outs[r % len(pools)][Rp:], q[Rp:], nk[Rp:].view(Sd, Hkv, D),
                                               nv[Rp:].view(Sd, Hkv, D), kp, vp, tables[Sp:], ctx[Sp:], **common)
@@ -308,25 +351,52 @@ def measure(batch, dev, layers, steps, warmup, partition_size=0, fused=False, gr
         if Sd:
             decode(i)
 
+    def region(fn, n):
+        """n calls of fn(i) between two HIP events on the launch stream, synchronised on both sides;
+        ms per call."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    def single_steps(n):
+        """n steps with an event between consecutive steps: the per-step times (us)."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i in range(n):
+            step(i)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n)]
+
+    def dist(xs):
+        return {"median": round(_pct(xs, 50), 2), "p10": round(_pct(xs, 10), 2), "p90": round(_pct(xs, 90), 2),
+                "n": len(xs)}
+
+    def launches(fn, reps):
+        """fn(r) launched reps times back to back between two HIP events, after one untimed launch
+        (so the first timed one does not wait for the host); us per launch.  Each figure includes
+        the gap between back-to-back launches, so it bounds the kernel's own duration from above."""
+        fn(reps)
+        return region(fn, reps) * 1e3
+
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region: exactly K steps, events only at its two ends (an event between kernels
-    # adds a gap to the step, so the per-kernel breakdown is taken in a second pass below).
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(steps):
-        step(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / steps
+    # Timed region: exactly K steps, events only at its two ends.
+    ms_per_step = region(step, steps)
+    step_times = single_steps(max(per_step, 1))
 
     graph_res = None
     if graph:
-        # The same K steps replayed from HIP graphs: one graph per layer pool, each holding one
-        # whole step (its launches record no memset and allocate nothing).
+        # The same steps replayed from HIP graphs: one graph per layer pool, each holding one whole
+        # step (the library's launches record no memset and allocate nothing).
         graphs = []
         side = torch.cuda.Stream()
         side.wait_stream(stream)
@@ -342,50 +412,26 @@ def measure(batch, dev, layers, steps, warmup, partition_size=0, fused=False, gr
         torch.cuda.synchronize()
         for i in range(max(warmup, 1)):
             graphs[i % len(graphs)].replay()
-        torch.cuda.synchronize()
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        g0.record(stream)
-        for i in range(steps):
-            graphs[i % len(graphs)].replay()
-        g1.record(stream)
-        torch.cuda.synchronize()
-        gms = g0.elapsed_time(g1) / steps
-        graph_res = {"ms_per_step": round(gms, 5), "value": None, "replays": steps,
-                     "what": "the same steps replayed from HIP graphs (one per layer pool)"}
-
-    # Profiled pass: each kernel of the step launched K times back to back (cycling the layer
-    # pools as in the step) between two HIP events on the launch stream; the average is the
-    # kernel's launch duration plus the inter-kernel gap, with no event inside a launch pair.
-    # One untimed launch goes first, so the first timed one does not wait for the host.
-    def launches(fn, reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        fn(reps)
-        e0.record(stream)
-        for r in range(reps):
-            fn(r)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / reps  # us
-
-    from paged_kv_cache_461_amd import workloads as W
+        gms = region(lambda i: graphs[i % len(graphs)].replay(), steps)
+        graph_res = {"ms_per_step": round(gms, 5), "eager_ms_per_step": round(ms_per_step, 5), "replays": steps,
+                     "what": "the same steps replayed from HIP graphs (one per layer pool), against eager launches"}
 
     kernels = {"kv_write": round(launches(write, steps), 2)} if Rw else {}
     if Sp:
         kernels["chunked_prefill"] = round(launches(prefill, steps), 2)
     if Sd:
         kernels["decode_stream"] = round(launches(lambda r: decode(r, 1), steps), 2)
-        if ws is not None:  # no workspace: one chunk per run, the merge phase launches nothing
+        if wss[part[0]] is not None:  # no workspace: one chunk per run, the merge phase launches nothing
             kernels["decode_merge"] = round(launches(lambda r: decode(steps - 1, 2), steps), 2)
-    kernels["timing"] = ("K back-to-back launches of each kernel between two HIP events on the launch stream, "
-                         "after the timed region" + ("; decode_stream includes the fused append of the decode "
-                                                     "rows' new tokens" if fused and Sd else ""))
+        kernels["decode_call"] = round(launches(lambda r: decode(r, 3), steps), 2)
+    kernels["timing"] = ("each kernel (decode_call: streaming + merge) launched K times back to back between two "
+                         "HIP events on the launch stream, after the timed region; upper bounds of the kernels' own "
+                         "durations (each includes the gap between back-to-back launches)"
+                         + ("; decode_stream includes the fused append of the decode rows' new tokens"
+                            if fused and Sd else ""))
 
     step_bytes = batch.decode_bytes() + batch.write_bytes()
     value = step_bytes / (ms_per_step * 1e-3) / 1e12
-    if graph_res is not None:
-        graph_res["value"] = round(step_bytes / (graph_res["ms_per_step"] * 1e-3) / 1e12, 4)
-        graph_res["seqs_per_s_per_layer"] = round(S / (graph_res["ms_per_step"] * 1e-3), 1)
     digest = source_digest("decode")
     eq = W.ELEM_BYTES[batch.q_dtype]
     res = {
@@ -399,7 +445,7 @@ def measure(batch, dev, layers, steps, warmup, partition_size=0, fused=False, gr
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": W.DTYPE_NAMES[batch.q_dtype],
         "data": "synthetic",
         "config": {
             "workload": batch.name, "num_seqs": S, "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
@@ -407,32 +453,59 @@ def measure(batch, dev, layers, steps, warmup, partition_size=0, fused=False, gr
             "context_lens": "seeded, %d..%d, sum %d" % (
                 batch.context_lens.min(), batch.context_lens.max(), int(batch.context_lens.sum())),
             "num_blocks": batch.num_blocks, "layers_cycled": layers,
-            "partition_size": "auto (equal chunks per wave)" if P == 0 else P,
+            "partition_size": "auto (equal chunks per wave)" if part[0] == 0 else part[0],
             "append": "fused into the decode call" if fused and Sd else "pa_kv_cache_write",
             "shared_block_hint": shared is not None,
         },
         "frac_of_hbm_peak": round(value * 1e3 / HBM_PEAK_GBS, 4),
         "seqs_per_s_per_layer": round(S / (ms_per_step * 1e-3), 1),
         "step_bytes": int(step_bytes),
+        "step_us": dict(dist(step_times), what="single steps, an event between consecutive steps"),
         "kernels_us": kernels,
     }
     if graph_res is not None:
+        graph_res["value"] = round(step_bytes / (graph_res["ms_per_step"] * 1e-3) / 1e12, 4)
+        graph_res["seqs_per_s_per_layer"] = round(S / (graph_res["ms_per_step"] * 1e-3), 1)
         res["graph_step"] = graph_res
     if Sp:
         res["config"]["prefill_rows"] = Rp
     if Sd:
-        # decode kernel: KV of the decode sequences + their queries + tables + lengths (+ scales)
+        # decode: KV of the decode sequences (a block shared by several sequences counted once) +
+        # their queries + tables + lengths (+ scales); the output rows are written by the decode call
         dec = dataclasses.replace(batch, context_lens=batch.context_lens[Sp:], query_lens=ql[Sp:],
                                   block_tables=batch.block_tables[Sp:])
-        part_bytes = dec.decode_bytes() - dec.num_rows * Hq * D * eq
+        out_bytes = dec.num_rows * Hq * D * eq
+        part_bytes = dec.decode_bytes() - out_bytes
         if fused:
             part_bytes += dec.write_bytes() - 8 * dec.num_rows  # appended rows (no slot ids: the table gives them)
         achieved = part_bytes / (kernels["decode_stream"] * 1e-6) / 1e9
         res["roofline"] = {"bound": "hbm", "kernel": "decode_stream_kernel" + (" (fused append)" if fused else ""),
-                           "achieved": round(achieved, 1),
-                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                           "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(achieved / HBM_PEAK_GBS, 4),
                            "traffic": stored_traffic(traffic_key(batch, fused), digest),
                            "algorithmic_bytes_per_launch": int(part_bytes), "source_digest": digest}
+        if len(dec.sharing) > 1:
+            res["roofline"]["logical_bytes_per_launch"] = int(dec.decode_bytes(unique=False) - out_bytes)
+        call_bytes = part_bytes + out_bytes
+        call_gbs = call_bytes / (kernels["decode_call"] * 1e-6) / 1e9
+        res["roofline_decode_call"] = {
+            "bound": "hbm", "kernel": "decode call: streaming kernel + split-K merge kernel", "achieved": round(call_gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(call_gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_launch": int(call_bytes)}
+        sweep = {}
+        for P in partitions[1:]:
+            part[0] = P
+            decode(0)
+            st = single_steps(max(per_step, 1))
+            d_call = launches(lambda r: decode(r, 3), steps)
+            d_stream = launches(lambda r: decode(r, 1), steps)
+            sweep[str(P)] = {"step_us": dist(st), "decode_call_us": round(d_call, 2),
+                             "decode_stream_us": round(d_stream, 2),
+                             "decode_call_frac": round(call_bytes / (d_call * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                             "decode_stream_frac": round(part_bytes / (d_stream * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        part[0] = partitions[0]
+        if sweep:
+            res["partition_sweep"] = sweep
     if Sp:
         pos = [np.arange(c - q, c, dtype=np.int64) for c, q in zip(batch.context_lens[:Sp], ql[:Sp])]
         visible = int(sum(int((p + 1).sum()) for p in pos))  # (row, key) pairs of the causal chunks
@@ -445,6 +518,9 @@ def measure(batch, dev, layers, steps, warmup, partition_size=0, fused=False, gr
                                    "algorithmic_flops_per_launch": flops, "source_digest": source_digest("prefill")}
     if "roofline" not in res:
         res["roofline"] = dict(res["roofline_prefill"])
+    del pools, outs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     return res, stream
 
 
@@ -455,8 +531,8 @@ def main():
               "sequences and KV heads shard across GPUs with no exchange inside attention, so the "
               "one-GPU figure is the per-GPU figure." % args.gpus, file=sys.stderr)
         sys.exit(2)
-    if args.layers < 1 or args.steps < 1 or args.warmup < 0:
-        sys.exit("--layers and --steps must be >= 1, --warmup >= 0")
+    if args.layers < 0 or args.steps < 1 or args.warmup < 0:
+        sys.exit("--layers must be >= 0, --steps >= 1, --warmup >= 0")
 
     import torch
 
@@ -471,24 +547,38 @@ def main():
     ops.library()  # fails loudly if the HIP library is missing
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    batch = make_batch(args.workload, args.block_size)
-    fused = args.fused_append
-    res, stream = measure(batch, dev, args.layers, args.steps, args.warmup, args.partition_size, fused, args.graph)
-    if args.extra_workload != "none" and args.extra_workload != args.workload:
-        # The rest of the hot path in the same run: the fp8 cache (in-kernel dequant) and the
-        # chunked-prefill kernel, on the mixed step (one layer).
-        extra = make_batch(args.extra_workload, args.block_size)
-        xres, _ = measure(extra, dev, 1, args.steps, min(args.warmup, 2), 0, fused)
-        keep = ("value", "unit", "ms_per_step", "steps", "warmup", "config", "seqs_per_s_per_layer", "step_bytes",
-                "kernels_us", "roofline", "roofline_prefill")
-        res["extra_step"] = {k: xres[k] for k in keep if k in xres}
+    t_start = time.time()
+
+    def run(name, headline):
+        batch = make_batch(name, args.block_size)
+        layers = args.layers if (headline and args.layers) else LAYERS.get(name, 2)
+        parts = PARTITIONS.get(name, (0,))
+        if headline and args.partition_size >= 0:
+            parts = (args.partition_size,)
+        graph = (args.graph and headline) or name == "tiny_fp32"
+        return measure(batch, dev, layers, args.steps, args.warmup, parts, args.fused_append and headline, graph,
+                       args.per_step)
+
+    res, stream = run(args.workload, True)
+    extra = [] if args.extra == "none" else [w for w in args.extra.split(",") if w and w != args.workload]
+    keep = ("value", "unit", "ms_per_step", "steps", "warmup", "config", "frac_of_hbm_peak", "seqs_per_s_per_layer",
+            "step_bytes", "step_us", "kernels_us", "roofline", "roofline_decode_call", "roofline_prefill",
+            "partition_sweep", "graph_step", "dtype")
+    if extra:
+        res["workloads"] = {}
+    for name in extra:
+        if name not in WORKLOAD_NAMES:
+            sys.exit("unknown workload %s" % name)
+        xres, _ = run(name, False)
+        res["workloads"][name] = {k: xres[k] for k in keep if k in xres}
     probe = read_probe(stream)
     res["hbm_read_probe"] = probe
     if res["roofline"]["bound"] == "hbm":
         res["roofline"]["frac_of_probe"] = round(res["roofline"]["achieved"] / probe["achieved"], 4)
     if not args.no_cpu_baseline:
-        print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(batch)
+        log("cpu baseline (oracle) ...")
+        res["cpu_baseline"] = cpu_baseline(make_batch(args.workload, args.block_size))
+    log("bench done in %.1f s" % (time.time() - t_start))
     print(json.dumps(res), flush=True)
 
 

@@ -17,7 +17,8 @@
  *   - the cache may be stored as 8-bit floats, E4M3 or E5M2, with per-head scales (page 1,
  *     section 15; page 2, quantisation, which also names per-tensor scales -- pass one value
  *     repeated per head; page 3, section 2.4, which prefers E4M3 because E5M2 can drift on
- *     long sequences);
+ *     long sequences), or as 8-bit integers (page 4, section 4.5, step 4: the KV cache brought
+ *     from FP16 down to INT8; page 2, quantisation, KV-cache quantisation);
  *   - a long prompt may be processed in chunks that run alongside decode rows (page 1,
  *     section 12; page 3, section 2.3).
  *
@@ -42,7 +43,9 @@
  * Element types (pa_dtype):  PA_F32 IEEE binary32; PA_BF16 bfloat16; PA_FP8_E4M3 the OCP
  * 8-bit float E4M3 (bias 7, no infinities, S.1111.111 = NaN, largest finite 448);
  * PA_FP8_E5M2 the OCP 8-bit float E5M2 (bias 15, S.11111.00 = +-inf, S.11111.mm with mm != 0
- * = NaN, largest finite 57344).
+ * = NaN, largest finite 57344); PA_INT8 a two's-complement 8-bit integer code.  The three 8-bit
+ * types are "quantised" caches: the cached value is code * scale with one fp32 scale per kv
+ * head (k_scale for K, v_scale for V).
  *
  * Pool layout.  k_pool and v_pool are each [num_blocks][num_kv_heads][block_size*head_dim]
  * elements of cache_dtype.  With e = element bytes, W = 64/e and T = min(16/e, block_size),
@@ -60,7 +63,7 @@
  * block size against fragmentation and access efficiency: page 2, the PagedAttention section;
  * the append takes any block size the layout allows); num_heads / num_kv_heads in
  * {1, 2, 4, 8}; (q dtype, cache dtype) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3),
- * (BF16, FP8_E5M2)};
+ * (BF16, FP8_E5M2), (BF16, INT8)};
  * up to 16384 sequences per decode call; chunked prefill with BF16 queries only.
  * Anything else returns PA_ERR_UNSUPPORTED.
  */
@@ -83,7 +86,7 @@ typedef enum {
     PA_ERR_NO_BLOCKS = 5    /* the block manager has no free or evictable block left      */
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2, PA_FP8_E5M2 = 3 } pa_dtype;
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2, PA_FP8_E5M2 = 3, PA_INT8 = 4 } pa_dtype;
 
 /*
  * Paged KV append (the step that stores each new token's K and V in its block slot).
@@ -92,12 +95,14 @@ typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2, PA_FP8_E5M2 = 3 } pa_dt
  *   slot_mapping   device int64 [num_tokens]; token i goes to physical block
  *                  slot / block_size at offset slot % block_size.  A negative slot skips the
  *                  token; a slot >= num_blocks*block_size is also skipped.
- *   k_scale, v_scale  device fp32 [num_kv_heads] for an fp8 cache, else NULL.
+ *   k_scale, v_scale  device fp32 [num_kv_heads] for a quantised cache, else NULL.
  * src_dtype == cache_dtype copies the bits.  A BF16 or F32 source into an FP8_E4M3 cache
  * stores e4m3(fl32(x / scale[h])): one binary32 division (round to nearest even), then
  * round-to-nearest-even to E4M3 saturating at +-448, NaN kept as NaN with its sign.  An
  * FP8_E5M2 cache stores e5m2(fl32(x / scale[h])) by the same rule, saturating at +-57344
- * (infinities included) and storing NaN as S.11111.11.  Only
+ * (infinities included) and storing NaN as S.11111.11.  An INT8 cache stores the nearest
+ * integer to fl32(x / scale[h]) (ties to even), saturated to [-127, 127] (the symmetric
+ * range; infinities saturate), NaN stored as 0.  Only
  * the addressed slots are written; every other byte of the pools is left unchanged.  Slots
  * must be distinct within one call.
  */
@@ -130,7 +135,7 @@ int64_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t nu
  *   max_context_len  host bound on context_lens (sizes the launch and the workspace).
  *   scale          softmax scale applied to q.k (1/sqrt(head_dim) for standard attention);
  *                  positive and finite, else PA_ERR_INVALID_ARG.
- *   k_scale, v_scale device fp32 [num_kv_heads] for an fp8 cache (the stored code times
+ *   k_scale, v_scale device fp32 [num_kv_heads] for a quantised cache (the stored code times
  *                  the scale is the cached value), else NULL.  Exactly num_kv_heads values are
  *                  read from each; a per-tensor scale is passed repeated per head.
  *   partition_size 0 = automatic, else a multiple of block_size.  The work is the list of
@@ -198,7 +203,7 @@ int64_t pa_chunked_prefill_workspace_size(int32_t num_query_rows, int32_t num_se
  *   out            device [num_query_rows][num_heads][head_dim] bf16 (written).
  *   query          device [num_query_rows][num_heads][head_dim] bf16.
  *   q_dtype        PA_BF16 (the products run on bf16 matrix cores with fp32 accumulation; an
- *                  fp8 cache is widened to bf16 exactly).  Other types: PA_ERR_UNSUPPORTED.
+ *                  fp8 or INT8 cache is widened to bf16 exactly).  Other types: PA_ERR_UNSUPPORTED.
  *   cu_query_lens  device int32 [num_seqs + 1], non-decreasing, cu_query_lens[0] = 0 and
  *                  cu_query_lens[num_seqs] = num_query_rows.  A sequence whose rows fall
  *                  outside [0, num_query_rows) is skipped.

@@ -42,11 +42,13 @@ int elem_bytes(int32_t dt)
     case PA_BF16: return 2;
     case PA_FP8_E4M3: return 1;
     case PA_FP8_E5M2: return 1;
+    case PA_INT8: return 1;
     default: return 0;
     }
 }
 
-bool is_fp8(int32_t dt) { return dt == PA_FP8_E4M3 || dt == PA_FP8_E5M2; }
+// A quantised cache: 8-bit codes (OCP E4M3 / E5M2 floats or INT8) times per-head scales.
+bool is_quant(int32_t dt) { return dt == PA_FP8_E4M3 || dt == PA_FP8_E5M2 || dt == PA_INT8; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -121,7 +123,7 @@ int32_t check_decode_shape(int32_t num_seqs, int32_t num_heads, int32_t num_kv_h
                     num_kv_heads, head_dim, block_size, max_context_len, partition_size);
     if (num_heads % num_kv_heads)
         return fail(PA_ERR_INVALID_ARG, "num_heads %d is not a multiple of num_kv_heads %d", num_heads, num_kv_heads);
-    if (!elem_bytes(q_dtype) || !elem_bytes(cache_dtype) || is_fp8(q_dtype))
+    if (!elem_bytes(q_dtype) || !elem_bytes(cache_dtype) || is_quant(q_dtype))
         return fail(PA_ERR_INVALID_ARG, "unknown dtype (q %d, cache %d)", q_dtype, cache_dtype);
     const int32_t g = num_heads / num_kv_heads;
     if (g != 1 && g != 2 && g != 4 && g != 8)
@@ -129,11 +131,11 @@ int32_t check_decode_shape(int32_t num_seqs, int32_t num_heads, int32_t num_kv_h
     if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
     if (block_size != 8 && block_size != 16 && block_size != 32)
         return fail(PA_ERR_UNSUPPORTED, "block_size %d (supported: 8, 16, 32)", block_size);
-    if (block_size == 8 && is_fp8(cache_dtype))
-        return fail(PA_ERR_UNSUPPORTED, "8-token blocks need a 16- or 32-bit cache (an fp8 V group of 8 tokens "
+    if (block_size == 8 && is_quant(cache_dtype))
+        return fail(PA_ERR_UNSUPPORTED, "8-token blocks need a 16- or 32-bit cache (an 8-bit V group of 8 tokens "
                     "does not fill the kernels' 16-byte V pieces)");
     const bool combo = (q_dtype == PA_F32 && cache_dtype == PA_F32) || (q_dtype == PA_BF16 && cache_dtype == PA_BF16) ||
-                       (q_dtype == PA_BF16 && is_fp8(cache_dtype));
+                       (q_dtype == PA_BF16 && is_quant(cache_dtype));
     if (!combo) return fail(PA_ERR_UNSUPPORTED, "(q dtype %d, cache dtype %d) not supported", q_dtype, cache_dtype);
     if (partition_size > 0 && partition_size % block_size)
         return fail(PA_ERR_INVALID_ARG, "partition_size %d is not a multiple of block_size %d", partition_size, block_size);
@@ -244,9 +246,9 @@ int32_t pa_kv_cache_write(const void* key, const void* value, int32_t src_dtype,
         return fail(PA_ERR_INVALID_ARG, "negative or zero size (num_tokens=%d num_kv_heads=%d head_dim=%d "
                     "block_size=%d num_blocks=%lld)", num_tokens, num_kv_heads, head_dim, block_size,
                     (long long)num_blocks);
-    if (!elem_bytes(src_dtype) || !elem_bytes(cache_dtype) || is_fp8(src_dtype))
+    if (!elem_bytes(src_dtype) || !elem_bytes(cache_dtype) || is_quant(src_dtype))
         return fail(PA_ERR_INVALID_ARG, "unknown dtype (src %d, cache %d)", src_dtype, cache_dtype);
-    if (!(src_dtype == cache_dtype || is_fp8(cache_dtype)))
+    if (!(src_dtype == cache_dtype || is_quant(cache_dtype)))
         return fail(PA_ERR_UNSUPPORTED, "append from dtype %d into a dtype %d cache", src_dtype, cache_dtype);
     if (head_dim % (64 / elem_bytes(cache_dtype)) || head_dim % (16 / elem_bytes(src_dtype)))
         return fail(PA_ERR_UNSUPPORTED, "head_dim %d is not a whole number of 64-byte cache slices", head_dim);
@@ -261,11 +263,11 @@ int32_t pa_kv_cache_write(const void* key, const void* value, int32_t src_dtype,
                     value, k_pool, v_pool, (const void*)slot_mapping);
     if (!aligned16(key) || !aligned16(value) || !aligned16(k_pool) || !aligned16(v_pool))
         return fail(PA_ERR_INVALID_ARG, "key, value and pools must be 16-byte aligned");
-    if (is_fp8(cache_dtype) && (!k_scale || !v_scale))
-        return fail(PA_ERR_INVALID_ARG, "an fp8 cache needs k_scale and v_scale");
+    if (is_quant(cache_dtype) && (!k_scale || !v_scale))
+        return fail(PA_ERR_INVALID_ARG, "a quantised (fp8 / INT8) cache needs k_scale and v_scale");
     pa::KvWriteArgs a{key, value, k_pool, v_pool, num_blocks, slot_mapping, num_tokens, num_kv_heads, head_dim,
-                      block_size, is_fp8(cache_dtype) ? k_scale : nullptr,
-                      is_fp8(cache_dtype) ? v_scale : nullptr};
+                      block_size, is_quant(cache_dtype) ? k_scale : nullptr,
+                      is_quant(cache_dtype) ? v_scale : nullptr};
     hipError_t e = pa::launch_kv_write(src_dtype, cache_dtype, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(PA_ERR_HIP, "kv_cache_write launch: %s", hipGetErrorString(e));
     return ok();
@@ -369,8 +371,8 @@ int32_t decode_call(int32_t phase, void* out, const void* query, int32_t q_dtype
                     (const void*)context_lens);
     if (!aligned16(query) || !aligned16(k_pool) || !aligned16(v_pool))
         return fail(PA_ERR_INVALID_ARG, "query and pools must be 16-byte aligned");
-    if (is_fp8(cache_dtype) && (!k_scale || !v_scale))
-        return fail(PA_ERR_INVALID_ARG, "an fp8 cache needs k_scale and v_scale");
+    if (is_quant(cache_dtype) && (!k_scale || !v_scale))
+        return fail(PA_ERR_INVALID_ARG, "a quantised (fp8 / INT8) cache needs k_scale and v_scale");
     if (!(scale > 0.0f && scale <= 3.402823466e38f))
         return fail(PA_ERR_INVALID_ARG, "scale %g: the softmax scale must be positive and finite", (double)scale);
     if ((new_key == nullptr) != (new_value == nullptr))
@@ -397,7 +399,7 @@ int32_t decode_call(int32_t phase, void* out, const void* query, int32_t q_dtype
         if (reinterpret_cast<uintptr_t>(workspace) % kWorkspaceAlign)
             return fail(PA_ERR_WORKSPACE, "workspace must be %d-byte aligned", (int)kWorkspaceAlign);
     }
-    const bool fp8 = is_fp8(cache_dtype);
+    const bool quant = is_quant(cache_dtype);
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     pa::DecodeArgs a{};
     a.out = out;
@@ -417,8 +419,8 @@ int32_t decode_call(int32_t phase, void* out, const void* query, int32_t q_dtype
     a.num_kv_heads = num_kv_heads;
     a.block_size = block_size;
     a.scale_log2 = scale * 1.4426950408889634f;
-    a.k_scale = fp8 ? k_scale : nullptr;
-    a.v_scale = fp8 ? v_scale : nullptr;
+    a.k_scale = quant ? k_scale : nullptr;
+    a.v_scale = quant ? v_scale : nullptr;
     a.chunk_blocks = pl.chunk_blocks;
     a.grid_workgroups = pl.grid_workgroups;
     a.max_chunks = pl.max_chunks;
@@ -483,6 +485,10 @@ int32_t pa_paged_attention_decode_append(int32_t phase, void* out, const void* q
                        head_dim, block_size, scale, k_scale, v_scale, partition_size, workspace, workspace_bytes,
                        stream);
 }
+
+}  // extern "C"
+
+extern "C" {
 
 int64_t pa_decode_noalloc_max_workspace(void) { return kNoAllocScratchBytes; }
 
@@ -553,8 +559,8 @@ int32_t pa_paged_attention_chunked_prefill(void* out, const void* query, int32_t
                     (const void*)block_tables, (const void*)context_lens);
     if (!aligned16(query) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool))
         return fail(PA_ERR_INVALID_ARG, "query, out and pools must be 16-byte aligned");
-    if (is_fp8(cache_dtype) && (!k_scale || !v_scale))
-        return fail(PA_ERR_INVALID_ARG, "an fp8 cache needs k_scale and v_scale");
+    if (is_quant(cache_dtype) && (!k_scale || !v_scale))
+        return fail(PA_ERR_INVALID_ARG, "a quantised (fp8 / INT8) cache needs k_scale and v_scale");
     if (!(scale > 0.0f && scale <= 3.402823466e38f))
         return fail(PA_ERR_INVALID_ARG, "scale %g: the softmax scale must be positive and finite", (double)scale);
     const PrefillPlan pl = plan_prefill(num_query_rows, num_seqs, max_query_len, num_heads, num_kv_heads, head_dim,
@@ -569,7 +575,7 @@ int32_t pa_paged_attention_chunked_prefill(void* out, const void* query, int32_t
             return fail(PA_ERR_WORKSPACE, "workspace must be %d-byte aligned", (int)kWorkspaceAlign);
     }
     if (pl.grid == 0) return ok();
-    const bool fp8 = is_fp8(cache_dtype);
+    const bool quant = is_quant(cache_dtype);
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     pa::PrefillArgs a{};
     a.out = out;
@@ -591,8 +597,8 @@ int32_t pa_paged_attention_chunked_prefill(void* out, const void* query, int32_t
     a.num_splits = pl.num_splits;
     a.split_keys = pl.split_keys;
     a.scale_log2 = scale * 1.4426950408889634f;
-    a.k_scale = fp8 ? k_scale : nullptr;
-    a.v_scale = fp8 ? v_scale : nullptr;
+    a.k_scale = quant ? k_scale : nullptr;
+    a.v_scale = quant ? v_scale : nullptr;
     a.o_part = pl.total > 0 ? reinterpret_cast<float*>(ws) : nullptr;
     a.ml_part = pl.total > 0 ? reinterpret_cast<float*>(ws + pl.o_bytes) : nullptr;
     hipError_t e = pa::launch_prefill(cache_dtype, head_dim, num_heads / num_kv_heads, a, pl.grid,

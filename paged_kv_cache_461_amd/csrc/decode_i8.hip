@@ -1,0 +1,11 @@
+// decode_i8.hip -- decode instances for bf16 queries over an INT8 cache (streaming and merge kernels).
+#include "decode_launch.hpp"
+
+namespace pa {
+
+hipError_t launch_decode_i8(int phase, int head_dim, int gqa, const DecodeArgs& a, hipStream_t stream)
+{
+    return launch_d<kBF16, kI8>(phase, head_dim, gqa, a, stream);
+}
+
+}  // namespace pa

@@ -82,7 +82,7 @@ struct Acc {
 template <int QT, int KT, int D, int G>
 struct QRegs {
     using S = Shape<QT, KT, D, G>;
-    static constexpr int NQW = kIsFp8<KT> ? 8 : 4;  // dwords per (slice, head)
+    static constexpr int NQW = kIsQuant<KT> ? 8 : 4;  // dwords per (slice, head)
     uint32_t w[S::NCH][G][NQW];
 };
 
@@ -158,15 +158,15 @@ __device__ __forceinline__ void qk_slice(const QSrc& q, int kp, int c, const uin
             acc[h] = dot2_bf16(kv.y, qw[1], acc[h]);
             acc[h] = dot2_bf16(kv.z, qw[2], acc[h]);
             acc[h] = dot2_bf16(kv.w, qw[3], acc[h]);
-        } else if constexpr (kIsFp8<KT>) {
-            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, false>(kv.x), qw[0], acc[h]);
-            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, true>(kv.x), qw[1], acc[h]);
-            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, false>(kv.y), qw[2], acc[h]);
-            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, true>(kv.y), qw[3], acc[h]);
-            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, false>(kv.z), qw[4], acc[h]);
-            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, true>(kv.z), qw[5], acc[h]);
-            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, false>(kv.w), qw[6], acc[h]);
-            acc[h] = dot2_bf16(fp8x2_to_bf16x2<KT, true>(kv.w), qw[7], acc[h]);
+        } else if constexpr (kIsQuant<KT>) {
+            acc[h] = dot2_bf16(q8x2_to_bf16x2<KT, false>(kv.x), qw[0], acc[h]);
+            acc[h] = dot2_bf16(q8x2_to_bf16x2<KT, true>(kv.x), qw[1], acc[h]);
+            acc[h] = dot2_bf16(q8x2_to_bf16x2<KT, false>(kv.y), qw[2], acc[h]);
+            acc[h] = dot2_bf16(q8x2_to_bf16x2<KT, true>(kv.y), qw[3], acc[h]);
+            acc[h] = dot2_bf16(q8x2_to_bf16x2<KT, false>(kv.z), qw[4], acc[h]);
+            acc[h] = dot2_bf16(q8x2_to_bf16x2<KT, true>(kv.z), qw[5], acc[h]);
+            acc[h] = dot2_bf16(q8x2_to_bf16x2<KT, false>(kv.w), qw[6], acc[h]);
+            acc[h] = dot2_bf16(q8x2_to_bf16x2<KT, true>(kv.w), qw[7], acc[h]);
         } else {
             acc[h] = __builtin_fmaf(as_float(kv.x), as_float(qw[0]), acc[h]);
             acc[h] = __builtin_fmaf(as_float(kv.y), as_float(qw[1]), acc[h]);
@@ -194,12 +194,12 @@ __device__ __forceinline__ void pv_load(Acc<QT, KT, D, G>& st, int c, const uint
             st.o[cg][h] = dot2_bf16(vv.z, pps[h][q * 4 + 2], st.o[cg][h]);
             st.o[cg][h] = dot2_bf16(vv.w, pps[h][q * 4 + 3], st.o[cg][h]);
         }
-    } else if constexpr (kIsFp8<KT>) {
+    } else if constexpr (kIsQuant<KT>) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const uint32_t w = u4_get(vv, i);
-            const uint32_t lo = fp8x2_to_bf16x2<KT, false>(w);
-            const uint32_t hi = fp8x2_to_bf16x2<KT, true>(w);
+            const uint32_t lo = q8x2_to_bf16x2<KT, false>(w);
+            const uint32_t hi = q8x2_to_bf16x2<KT, true>(w);
 #pragma unroll
             for (int h = 0; h < G; h++) {
                 st.o[cg][h] = dot2_bf16(lo, pps[h][2 * i], st.o[cg][h]);
@@ -484,7 +484,7 @@ __device__ __forceinline__ void stage_new_row(const DecodeArgs& a, int s, int g,
                                    (((int64_t)s * a.num_kv_heads + g) * D + piece * R::N) * R::ES;
         const uint4 raw = load16(src);
         const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
-        const float sc = kIsFp8<KT> && QT != KT ? (kv ? a.v_scale : a.k_scale)[g] : 1.0f;
+        const float sc = kIsQuant<KT> && QT != KT ? (kv ? a.v_scale : a.k_scale)[g] : 1.0f;
         unsigned char* dst = row + kv * R::ROW + piece * R::N * R::EC;
         if constexpr (R::EC == R::ES) {
             *reinterpret_cast<uint4*>(dst) = raw;
@@ -695,7 +695,7 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) voi
         };
         load_query(cc);
         stage_if_run_ends(cc);
-        float c2 = a.scale_log2 * (kIsFp8<KT> ? a.k_scale[cc.g] : 1.0f);
+        float c2 = a.scale_log2 * (kIsQuant<KT> ? a.k_scale[cc.g] : 1.0f);
 
         Acc<QT, KT, D, G> st;
         auto reset = [&]() {
@@ -731,7 +731,7 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) voi
             }
             const int64_t piece = run + k;
             if (whole) {
-                const float vs = kIsFp8<KT> ? a.v_scale[cc.g] : 1.0f;
+                const float vs = kIsQuant<KT> ? a.v_scale[cc.g] : 1.0f;
 #pragma unroll
                 for (int h = 0; h < G; h++) {
                     const float f = st.l[h] > 0.0f ? vs / st.l[h] : 0.0f;
@@ -810,7 +810,7 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) voi
                     if (ta > 0 && cc.j == 0) {       // a new run: start its piece
                         load_query(cc);
                         stage_if_run_ends(cc);
-                        c2 = a.scale_log2 * (kIsFp8<KT> ? a.k_scale[cc.g] : 1.0f);
+                        c2 = a.scale_log2 * (kIsQuant<KT> ? a.k_scale[cc.g] : 1.0f);
                         reset();
                         piece_j0 = 0;
                     }

@@ -29,13 +29,13 @@ __device__ __forceinline__ uint32_t encode_elem(const uint32_t (&words)[4], int 
         else
             return (words[i / 2] >> (16 * (i % 2))) & 0xFFFFu;
     } else {
-        static_assert(kIsFp8<CT>, "conversions go to fp8 only");
+        static_assert(kIsQuant<CT>, "conversions go to 8-bit codes only");
         float x;
         if constexpr (ST == kBF16)
             x = bf16_bits_to_f32((words[i / 2] >> (16 * (i % 2))) & 0xFFFFu);
         else
             x = as_float(words[i]);
-        return f32_to_fp8<CT>(__fdiv_rn(x, scale));
+        return f32_to_q8<CT>(__fdiv_rn(x, scale));
     }
 }
 
@@ -70,7 +70,7 @@ __device__ __forceinline__ void store_kv_piece(const uint4 raw, unsigned char* p
             }
         }
     } else {
-        static_assert(kIsFp8<CT>, "conversions go to fp8 only");
+        static_assert(kIsQuant<CT>, "conversions go to 8-bit codes only");
         uint32_t codes[N];
 #pragma unroll
         for (int i = 0; i < N; i++) codes[i] = encode_elem<ST, CT>(words, i, scale);

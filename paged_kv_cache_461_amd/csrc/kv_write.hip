@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const KvWriteArgs a)
                                (((tok * Hkv + h) * D) + (int64_t)piece * N) * ES;
     const int64_t tile = (blk * Hkv + h) * (int64_t)B * D;  // element offset of the tile
     unsigned char* pool = static_cast<unsigned char*>(kv ? a.v_pool : a.k_pool);
-    const float sc = kIsFp8<CT> && ST != CT ? (kv ? a.v_scale : a.k_scale)[h] : 1.0f;
+    const float sc = kIsQuant<CT> && ST != CT ? (kv ? a.v_scale : a.k_scale)[h] : 1.0f;
     store_kv_piece<ST, CT>(load16(src), pool, tile, piece * N, o, kv, D, B, sc);
 }
 
@@ -66,6 +66,8 @@ hipError_t launch_kv_write(int src_dtype, int cache_dtype, const KvWriteArgs& a,
     if (src_dtype == kF32 && cache_dtype == kFP8) return launch_t<kF32, kFP8>(a, stream);
     if (src_dtype == kBF16 && cache_dtype == kE5M2) return launch_t<kBF16, kE5M2>(a, stream);
     if (src_dtype == kF32 && cache_dtype == kE5M2) return launch_t<kF32, kE5M2>(a, stream);
+    if (src_dtype == kBF16 && cache_dtype == kI8) return launch_t<kBF16, kI8>(a, stream);
+    if (src_dtype == kF32 && cache_dtype == kI8) return launch_t<kF32, kI8>(a, stream);
     return hipErrorInvalidValue;
 }
 

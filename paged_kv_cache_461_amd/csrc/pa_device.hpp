@@ -3,7 +3,8 @@
 // Element conversions and cross-lane primitives, written directly against CDNA4
 // instructions through clang builtins: v_dot2c_f32_bf16, DPP row/quad moves, ds_swizzle,
 // v_exp_f32, v_cvt_scalef32_pk_bf16_fp8 / _bf8 (OCP E4M3 / E5M2 -> bf16 pair),
-// v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 (f32 -> OCP E4M3 / E5M2) and the gfx950 f32 -> bf16 pack.
+// v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 (f32 -> OCP E4M3 / E5M2), v_cvt_f32_i32 with SDWA byte
+// selects (INT8 -> f32), v_rndne_f32 (f32 -> INT8) and the gfx950 f32 -> bf16 pack.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -11,11 +12,16 @@
 
 namespace pa {
 
-// kFP8 is OCP fp8 E4M3, kE5M2 OCP fp8 E5M2 (AMD's "bf8").
-enum Dtype : int { kF32 = 0, kBF16 = 1, kFP8 = 2, kE5M2 = 3 };
+// kFP8 is OCP fp8 E4M3, kE5M2 OCP fp8 E5M2 (AMD's "bf8"), kI8 a two's-complement 8-bit integer
+// code (INT8 cache: value = code * scale).
+enum Dtype : int { kF32 = 0, kBF16 = 1, kFP8 = 2, kE5M2 = 3, kI8 = 4 };
 
 template <int DT>
 constexpr bool kIsFp8 = DT == kFP8 || DT == kE5M2;
+
+// A quantised cache: 8-bit codes times a per-(layer, kv head) scale (fp8 or INT8).
+template <int DT>
+constexpr bool kIsQuant = kIsFp8<DT> || DT == kI8;
 
 template <int DT>
 struct DtypeBytes;
@@ -33,6 +39,10 @@ struct DtypeBytes<kFP8> {
 };
 template <>
 struct DtypeBytes<kE5M2> {
+    static constexpr int value = 1;
+};
+template <>
+struct DtypeBytes<kI8> {
     static constexpr int value = 1;
 };
 
@@ -81,15 +91,28 @@ __device__ __forceinline__ uint32_t e5m2x2_to_bf16x2(uint32_t w)
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HI));
 }
 
-// Two fp8 bytes of cache format KT -> two bf16.
-template <int KT, bool HI>
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w)
+// Two INT8 codes (bytes 0, 1 if !hi, bytes 2, 3 if hi) -> two bf16, exact (every integer in
+// [-128, 127] is a bf16 value): each byte is sign-extended and converted to fp32 in one
+// v_cvt_f32_i32 with an SDWA byte select, then the pair is packed with v_cvt_pk_bf16_f32.
+template <bool HI>
+__device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w)
 {
-    static_assert(kIsFp8<KT>, "fp8 formats only");
+    const float lo = (float)(int8_t)(HI ? (w >> 16) & 0xFFu : w & 0xFFu);
+    const float hi = (float)(int8_t)(HI ? w >> 24 : (w >> 8) & 0xFFu);
+    return pack_bf16x2(lo, hi);
+}
+
+// Two 8-bit codes of quantised cache format KT -> two bf16 (exact for every format).
+template <int KT, bool HI>
+__device__ __forceinline__ uint32_t q8x2_to_bf16x2(uint32_t w)
+{
+    static_assert(kIsQuant<KT>, "8-bit cache formats only");
     if constexpr (KT == kFP8)
         return e4m3x2_to_bf16x2<HI>(w);
-    else
+    else if constexpr (KT == kE5M2)
         return e5m2x2_to_bf16x2<HI>(w);
+    else
+        return i8x2_to_bf16x2<HI>(w);
 }
 
 // fp32 -> OCP E4M3 code: round to nearest even, finite overflow saturates to +-448, NaN
@@ -110,14 +133,25 @@ __device__ __forceinline__ uint32_t f32_to_e5m2(float y)
     return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c, c, 0, false) & 0xFFu;
 }
 
-template <int CT>
-__device__ __forceinline__ uint32_t f32_to_fp8(float y)
+// fp32 -> INT8 code byte: the nearest integer, ties to even (v_rndne_f32), saturated to
+// [-127, 127] (the symmetric range); NaN stores 0.
+__device__ __forceinline__ uint32_t f32_to_i8(float y)
 {
-    static_assert(kIsFp8<CT>, "fp8 formats only");
+    if (__builtin_isnan(y)) return 0u;
+    const float r = __builtin_rintf(__builtin_fminf(__builtin_fmaxf(y, -127.0f), 127.0f));
+    return (uint32_t)(int32_t)r & 0xFFu;
+}
+
+template <int CT>
+__device__ __forceinline__ uint32_t f32_to_q8(float y)
+{
+    static_assert(kIsQuant<CT>, "8-bit cache formats only");
     if constexpr (CT == kFP8)
         return f32_to_e4m3(y);
-    else
+    else if constexpr (CT == kE5M2)
         return f32_to_e5m2(y);
+    else
+        return f32_to_i8(y);
 }
 
 // v_exp_f32: 2^x.

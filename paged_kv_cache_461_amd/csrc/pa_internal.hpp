@@ -111,6 +111,19 @@ hipError_t launch_decode(int phase, int q_dtype, int cache_dtype, int head_dim, 
 hipError_t launch_decode_stream_fused(int q_dtype, int cache_dtype, int head_dim, int gqa, const DecodeArgs& a,
                                       hipStream_t stream);
 
+// Per (query dtype, cache dtype) launchers, one translation unit each (decode_<dtype>.hip and
+// decode_fused_<dtype>.hip).
+hipError_t launch_decode_f32(int phase, int head_dim, int gqa, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_bf16(int phase, int head_dim, int gqa, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_e4m3(int phase, int head_dim, int gqa, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_e5m2(int phase, int head_dim, int gqa, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_i8(int phase, int head_dim, int gqa, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_fused_f32(int head_dim, int gqa, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_fused_bf16(int head_dim, int gqa, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_fused_e4m3(int head_dim, int gqa, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_fused_e5m2(int head_dim, int gqa, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_fused_i8(int head_dim, int gqa, const DecodeArgs& a, hipStream_t stream);
+
 // grid = num_seqs * num_kv_heads * row_blocks * num_splits workgroups.
 hipError_t launch_prefill(int cache_dtype, int head_dim, int gqa, const PrefillArgs& a, int64_t grid,
                           hipStream_t stream);

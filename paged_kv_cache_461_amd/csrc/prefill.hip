@@ -77,14 +77,14 @@ template <int KT, int D>
 __device__ __forceinline__ int k_pos_of_chunk(int c8)
 {
     if constexpr (D != 128) return c8;
-    else if constexpr (kIsFp8<KT>) return 4 * ((c8 & 7) >> 1) + 2 * (c8 >> 3) + (c8 & 1);
+    else if constexpr (kIsQuant<KT>) return 4 * ((c8 & 7) >> 1) + 2 * (c8 >> 3) + (c8 & 1);
     else return 4 * (c8 & 3) + (c8 >> 2);
 }
 template <int KT, int D>
 __device__ __forceinline__ int k_chunk_of_pos(int p)
 {
     if constexpr (D != 128) return p;
-    else if constexpr (kIsFp8<KT>) return 8 * ((p & 3) >> 1) + 2 * (p >> 2) + (p & 1);
+    else if constexpr (kIsQuant<KT>) return 8 * ((p & 3) >> 1) + 2 * (p >> 2) + (p & 1);
     else return 4 * (p & 3) + (p >> 2);
 }
 
@@ -116,7 +116,7 @@ template <int KT, int D, int G, int R, bool B8>
 __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs a)
 {
     using L = PfLds<D>;
-    constexpr int EB = kIsFp8<KT> ? 1 : 2;
+    constexpr int EB = kIsQuant<KT> ? 1 : 2;
     constexpr int TILE_BYTES = kUnitTokens * D * EB;  // one 16-token unit of one kv head
     constexpr int CH_PER_TILE = TILE_BYTES / 16;     // 16-byte pieces per tile
     constexpr int NCH = 4 * CH_PER_TILE / kPrefillThreads;  // K (and V) pieces per thread per iteration
@@ -194,8 +194,8 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
     for (int r = 0; r < R; r++) klim[r] = min(prow[r], kstop - 1);
     const int kw_min = min(pw_min, kstop - 1);
 
-    const float sc = a.scale_log2 * (kIsFp8<KT> ? a.k_scale[g] : 1.0f);
-    const float vsc = kIsFp8<KT> ? a.v_scale[g] : 1.0f;
+    const float sc = a.scale_log2 * (kIsQuant<KT> ? a.k_scale[g] : 1.0f);
+    const float vsc = kIsQuant<KT> ? a.v_scale[g] : 1.0f;
 
     f32x4_t o[R][ND];
     float m[R], l[R];
@@ -297,23 +297,23 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
         const int tok = (off & 1023) >> 6;
         __bf16* krow = kl + k_lds_row(b, tok) * L::KS;
         const bool kzero = MASK && tok >= nval;
-        if constexpr (kIsFp8<KT>) {
+        if constexpr (kIsQuant<KT>) {
             const int c8 = (64 * slice + (off & 63)) >> 3;
             const uint4 w = kr[SET][j];
-            u32x4_t lo = {fp8x2_to_bf16x2<KT, false>(w.x), fp8x2_to_bf16x2<KT, true>(w.x), fp8x2_to_bf16x2<KT, false>(w.y),
-                          fp8x2_to_bf16x2<KT, true>(w.y)};
-            u32x4_t hi = {fp8x2_to_bf16x2<KT, false>(w.z), fp8x2_to_bf16x2<KT, true>(w.z), fp8x2_to_bf16x2<KT, false>(w.w),
-                          fp8x2_to_bf16x2<KT, true>(w.w)};
+            u32x4_t lo = {q8x2_to_bf16x2<KT, false>(w.x), q8x2_to_bf16x2<KT, true>(w.x), q8x2_to_bf16x2<KT, false>(w.y),
+                          q8x2_to_bf16x2<KT, true>(w.y)};
+            u32x4_t hi = {q8x2_to_bf16x2<KT, false>(w.z), q8x2_to_bf16x2<KT, true>(w.z), q8x2_to_bf16x2<KT, false>(w.w),
+                          q8x2_to_bf16x2<KT, true>(w.w)};
             if (kzero) lo = hi = u32x4_t{0, 0, 0, 0};
             *reinterpret_cast<u32x4_t*>(krow + 8 * k_pos_of_chunk<KT, D>(c8)) = lo;
             *reinterpret_cast<u32x4_t*>(krow + 8 * k_pos_of_chunk<KT, D>(c8 + 1)) = hi;
             // V: 16 tokens of channel d side by side
             const int d = off >> 4;
             const uint4 v = vr[SET][j];
-            u32x4_t vlo = {fp8x2_to_bf16x2<KT, false>(v.x), fp8x2_to_bf16x2<KT, true>(v.x), fp8x2_to_bf16x2<KT, false>(v.y),
-                           fp8x2_to_bf16x2<KT, true>(v.y)};
-            u32x4_t vhi = {fp8x2_to_bf16x2<KT, false>(v.z), fp8x2_to_bf16x2<KT, true>(v.z), fp8x2_to_bf16x2<KT, false>(v.w),
-                           fp8x2_to_bf16x2<KT, true>(v.w)};
+            u32x4_t vlo = {q8x2_to_bf16x2<KT, false>(v.x), q8x2_to_bf16x2<KT, true>(v.x), q8x2_to_bf16x2<KT, false>(v.y),
+                           q8x2_to_bf16x2<KT, true>(v.y)};
+            u32x4_t vhi = {q8x2_to_bf16x2<KT, false>(v.z), q8x2_to_bf16x2<KT, true>(v.z), q8x2_to_bf16x2<KT, false>(v.w),
+                           q8x2_to_bf16x2<KT, true>(v.w)};
             if constexpr (MASK) {
                 vlo = keep_bf16(vlo, nval);
                 vhi = keep_bf16(vhi, nval - 8);
@@ -576,6 +576,9 @@ hipError_t launch_prefill(int cache_dtype, int head_dim, int gqa, const PrefillA
     } else if (cache_dtype == kE5M2) {
         if (head_dim == 128) return launch_g<kE5M2, 128>(gqa, a, (int)grid, stream);
         if (head_dim == 64) return launch_g<kE5M2, 64>(gqa, a, (int)grid, stream);
+    } else if (cache_dtype == kI8) {
+        if (head_dim == 128) return launch_g<kI8, 128>(gqa, a, (int)grid, stream);
+        if (head_dim == 64) return launch_g<kI8, 64>(gqa, a, (int)grid, stream);
     } else if (cache_dtype == kBF16) {
         if (head_dim == 128) return launch_g<kBF16, 128>(gqa, a, (int)grid, stream);
         if (head_dim == 64) return launch_g<kBF16, 64>(gqa, a, (int)grid, stream);

@@ -12,11 +12,11 @@ import threading
 
 import torch
 
-F32, BF16, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3
-# A uint8 pool holds E4M3 codes; an E5M2 pool must be typed torch.float8_e5m2 (a uint8 buffer
-# can be viewed as one).
+F32, BF16, FP8_E4M3, FP8_E5M2, INT8 = 0, 1, 2, 3, 4
+# A uint8 pool holds E4M3 codes; an E5M2 pool must be typed torch.float8_e5m2 and an INT8 pool
+# torch.int8 (a uint8 buffer can be viewed as either).
 _TORCH_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.uint8: FP8_E4M3,
-               torch.float8_e4m3fn: FP8_E4M3, torch.float8_e5m2: FP8_E5M2}
+               torch.float8_e4m3fn: FP8_E4M3, torch.float8_e5m2: FP8_E5M2, torch.int8: INT8}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
 _lib = None

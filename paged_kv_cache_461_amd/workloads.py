@@ -455,8 +455,8 @@ def mixed_continuous_batch(seed=0, num_seqs=256, num_sharing=64, prefix=2048,
 def fp8_chunked_prefill(seed=0, num_decode=128, chunk=512, chunk_ctx=8192,
                         decode_range=(256, 8192), layer=0, cache_dtype=FP8_E4M3, fp8_scale="head",
                         name="fp8_chunked_prefill", block_size=16) -> PagedBatch:
-    """fp8 KV cache (E4M3 unless cache_dtype says E5M2) with per-(layer, kv head) scales
-    (fp8_scale="tensor": one scale per layer, repeated per head): sequence 0 is a 512-row prefill
+    """Quantised KV cache (fp8 E4M3 unless cache_dtype says E5M2 or INT8) with per-(layer, kv head)
+    scales (fp8_scale="tensor": one scale per layer, repeated per head): sequence 0 is a 512-row prefill
     chunk that is the last 512 positions of an 8192-token context; sequences 1..128 are
     decode rows with contexts uniform in [256, 8192].  32 query / 8 KV heads, head dim 128,
     bf16 queries and K/V rows."""
@@ -479,4 +479,7 @@ WORKLOADS = {
     "fp8_e5m2_chunked_prefill": lambda seed=0, layer=0, block_size=16: fp8_chunked_prefill(
         seed=seed, layer=layer, cache_dtype=FP8_E5M2, fp8_scale="tensor", name="fp8_e5m2_chunked_prefill",
         block_size=block_size),
+    # the same step over an INT8 cache with per-head scales (page 4, section 4.5, step 4)
+    "int8_chunked_prefill": lambda seed=0, layer=0, block_size=16: fp8_chunked_prefill(
+        seed=seed, layer=layer, cache_dtype=INT8, name="int8_chunked_prefill", block_size=block_size),
 }

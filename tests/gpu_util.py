@@ -25,6 +25,8 @@ def to_dev(raw: np.ndarray, dtype: int) -> torch.Tensor:
         return torch.from_numpy(raw.astype(np.uint8, copy=False)).to(DEV)
     if dtype == W.FP8_E5M2:
         return torch.from_numpy(raw.astype(np.uint8, copy=False)).to(DEV).view(torch.float8_e5m2)
+    if dtype == W.INT8:
+        return torch.from_numpy(raw.astype(np.uint8, copy=False)).to(DEV).view(torch.int8)
     raise ValueError(dtype)
 
 
@@ -36,7 +38,7 @@ def to_host_raw(t: torch.Tensor) -> np.ndarray:
         return t.view(torch.int16).numpy().view(np.uint16)
     if t.dtype == torch.uint8:
         return t.numpy()
-    if t.dtype == torch.float8_e5m2:
+    if t.dtype in (torch.float8_e5m2, torch.int8):
         return t.view(torch.uint8).numpy()
     raise ValueError(t.dtype)
 
@@ -131,14 +133,14 @@ class DeviceBatch:
         return out
 
 
-TOL = {W.F32: None, W.BF16: 2e-2, W.FP8_E4M3: 6e-2, W.FP8_E5M2: 6e-2}
+TOL = {W.F32: None, W.BF16: 2e-2, W.FP8_E4M3: 6e-2, W.FP8_E5M2: 6e-2, W.INT8: 6e-2}
 
 
 def assert_close(batch, got: np.ndarray, ref: np.ndarray, rows=None):
     """The pass bar: fp32 -- per (row, head) max|g-o| <= 1e-5 * max|o|; bf16 cache -- elementwise
-    |g-o| <= 2e-2; fp8 cache (E4M3 or E5M2) -- elementwise |g-o| <= 6e-2.  Both sides attend
-    over the same stored codes, so the fp8 bar covers only the kernel's arithmetic, not the
-    quantisation."""
+    |g-o| <= 2e-2; quantised cache (E4M3, E5M2 or INT8) -- elementwise |g-o| <= 6e-2.  Both sides
+    attend over the same stored codes, so the quantised-cache bar covers only the kernel's
+    arithmetic, not the quantisation."""
     assert got.shape == ref.shape
     assert np.isfinite(got).all(), "non-finite output"
     if batch.cache_dtype == W.F32:

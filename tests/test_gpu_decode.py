@@ -52,7 +52,7 @@ def test_bf16_shapes(gqa, head_dim):
     step_and_compare(b, partition_size=256)
 
 
-@pytest.mark.parametrize("cache", [W.BF16, W.FP8_E4M3, W.FP8_E5M2, W.F32])
+@pytest.mark.parametrize("cache", [W.BF16, W.FP8_E4M3, W.FP8_E5M2, W.F32, W.INT8])
 @pytest.mark.parametrize("P", [0, 32, 256])
 def test_block_size_32(cache, P):
     """32-token blocks: each block is two 16-token units at fixed offsets of its tile; ragged
@@ -75,7 +75,7 @@ def test_block_size_8(cache, P, short):
     step_and_compare(b, partition_size=P)
 
 
-@pytest.mark.parametrize("cache", [W.BF16, W.FP8_E4M3, W.F32])
+@pytest.mark.parametrize("cache", [W.BF16, W.FP8_E4M3, W.F32, W.INT8])
 def test_short_contexts_one_chunk_per_run(cache):
     """max_context_len <= 128: one chunk per (sequence, kv head), no workspace and no merge.
     2600 runs outnumber the grid's waves, some sequences are empty (zero rows), and the two
@@ -109,7 +109,7 @@ def test_fp32_shapes(gqa):
     step_and_compare(b, partition_size=128)
 
 
-@pytest.mark.parametrize("cache", [W.FP8_E4M3, W.FP8_E5M2])
+@pytest.mark.parametrize("cache", [W.FP8_E4M3, W.FP8_E5M2, W.INT8])
 @pytest.mark.parametrize("head_dim", [64, 128])
 def test_fp8_cache(cache, head_dim):
     b = W.build_batch([1, 9, 16, 33, 250, 1000, 2049], num_heads=32, num_kv_heads=8, head_dim=head_dim,
@@ -117,7 +117,7 @@ def test_fp8_cache(cache, head_dim):
     step_and_compare(b, partition_size=512)
 
 
-@pytest.mark.parametrize("cache", [W.FP8_E4M3, W.FP8_E5M2])
+@pytest.mark.parametrize("cache", [W.FP8_E4M3, W.FP8_E5M2, W.INT8])
 def test_fp8_per_tensor_scale(cache):
     """One scale per layer, repeated per kv head (a per-tensor scale) goes through the same
     per-head path."""
@@ -199,7 +199,8 @@ def test_phase_api_equals_one_call():
 
 
 @pytest.mark.parametrize("src,cache", [(W.F32, W.F32), (W.BF16, W.BF16), (W.BF16, W.FP8_E4M3),
-                                       (W.F32, W.FP8_E4M3), (W.BF16, W.FP8_E5M2), (W.F32, W.FP8_E5M2)])
+                                       (W.F32, W.FP8_E4M3), (W.BF16, W.FP8_E5M2), (W.F32, W.FP8_E5M2),
+                                       (W.BF16, W.INT8), (W.F32, W.INT8)])
 def test_kv_write_bit_exact_whole_pool(src, cache):
     """Random bytes everywhere, then an append of 300 tokens to scattered unique slots (some
     skipped with -1): the whole pool equals the oracle's, byte for byte."""
@@ -217,7 +218,7 @@ def test_kv_write_bit_exact_whole_pool(src, cache):
     fmax = W.QUANT_MAX.get(cache, 1.0)
     ks = (np.abs(vals[0]).max(axis=(0, 2)) / fmax * 0.5).astype(np.float32)   # forces some saturation
     vs = (np.abs(vals[1]).max(axis=(0, 2)) / fmax * 1.3).astype(np.float32)
-    fp8 = cache in W.FP8_DTYPES
+    fp8 = cache in W.QUANT_DTYPES
     kp, vp = to_dev(kp_h, cache), to_dev(vp_h, cache)
     from paged_kv_cache_461_amd import ops
     ops.kv_cache_write(to_dev(key, src), to_dev(value, src), kp, vp, torch.from_numpy(slots).cuda(),
@@ -231,10 +232,11 @@ def test_kv_write_bit_exact_whole_pool(src, cache):
 
 
 @pytest.mark.parametrize("cache,scale", [(W.FP8_E4M3, s) for s in (1.0, 0.0103125, 1.0 / 448.0, 2.0 ** -12, 3.0)] +
-                         [(W.FP8_E5M2, s) for s in (1.0, 8.7e-5, 1.0 / 57344.0, 2.0 ** -20, 3.0)])
+                         [(W.FP8_E5M2, s) for s in (1.0, 8.7e-5, 1.0 / 57344.0, 2.0 ** -20, 3.0)] +
+                         [(W.INT8, s) for s in (1.0, 4.5 / 127.0, 1.0 / 127.0, 2.0 ** -12, 3.0)])
 def test_fp8_encode_exhaustive_over_bf16(cache, scale):
-    """All 65536 bf16 bit patterns (NaN, inf, subnormal, +-0 included) appended to an fp8
-    cache: every code equals the oracle's E4M3 (E5M2) rounding of fl32(x / scale)."""
+    """All 65536 bf16 bit patterns (NaN, inf, subnormal, +-0 included) appended to an 8-bit
+    cache: every code equals the oracle's E4M3 (E5M2, INT8) rounding of fl32(x / scale)."""
     hkv, d, bs = 4, 128, 16
     T = 65536 // (hkv * d)
     key = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(T, hkv, d)
@@ -257,16 +259,17 @@ def test_fp8_encode_exhaustive_over_bf16(cache, scale):
     assert np.array_equal(gv, vp_h)
 
 
-@pytest.mark.parametrize("cache", [W.FP8_E4M3, W.FP8_E5M2])
+@pytest.mark.parametrize("cache", [W.FP8_E4M3, W.FP8_E5M2, W.INT8])
 def test_fp8_decode_exhaustive_via_single_token(cache):
     """A one-token context returns that token's V: with v_scale 1, the bf16 output is the exact
-    value of every fp8 code (all 256, NaN and E5M2's infinities included) stored in the V row."""
+    value of every 8-bit code (all 256: NaN and E5M2's infinities included, INT8's -128 too)
+    stored in the V row."""
     hkv, d = 2, 128
     b = W.build_batch([1], num_heads=hkv, num_kv_heads=hkv, head_dim=d, q_dtype=W.BF16, cache_dtype=cache,
                       seed=0)
     codes = np.arange(256, dtype=np.uint8).reshape(hkv, d)
     kp_h, vp_h = b.empty_pool()
-    kp_h[:] = 0x38 if cache == W.FP8_E4M3 else 0x3C  # K = 1.0 everywhere (irrelevant with one token)
+    kp_h[:] = {W.FP8_E4M3: 0x38, W.FP8_E5M2: 0x3C, W.INT8: 0x01}[cache]  # K = 1 everywhere (irrelevant here)
     blk = int(b.block_tables[0, 0])
     for h in range(hkv):
         for c in range(d):
@@ -276,7 +279,8 @@ def test_fp8_decode_exhaustive_via_single_token(cache):
     db.v_scale = torch.ones(hkv, device="cuda")
     out = db.decode(to_dev(kp_h, cache), to_dev(vp_h, cache))
     got = out_to_f64(out)[0]
-    want = (oracle.e4m3_to_float64 if cache == W.FP8_E4M3 else oracle.e5m2_to_float64)(codes)
+    want = {W.FP8_E4M3: oracle.e4m3_to_float64, W.FP8_E5M2: oracle.e5m2_to_float64,
+            W.INT8: oracle.int8_to_float64}[cache](codes)
     assert np.array_equal(np.isnan(got), np.isnan(want))
     ok = ~np.isnan(want)
     assert np.array_equal(got[ok], want[ok])
@@ -301,7 +305,8 @@ def _fused(db, k_pool, v_pool, partition_size=0):
     (W.BF16, 0, 16, False), (W.BF16, 16, 16, False), (W.BF16, 256, 16, False), (W.FP8_E4M3, 0, 16, False),
     (W.FP8_E4M3, 64, 16, False), (W.FP8_E5M2, 0, 16, False), (W.F32, 0, 16, False), (W.F32, 32, 16, False),
     (W.BF16, 0, 32, False), (W.FP8_E4M3, 32, 32, False), (W.BF16, 0, 16, True), (W.FP8_E4M3, 0, 32, True),
-    (W.BF16, 0, 8, False), (W.F32, 16, 8, True)])
+    (W.BF16, 0, 8, False), (W.F32, 16, 8, True), (W.INT8, 0, 16, False), (W.INT8, 64, 32, False),
+    (W.INT8, 0, 16, True)])
 def test_fused_append_equals_separate_calls(cache, P, B, short):
     """pa_paged_attention_decode_append writes the same pool bytes as pa_kv_cache_write and
     returns the same output bits as the decode that follows it; both match the oracle.  The
@@ -412,7 +417,7 @@ def test_merge_more_than_64_pieces_per_run():
     assert torch.equal(got, _two_phase(db, kp, vp, 16))
 
 
-@pytest.mark.parametrize("cache,B", [(W.BF16, 16), (W.FP8_E4M3, 16), (W.BF16, 32), (W.F32, 8)])
+@pytest.mark.parametrize("cache,B", [(W.BF16, 16), (W.FP8_E4M3, 16), (W.BF16, 32), (W.F32, 8), (W.INT8, 16)])
 def test_shared_block_hint_changes_nothing_but_cache_policy(cache, B):
     """Sequences sharing a 256-token prefix through identical block ids: the decode with the
     shared-block hint (cached loads for the shared leading blocks) gives the same bits as without

@@ -77,9 +77,10 @@ def test_mixed_continuous_batch_full():
     full_step_and_check(b)
 
 
-@pytest.mark.parametrize("cache,granularity", [(W.FP8_E4M3, "head"), (W.FP8_E5M2, "tensor")])
+@pytest.mark.parametrize("cache,granularity", [(W.FP8_E4M3, "head"), (W.FP8_E5M2, "tensor"), (W.INT8, "head")])
 def test_fp8_chunked_prefill_full(cache, granularity):
-    """512-row chunk ending an 8192-token context (fp8 cache) plus 128 decode rows: all 640 rows."""
+    """512-row chunk ending an 8192-token context (fp8 / INT8 cache) plus 128 decode rows: all 640
+    rows."""
     full_step_and_check(W.fp8_chunked_prefill(cache_dtype=cache, fp8_scale=granularity))
 
 

@@ -40,7 +40,7 @@ def prefill_and_compare(batch, partition_size=0, poison=True):
 MIXED = ([300, 1, 64, 700, 129, 40, 1000], [37, 1, 64, 200, 1, 40, 130])
 
 
-@pytest.mark.parametrize("cache", [W.BF16, W.FP8_E4M3, W.FP8_E5M2])
+@pytest.mark.parametrize("cache", [W.BF16, W.FP8_E4M3, W.FP8_E5M2, W.INT8])
 @pytest.mark.parametrize("gqa", [1, 2, 4, 8])
 @pytest.mark.parametrize("head_dim", [64, 128])
 def test_mixed_chunks(cache, gqa, head_dim):
@@ -59,7 +59,7 @@ def test_block_size_8(P):
     prefill_and_compare(b, partition_size=P)
 
 
-@pytest.mark.parametrize("cache", [W.BF16, W.FP8_E4M3])
+@pytest.mark.parametrize("cache", [W.BF16, W.FP8_E4M3, W.INT8])
 @pytest.mark.parametrize("P", [0, 32, 96])
 def test_block_size_32(cache, P):
     """32-token blocks: a 64-key iteration spans two blocks (four 16-token units); split
@@ -118,7 +118,7 @@ def test_physical_block_relabelling_is_bit_identical():
     assert torch.equal(base.view(torch.int16), again.view(torch.int16))
 
 
-@pytest.mark.parametrize("cache", [W.BF16, W.FP8_E4M3, W.FP8_E5M2])
+@pytest.mark.parametrize("cache", [W.BF16, W.FP8_E4M3, W.FP8_E5M2, W.INT8])
 def test_unused_slots_never_read(cache):
     """NaN in every unwritten slot, free block and stale table entry: same bits as zeros."""
     b = W.build_batch([7, 17, 300], num_heads=8, num_kv_heads=2, head_dim=128, q_dtype=W.BF16, cache_dtype=cache,
