@@ -149,8 +149,9 @@ struct PrefillPlan {
     int64_t total;
 };
 
-// Workgroups the prefill grid should reach before splitting keys: 2 per CU of 256 CUs.
-constexpr int64_t kPrefillTargetWorkgroups = 512;
+// Workgroups the prefill grid should reach before splitting keys: one per CU of 256 CUs (a
+// prefill workgroup fills a CU: 8 waves and 102 KiB of LDS).
+constexpr int64_t kPrefillTargetWorkgroups = 256;
 // Automatic splits keep at least this many keys per split.
 constexpr int32_t kPrefillMinSplitKeys = 256;
 

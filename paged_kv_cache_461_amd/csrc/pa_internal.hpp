@@ -67,8 +67,10 @@ struct DecodeArgs {
 };
 
 // Chunked prefill: MFMA attention kernel (+ merge kernel when the keys are split).
-constexpr int kPrefillThreads = 256;  // 4 waves per workgroup
-constexpr int kPrefillRowTiles = 2;   // 16-row MFMA tiles per wave: 128 stacked rows per workgroup
+// Prefill: 8 waves per workgroup (two groups that alternate matrix and vector phases on each
+// SIMD), one workgroup per CU.
+constexpr int kPrefillThreads = 512;
+constexpr int kPrefillRowTiles = 2;   // 16-row MFMA tiles per wave
 
 struct PrefillArgs {
     void* out;                     // [num_query_rows][Hq][D], bf16
