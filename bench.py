@@ -314,17 +314,28 @@ def measure(batch, dev, layers, steps, warmup, partitions=(0,), fused=False, gra
     # call appends its own
     Rw = Rp if (fused and Sd) else batch.num_rows
 
+    # Every library call of the step is prepared once per (call, layer pool, options): its
+    # arguments are checked and converted at preparation, so a launch costs one foreign call.
+    prepared = {}
+
+    def launch(key, make):
+        c = prepared.get(key)
+        if c is None:
+            c = prepared[key] = make()
+        c(None if cur[0] is stream else cur[0])
+
     def write(r):
         kp, vp, (nk, nv, nslots), q, ks, vs = pools[r % len(pools)]
-        ops.kv_cache_write(nk[:Rw], nv[:Rw], kp, vp, nslots[:Rw], num_kv_heads=Hkv, head_dim=D, block_size=B,
-                           k_scale=ks, v_scale=vs, stream=cur[0])
+        launch(("write", r % len(pools)), lambda: ops.prepare_kv_cache_write(
+            nk[:Rw], nv[:Rw], kp, vp, nslots[:Rw], num_kv_heads=Hkv, head_dim=D, block_size=B, k_scale=ks,
+            v_scale=vs, stream=stream))
 
     def prefill(r):
         kp, vp, _, q, ks, vs = pools[r % len(pools)]
-        ops.paged_attention_chunked_prefill(outs[r % len(pools)][:Rp], q[:Rp], cu[:Sp + 1], kp, vp, tables[:Sp],
-                                            ctx[:Sp], max_query_len=pf_max_q, max_context_len=pf_max_ctx,
-                                            num_kv_heads=Hkv, scale=batch.scale, block_size=B, k_scale=ks,
-                                            v_scale=vs, workspace=pf_ws, stream=cur[0])
+        launch(("prefill", r % len(pools)), lambda: ops.prepare_paged_attention_chunked_prefill(
+            outs[r % len(pools)][:Rp], q[:Rp], cu[:Sp + 1], kp, vp, tables[:Sp], ctx[:Sp], max_query_len=pf_max_q,
+            max_context_len=pf_max_ctx, num_kv_heads=Hkv, scale=batch.scale, block_size=B, k_scale=ks, v_scale=vs,
+            workspace=pf_ws, stream=stream))
 
     # sequences sharing leading blocks: the decode call gets the shared-block hint (cached loads
     # for those blocks), as a prefix cache's host side would pass it
@@ -335,13 +346,14 @@ def measure(batch, dev, layers, steps, warmup, partitions=(0,), fused=False, gra
         kp, vp, (nk, nv, _), q, ks, vs = pools[r % len(pools)]
         P = part[0]
         common = dict(max_context_len=dec_max_ctx, num_kv_heads=Hkv, scale=batch.scale, block_size=B, k_scale=ks,
-                      v_scale=vs, partition_size=P, workspace=wss[P], phase=phase, stream=cur[0])
+                      v_scale=vs, partition_size=P, workspace=wss[P], phase=phase, stream=stream)
         if fused:
-            ops.paged_attention_decode_append(outs[r % len(pools)][Rp:], q[Rp:], nk[Rp:].view(Sd, Hkv, D),
-                                              nv[Rp:].view(Sd, Hkv, D), kp, vp, tables[Sp:], ctx[Sp:], **common)
+            launch(("decode", r % len(pools), phase, P), lambda: ops.prepare_paged_attention_decode_append(
+                outs[r % len(pools)][Rp:], q[Rp:], nk[Rp:].view(Sd, Hkv, D), nv[Rp:].view(Sd, Hkv, D), kp, vp,
+                tables[Sp:], ctx[Sp:], **common))
         else:
-            ops.paged_attention_decode(outs[r % len(pools)][Rp:], q[Rp:], kp, vp, tables[Sp:], ctx[Sp:],
-                                       shared_blocks=shared, **common)
+            launch(("decode", r % len(pools), phase, P), lambda: ops.prepare_paged_attention_decode(
+                outs[r % len(pools)][Rp:], q[Rp:], kp, vp, tables[Sp:], ctx[Sp:], shared_blocks=shared, **common))
 
     def step(i):
         if Rw:

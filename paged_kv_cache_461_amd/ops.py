@@ -50,6 +50,9 @@ class PagedAttnError(RuntimeError):
 def library():
     """The loaded library (ctypes.CDLL) with its signatures declared."""
     global _lib
+    lib = _lib
+    if lib is not None:
+        return lib
     with _lock:
         if _lib is not None:
             return _lib
@@ -159,6 +162,27 @@ def _stream(stream):
     return ctypes.c_void_p(int(stream))
 
 
+class PreparedCall:
+    """One library call whose arguments were checked and converted once (prepare_* functions).
+    Calling it launches with exactly those arguments: the tensors must stay alive, keep their
+    storage and shapes, and hold the step's data when it is called; `stream` (a torch stream or
+    a raw handle) replaces the stream chosen at preparation.  A repeated step (a decode loop, a
+    benchmark) pays the argument checks and conversions once instead of on every launch."""
+
+    __slots__ = ("_fn", "_args", "_keep")
+
+    def __init__(self, fn, args, keep):
+        self._fn, self._args, self._keep = fn, tuple(args), keep
+
+    def __call__(self, stream=None):
+        if stream is None:
+            st = self._fn(*self._args)
+        else:
+            st = self._fn(*self._args[:-1], _stream(stream))
+        if st != PA_OK:
+            _check(st)
+
+
 def num_pool_blocks(pool: torch.Tensor, num_kv_heads: int, head_dim: int, block_size: int) -> int:
     tile = num_kv_heads * block_size * head_dim
     if pool.numel() % tile:
@@ -166,9 +190,8 @@ def num_pool_blocks(pool: torch.Tensor, num_kv_heads: int, head_dim: int, block_
     return pool.numel() // tile
 
 
-def kv_cache_write(key, value, k_pool, v_pool, slot_mapping, *, num_kv_heads, head_dim, block_size=16,
-                   k_scale=None, v_scale=None, stream=None):
-    """Store key/value rows [T][Hkv][D] into their pool slots (pa_kv_cache_write)."""
+def _kv_cache_write_args(key, value, k_pool, v_pool, slot_mapping, num_kv_heads, head_dim, block_size, k_scale,
+                         v_scale, stream):
     for n, t in (("key", key), ("value", value), ("k_pool", k_pool), ("v_pool", v_pool)):
         _dev(n, t)
     _dev("slot_mapping", slot_mapping, torch.int64)
@@ -179,9 +202,25 @@ def kv_cache_write(key, value, k_pool, v_pool, slot_mapping, *, num_kv_heads, he
     T = slot_mapping.numel()
     if key.numel() != T * num_kv_heads * head_dim or value.shape != key.shape:
         raise ValueError("key/value must be [%d][%d][%d]" % (T, num_kv_heads, head_dim))
-    _check(library().pa_kv_cache_write(_ptr(key), _ptr(value), dtype_code(key), _ptr(k_pool), _ptr(v_pool), nb,
-                                       dtype_code(k_pool), _ptr(slot_mapping), T, num_kv_heads, head_dim,
-                                       block_size, _ptr(k_scale), _ptr(v_scale), _stream(stream)))
+    return library().pa_kv_cache_write, (
+        _ptr(key), _ptr(value), dtype_code(key), _ptr(k_pool), _ptr(v_pool), nb, dtype_code(k_pool),
+        _ptr(slot_mapping), T, num_kv_heads, head_dim, block_size, _ptr(k_scale), _ptr(v_scale), _stream(stream))
+
+
+def kv_cache_write(key, value, k_pool, v_pool, slot_mapping, *, num_kv_heads, head_dim, block_size=16,
+                   k_scale=None, v_scale=None, stream=None):
+    """Store key/value rows [T][Hkv][D] into their pool slots (pa_kv_cache_write)."""
+    fn, args = _kv_cache_write_args(key, value, k_pool, v_pool, slot_mapping, num_kv_heads, head_dim, block_size,
+                                    k_scale, v_scale, stream)
+    _check(fn(*args))
+
+
+def prepare_kv_cache_write(key, value, k_pool, v_pool, slot_mapping, *, num_kv_heads, head_dim, block_size=16,
+                           k_scale=None, v_scale=None, stream=None) -> PreparedCall:
+    """kv_cache_write with its arguments checked and converted once (PreparedCall)."""
+    fn, args = _kv_cache_write_args(key, value, k_pool, v_pool, slot_mapping, num_kv_heads, head_dim, block_size,
+                                    k_scale, v_scale, stream)
+    return PreparedCall(fn, args, (key, value, k_pool, v_pool, slot_mapping, k_scale, v_scale))
 
 
 def decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, block_size=16,
@@ -201,13 +240,8 @@ def decode_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_context_le
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
-def paged_attention_decode(out, query, k_pool, v_pool, block_tables, context_lens, *, max_context_len,
-                           num_kv_heads, scale, block_size=16, k_scale=None, v_scale=None, partition_size=0,
-                           workspace=None, phase=3, stream=None, shared_blocks=None):
-    """One query row per sequence over its paged context (pa_paged_attention_decode[_phase]).
-    query/out: [S][Hq][D]; block_tables: int32 [S][max_blocks]; context_lens: int32 [S].
-    shared_blocks: optional int32 [S], the leading blocks of each sequence that other sequences
-    share (pa_paged_attention_decode_shared: those are read with cached loads)."""
+def _decode_args(out, query, k_pool, v_pool, block_tables, context_lens, max_context_len, num_kv_heads, scale,
+                 block_size, k_scale, v_scale, partition_size, workspace, phase, stream, shared_blocks):
     for n, t in (("out", out), ("query", query), ("k_pool", k_pool), ("v_pool", v_pool)):
         _dev(n, t)
     _dev("block_tables", block_tables, torch.int32)
@@ -223,22 +257,42 @@ def paged_attention_decode(out, query, k_pool, v_pool, block_tables, context_len
         raise ValueError("block_tables must be [num_seqs][max_blocks] and context_lens [num_seqs]")
     nb = num_pool_blocks(k_pool, num_kv_heads, D, block_size)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    head = (int(phase), _ptr(out), _ptr(query), dtype_code(query), _ptr(k_pool), _ptr(v_pool), nb,
+            dtype_code(k_pool), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens))
+    tail = (int(max_context_len), S, Hq, num_kv_heads, D, block_size, float(scale), _ptr(k_scale), _ptr(v_scale),
+            int(partition_size), _ptr(workspace), ws_bytes, _stream(stream))
     if shared_blocks is not None:
         _dev("shared_blocks", shared_blocks, torch.int32)
         if shared_blocks.numel() != S:
             raise ValueError("shared_blocks must be [num_seqs]")
-        _check(library().pa_paged_attention_decode_shared(
-            int(phase), _ptr(out), _ptr(query), dtype_code(query), _ptr(k_pool), _ptr(v_pool), nb,
-            dtype_code(k_pool), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), _ptr(shared_blocks),
-            int(max_context_len), S, Hq, num_kv_heads, D, block_size, float(scale), _ptr(k_scale), _ptr(v_scale),
-            int(partition_size), _ptr(workspace), ws_bytes, _stream(stream)))
-        return out
-    _check(library().pa_paged_attention_decode_phase(
-        int(phase), _ptr(out), _ptr(query), dtype_code(query), _ptr(k_pool), _ptr(v_pool), nb, dtype_code(k_pool),
-        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), int(max_context_len), S, Hq, num_kv_heads, D,
-        block_size, float(scale), _ptr(k_scale), _ptr(v_scale), int(partition_size), _ptr(workspace), ws_bytes,
-        _stream(stream)))
+        return library().pa_paged_attention_decode_shared, head + (_ptr(shared_blocks),) + tail
+    return library().pa_paged_attention_decode_phase, head + tail
+
+
+def paged_attention_decode(out, query, k_pool, v_pool, block_tables, context_lens, *, max_context_len,
+                           num_kv_heads, scale, block_size=16, k_scale=None, v_scale=None, partition_size=0,
+                           workspace=None, phase=3, stream=None, shared_blocks=None):
+    """One query row per sequence over its paged context (pa_paged_attention_decode[_phase]).
+    query/out: [S][Hq][D]; block_tables: int32 [S][max_blocks]; context_lens: int32 [S].
+    shared_blocks: optional int32 [S], the leading blocks of each sequence that other sequences
+    share (pa_paged_attention_decode_shared: those are read with cached loads)."""
+    fn, args = _decode_args(out, query, k_pool, v_pool, block_tables, context_lens, max_context_len, num_kv_heads,
+                            scale, block_size, k_scale, v_scale, partition_size, workspace, phase, stream,
+                            shared_blocks)
+    _check(fn(*args))
     return out
+
+
+def prepare_paged_attention_decode(out, query, k_pool, v_pool, block_tables, context_lens, *, max_context_len,
+                                   num_kv_heads, scale, block_size=16, k_scale=None, v_scale=None,
+                                   partition_size=0, workspace=None, phase=3, stream=None,
+                                   shared_blocks=None) -> PreparedCall:
+    """paged_attention_decode with its arguments checked and converted once (PreparedCall)."""
+    fn, args = _decode_args(out, query, k_pool, v_pool, block_tables, context_lens, max_context_len, num_kv_heads,
+                            scale, block_size, k_scale, v_scale, partition_size, workspace, phase, stream,
+                            shared_blocks)
+    return PreparedCall(fn, args, (out, query, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale,
+                                   workspace, shared_blocks))
 
 
 def paged_attention_decode_noalloc(out, query, k_pool, v_pool, block_tables, context_lens, *, max_context_len,
@@ -289,12 +343,9 @@ def chunked_prefill_workspace(num_query_rows, num_seqs, max_query_len, num_heads
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
-def paged_attention_chunked_prefill(out, query, cu_query_lens, k_pool, v_pool, block_tables, context_lens, *,
-                                    max_query_len, max_context_len, num_kv_heads, scale, block_size=16,
-                                    k_scale=None, v_scale=None, partition_size=0, workspace=None, stream=None):
-    """Causal attention of each sequence's last q_len positions over its paged context
-    (pa_paged_attention_chunked_prefill).  query/out: [rows][Hq][D] bf16; cu_query_lens:
-    int32 [S+1]; block_tables: int32 [S][max_blocks]; context_lens: int32 [S]."""
+def _prefill_args(out, query, cu_query_lens, k_pool, v_pool, block_tables, context_lens, max_query_len,
+                  max_context_len, num_kv_heads, scale, block_size, k_scale, v_scale, partition_size, workspace,
+                  stream):
     for n, t in (("out", out), ("query", query), ("k_pool", k_pool), ("v_pool", v_pool)):
         _dev(n, t)
     _dev("cu_query_lens", cu_query_lens, torch.int32)
@@ -312,19 +363,41 @@ def paged_attention_chunked_prefill(out, query, cu_query_lens, k_pool, v_pool, b
         raise ValueError("cu_query_lens must be [S+1], block_tables [S][max_blocks], context_lens [S]")
     nb = num_pool_blocks(k_pool, num_kv_heads, D, block_size)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(library().pa_paged_attention_chunked_prefill(
+    return library().pa_paged_attention_chunked_prefill, (
         _ptr(out), _ptr(query), dtype_code(query), _ptr(cu_query_lens), rows, int(max_query_len), _ptr(k_pool),
         _ptr(v_pool), nb, dtype_code(k_pool), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
         int(max_context_len), S, Hq, num_kv_heads, D, block_size, float(scale), _ptr(k_scale), _ptr(v_scale),
-        int(partition_size), _ptr(workspace), ws_bytes, _stream(stream)))
+        int(partition_size), _ptr(workspace), ws_bytes, _stream(stream))
+
+
+def paged_attention_chunked_prefill(out, query, cu_query_lens, k_pool, v_pool, block_tables, context_lens, *,
+                                    max_query_len, max_context_len, num_kv_heads, scale, block_size=16,
+                                    k_scale=None, v_scale=None, partition_size=0, workspace=None, stream=None):
+    """Causal attention of each sequence's last q_len positions over its paged context
+    (pa_paged_attention_chunked_prefill).  query/out: [rows][Hq][D] bf16; cu_query_lens:
+    int32 [S+1]; block_tables: int32 [S][max_blocks]; context_lens: int32 [S]."""
+    fn, args = _prefill_args(out, query, cu_query_lens, k_pool, v_pool, block_tables, context_lens, max_query_len,
+                             max_context_len, num_kv_heads, scale, block_size, k_scale, v_scale, partition_size,
+                             workspace, stream)
+    _check(fn(*args))
     return out
 
 
-def paged_attention_decode_append(out, query, new_key, new_value, k_pool, v_pool, block_tables, context_lens, *,
-                                  max_context_len, num_kv_heads, scale, block_size=16, k_scale=None, v_scale=None,
-                                  partition_size=0, workspace=None, phase=3, stream=None):
-    """Store each sequence's new K/V row at position context_lens[s] - 1, then decode
-    (pa_paged_attention_decode_append).  new_key/new_value: [S][Hkv][D] in the query dtype."""
+def prepare_paged_attention_chunked_prefill(out, query, cu_query_lens, k_pool, v_pool, block_tables,
+                                            context_lens, *, max_query_len, max_context_len, num_kv_heads, scale,
+                                            block_size=16, k_scale=None, v_scale=None, partition_size=0,
+                                            workspace=None, stream=None) -> PreparedCall:
+    """paged_attention_chunked_prefill with its arguments checked and converted once (PreparedCall)."""
+    fn, args = _prefill_args(out, query, cu_query_lens, k_pool, v_pool, block_tables, context_lens, max_query_len,
+                             max_context_len, num_kv_heads, scale, block_size, k_scale, v_scale, partition_size,
+                             workspace, stream)
+    return PreparedCall(fn, args, (out, query, cu_query_lens, k_pool, v_pool, block_tables, context_lens, k_scale,
+                                   v_scale, workspace))
+
+
+def _decode_append_args(out, query, new_key, new_value, k_pool, v_pool, block_tables, context_lens,
+                        max_context_len, num_kv_heads, scale, block_size, k_scale, v_scale, partition_size,
+                        workspace, phase, stream):
     for n, t in (("out", out), ("query", query), ("new_key", new_key), ("new_value", new_value),
                  ("k_pool", k_pool), ("v_pool", v_pool)):
         _dev(n, t)
@@ -344,12 +417,35 @@ def paged_attention_decode_append(out, query, new_key, new_value, k_pool, v_pool
         raise ValueError("block_tables must be [num_seqs][max_blocks] and context_lens [num_seqs]")
     nb = num_pool_blocks(k_pool, num_kv_heads, D, block_size)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(library().pa_paged_attention_decode_append(
+    return library().pa_paged_attention_decode_append, (
         int(phase), _ptr(out), _ptr(query), dtype_code(query), _ptr(new_key), _ptr(new_value), _ptr(k_pool),
         _ptr(v_pool), nb, dtype_code(k_pool), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
         int(max_context_len), S, Hq, num_kv_heads, D, block_size, float(scale), _ptr(k_scale), _ptr(v_scale),
-        int(partition_size), _ptr(workspace), ws_bytes, _stream(stream)))
+        int(partition_size), _ptr(workspace), ws_bytes, _stream(stream))
+
+
+def paged_attention_decode_append(out, query, new_key, new_value, k_pool, v_pool, block_tables, context_lens, *,
+                                  max_context_len, num_kv_heads, scale, block_size=16, k_scale=None, v_scale=None,
+                                  partition_size=0, workspace=None, phase=3, stream=None):
+    """Store each sequence's new K/V row at position context_lens[s] - 1, then decode
+    (pa_paged_attention_decode_append).  new_key/new_value: [S][Hkv][D] in the query dtype."""
+    fn, args = _decode_append_args(out, query, new_key, new_value, k_pool, v_pool, block_tables, context_lens,
+                                   max_context_len, num_kv_heads, scale, block_size, k_scale, v_scale,
+                                   partition_size, workspace, phase, stream)
+    _check(fn(*args))
     return out
+
+
+def prepare_paged_attention_decode_append(out, query, new_key, new_value, k_pool, v_pool, block_tables,
+                                          context_lens, *, max_context_len, num_kv_heads, scale, block_size=16,
+                                          k_scale=None, v_scale=None, partition_size=0, workspace=None, phase=3,
+                                          stream=None) -> PreparedCall:
+    """paged_attention_decode_append with its arguments checked and converted once (PreparedCall)."""
+    fn, args = _decode_append_args(out, query, new_key, new_value, k_pool, v_pool, block_tables, context_lens,
+                                   max_context_len, num_kv_heads, scale, block_size, k_scale, v_scale,
+                                   partition_size, workspace, phase, stream)
+    return PreparedCall(fn, args, (out, query, new_key, new_value, k_pool, v_pool, block_tables, context_lens,
+                                   k_scale, v_scale, workspace))
 
 
 def kv_bytes_per_token(num_layers, num_kv_heads, head_dim, cache_dtype) -> int:
