@@ -133,8 +133,10 @@ def make_batch(name, block_size=16):
 
 
 KERNEL_SOURCES = {
-    "decode": ("decode_kernel.hpp", "decode_launch.hpp", "decode.hip", "kv_store.hpp", "pa_device.hpp",
-               "pa_internal.hpp"),
+    "decode": ("decode_kernel.hpp", "decode_launch.hpp", "decode.hip", "decode_bf16.hip", "decode_e4m3.hip",
+               "decode_e5m2.hip", "decode_f32.hip", "decode_i8.hip", "decode_fused_bf16.hip",
+               "decode_fused_e4m3.hip", "decode_fused_e5m2.hip", "decode_fused_f32.hip", "decode_fused_i8.hip",
+               "kv_store.hpp", "pa_device.hpp", "pa_internal.hpp"),
     "prefill": ("prefill.hip", "pa_device.hpp", "pa_internal.hpp"),
 }
 

@@ -381,7 +381,8 @@ int32_t decode_call(int32_t phase, void* out, const void* query, int32_t q_dtype
     if (new_key && (!aligned16(new_key) || !aligned16(new_value)))
         return fail(PA_ERR_INVALID_ARG, "new_key and new_value must be 16-byte aligned");
     const int64_t stream_waves =
-        (int64_t)pa::kSimds * pa::decode_waves_per_simd(q_dtype, cache_dtype, head_dim, num_heads / num_kv_heads);
+        (int64_t)pa::kSimds *
+        pa::decode_waves_per_simd(q_dtype, cache_dtype, head_dim, num_heads / num_kv_heads, new_key != nullptr);
     const DecodePlan pl = plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
                                       partition_size, stream_waves);
     if (use_scratch) {  // the no-allocation form: this GPU's static scratch array is the workspace

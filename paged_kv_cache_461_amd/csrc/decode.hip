@@ -7,32 +7,33 @@
 namespace pa {
 
 namespace {
-template <int KT, int D>
+template <int KT, int D, bool FUSED>
 int waves_g(int gqa)
 {
     switch (gqa) {
-    case 1: return stream_waves_per_simd<KT, D, 1>();
-    case 2: return stream_waves_per_simd<KT, D, 2>();
-    case 4: return stream_waves_per_simd<KT, D, 4>();
-    default: return stream_waves_per_simd<KT, D, 8>();
+    case 1: return stream_waves_per_simd<KT, D, 1, FUSED>();
+    case 2: return stream_waves_per_simd<KT, D, 2, FUSED>();
+    case 4: return stream_waves_per_simd<KT, D, 4, FUSED>();
+    default: return stream_waves_per_simd<KT, D, 8, FUSED>();
     }
 }
 template <int KT>
-int waves_d(int head_dim, int gqa)
+int waves_d(int head_dim, int gqa, bool fused)
 {
-    return head_dim == 64 ? waves_g<KT, 64>(gqa) : waves_g<KT, 128>(gqa);
+    if (fused) return head_dim == 64 ? waves_g<KT, 64, true>(gqa) : waves_g<KT, 128, true>(gqa);
+    return head_dim == 64 ? waves_g<KT, 64, false>(gqa) : waves_g<KT, 128, false>(gqa);
 }
 }  // namespace
 
-int decode_waves_per_simd(int q_dtype, int cache_dtype, int head_dim, int gqa)
+int decode_waves_per_simd(int q_dtype, int cache_dtype, int head_dim, int gqa, bool fused)
 {
     (void)q_dtype;  // fp32 queries go with an fp32 cache, bf16 with the others
     switch (cache_dtype) {
-    case kF32: return waves_d<kF32>(head_dim, gqa);
-    case kBF16: return waves_d<kBF16>(head_dim, gqa);
-    case kFP8: return waves_d<kFP8>(head_dim, gqa);
-    case kE5M2: return waves_d<kE5M2>(head_dim, gqa);
-    case kI8: return waves_d<kI8>(head_dim, gqa);
+    case kF32: return waves_d<kF32>(head_dim, gqa, fused);
+    case kBF16: return waves_d<kBF16>(head_dim, gqa, fused);
+    case kFP8: return waves_d<kFP8>(head_dim, gqa, fused);
+    case kE5M2: return waves_d<kE5M2>(head_dim, gqa, fused);
+    case kI8: return waves_d<kI8>(head_dim, gqa, fused);
     default: return 2;
     }
 }

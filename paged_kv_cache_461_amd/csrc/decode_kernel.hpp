@@ -526,26 +526,30 @@ struct ChunkMap {
 //     SIMD (157 -> 139 us despite a few spills), and for fp8 G 8 (it fits 256 registers);
 //   otherwise the compiler's choice: 2 waves per SIMD for most variants (bf16 G 1 / 2 measured
 //     slower at 3), one for fp32 D 128, which measured slower when forced to 2 with spills.
+// The fused-append instances of the 8-bit caches at D 128 run 2 waves per SIMD: the append's
+// registers do not fit beside the ring in 168 (at 3 they spilled 14 VGPRs, and scratch traffic
+// is HBM traffic).
 // The persistent grid has max(2, this) waves per SIMD.
-template <int KT, int D, int G>
+template <int KT, int D, int G, bool FUSED = false>
 constexpr int stream_min_waves()
 {
     if constexpr (KT == kF32) return 1;
     else if constexpr (KT == kBF16) return D == 64 && G <= 4 ? 3 : D == 128 && G == 8 ? 2 : 1;
+    else if constexpr (FUSED && D == 128) return 2;
     else return G <= 4 ? 3 : 2;
 }
 
-template <int KT, int D, int G>
+template <int KT, int D, int G, bool FUSED = false>
 constexpr int stream_waves_per_simd()
 {
-    return stream_min_waves<KT, D, G>() > 2 ? stream_min_waves<KT, D, G>() : 2;
+    return stream_min_waves<KT, D, G, FUSED>() > 2 ? stream_min_waves<KT, D, G, FUSED>() : 2;
 }
 
 // PER_RUN: the one-chunk-per-run form (chunk_blocks < 0); FUSED: the fused append (new_key set);
 // HINT: cached loads for the leading blocks a.shared_blocks marks as shared.  Separate instances,
 // so that their extra paths leave the plain balanced form's registers alone.
 template <int QT, int KT, int D, int G, bool PER_RUN, bool FUSED, bool HINT = false>
-__global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G>())) void decode_stream_kernel(
+__global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>())) void decode_stream_kernel(
     const DecodeArgs a)
 {
     using S = Shape<QT, KT, D, G>;

@@ -102,7 +102,7 @@ hipError_t launch_kv_write(int src_dtype, int cache_dtype, const KvWriteArgs& a,
 
 // Waves per SIMD the streaming kernel of this variant is built for (2 or 3); the persistent
 // grid has that many waves per SIMD.
-int decode_waves_per_simd(int q_dtype, int cache_dtype, int head_dim, int gqa);
+int decode_waves_per_simd(int q_dtype, int cache_dtype, int head_dim, int gqa, bool fused = false);
 
 // phase 1 = streaming kernel, 2 = merge kernel, 3 = both.  Returns hipErrorInvalidValue when
 // no kernel exists for the combination.
