@@ -666,30 +666,39 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_kernel(PrefillArgs
 }
 
 // Combine the splits of every (query row, head): M = max_k m_k, w_k = 2^(m_k - M),
-// out = sum_k w_k o_k / sum_k w_k l_k (o_k already times v_scale).  One wave per row-head.
+// out = sum_k w_k o_k / sum_k w_k l_k (o_k already times v_scale).  D / 4 lanes per row-head,
+// 4 channels each (one 16-byte load per split), so a wave merges 64 / (D / 4) row-heads and
+// every lane has all of its splits' loads in flight at once.
+constexpr int kMergeThreads = 256;
 template <int D>
-__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a)
+constexpr int merge_rows_per_wg()
 {
+    return kMergeThreads / (D / 4);
+}
+
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArgs a)
+{
+    constexpr int LPR = D / 4;  // lanes per row-head
     const int64_t n = (int64_t)a.num_query_rows * a.num_heads;
-    const int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t idx = (int64_t)blockIdx.x * merge_rows_per_wg<D>() + threadIdx.x / LPR;
     if (idx >= n) return;
-    const int lane = threadIdx.x & 63;
-    constexpr int PER = D / 64;
+    const int c4 = (threadIdx.x % LPR) * 4;
+    const int ns = a.num_splits;
     float mm = -__builtin_inff();
-    for (int k = 0; k < a.num_splits; k++) mm = __builtin_fmaxf(mm, a.ml_part[2 * (k * n + idx)]);
-    float lsum = 0.0f, acc[PER] = {};
-    for (int k = 0; k < a.num_splits; k++) {
-        const float* ml = a.ml_part + 2 * (k * n + idx);
+    for (int k = 0; k < ns; k++) mm = __builtin_fmaxf(mm, a.ml_part[2 * (k * n + idx)]);
+    float lsum = 0.0f;
+    f32x4_t acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k = 0; k < ns; k++) {
+        const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(a.ml_part + 2 * (k * n + idx));
         const float wk = fast_exp2(ml[0] - mm);
         lsum += wk * ml[1];
-        const float* op = a.o_part + (k * n + idx) * D;
-#pragma unroll
-        for (int e = 0; e < PER; e++) acc[e] += wk * op[lane + 64 * e];
+        const f32x4_t o = *reinterpret_cast<const f32x4_t*>(a.o_part + (k * n + idx) * D + c4);
+        acc += wk * o;
     }
     const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-    __bf16* out = static_cast<__bf16*>(a.out) + idx * D;
-#pragma unroll
-    for (int e = 0; e < PER; e++) out[lane + 64 * e] = __builtin_bit_cast(__bf16, f32_to_bf16_bits(acc[e] * inv));
+    *reinterpret_cast<uint2*>(static_cast<__bf16*>(a.out) + idx * D + c4) =
+        make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv));
 }
 
 template <int KT, int D, int G>
@@ -708,7 +717,9 @@ hipError_t launch_one(const PrefillArgs& a, int grid, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.num_splits == 1) return e;
     const int64_t n = (int64_t)a.num_query_rows * a.num_heads;
-    hipLaunchKernelGGL((prefill_merge_kernel<D>), dim3((unsigned)((n + 3) / 4)), dim3(256), 0, stream, a);
+    constexpr int rpw = merge_rows_per_wg<D>();
+    hipLaunchKernelGGL((prefill_merge_kernel<D>), dim3((unsigned)((n + rpw - 1) / rpw)), dim3(kMergeThreads), 0,
+                       stream, a);
     return hipGetLastError();
 }
 
