@@ -455,13 +455,15 @@ __device__ __forceinline__ void next_run(Cursor& c, const int* lctx, int num_seq
 }
 
 // Fused append.  The chunk that holds a run's last unit is the only one that reads the new
-// token's slot (position ctx - 1).  Its wave stages the new K and V rows -- source [s][g] of
-// new_key / new_value, in the query dtype -- encoded in the cache dtype into a per-wave LDS row
-// when it starts the run's piece (beside the query load).  At the last unit it patches the
-// token's K and V from that row into the unit's loaded registers and stores them into the slot.
-// Nothing reads the slot back in this launch, so the stores need no wait; the pool bytes are
-// those of the append kernel (encode_elem) and the attention sees the same values in the same
-// places as after a separate append.
+// token's slot (position ctx - 1).  When its wave issues that unit's K/V loads it also loads the
+// run's new K and V rows (source [s][g] of new_key / new_value, in the query dtype), one
+// 16-byte piece per lane.  When it attends the unit, the lanes encode their pieces in the
+// cache dtype, store them into the slot and stage them in a per-wave LDS row, and the token's
+// K and V are patched from that row into the unit's loaded registers: the ring's copy of the
+// slot may or may not include the store, and either way the attention sees the same values in
+// the same places as after a separate append.  The row travels with the unit's loads, so
+// nothing waits for it.  Nothing in the launch waits for the store either; the pool bytes are
+// those of the append kernel (encode_elem, store_piece_codes).
 template <int QT, int KT, int D>
 struct NewRow {
     static constexpr int ES = DtypeBytes<QT>::value;  // source element bytes (query dtype)
@@ -472,31 +474,43 @@ struct NewRow {
     static_assert(2 * P <= 64, "the K and V rows of a token fit one wave");
 };
 
-// Lanes 0..P-1 encode the K row's P pieces, lanes P..2P-1 the V row's, into row (K at 0, V at
-// ROW).
-template <int QT, int KT, int D>
-__device__ __forceinline__ void stage_new_row(const DecodeArgs& a, int s, int g, unsigned char* row, int lane)
+// Deferred stores.  A store counts on the same wait counter as the ring's loads, so a store
+// issued in the middle of a chunk makes the next wait on the ring wait for it to be written as
+// well (the ring runs dry meanwhile).  The results of pieces that end inside the chunk -- and,
+// with the fused append, the new rows -- are kept in a per-wave LDS stage and written after
+// the chunk's last unit; a piece that finds the stage full is written at once.
+template <int G, int CG>
+constexpr int defer_slots()
 {
-    using R = NewRow<QT, KT, D>;
-    if (lane < 2 * R::P) {
-        const int kv = lane / R::P, piece = lane % R::P;
-        const unsigned char* src = static_cast<const unsigned char*>(kv ? a.new_value : a.new_key) +
-                                   (((int64_t)s * a.num_kv_heads + g) * D + piece * R::N) * R::ES;
-        const uint4 raw = load16(src);
-        const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
-        const float sc = kIsQuant<KT> && QT != KT ? (kv ? a.v_scale : a.k_scale)[g] : 1.0f;
-        unsigned char* dst = row + kv * R::ROW + piece * R::N * R::EC;
-        if constexpr (R::EC == R::ES) {
-            *reinterpret_cast<uint4*>(dst) = raw;
-        } else {
-            static_assert(R::EC == 1 && R::N == 8, "bf16 source, fp8 cache");
-            uint32_t c[8];
-#pragma unroll
-            for (int i = 0; i < 8; i++) c[i] = encode_elem<QT, KT>(words, i, sc);
-            *reinterpret_cast<uint2*>(dst) =
-                make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24, c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
-        }
-    }
+    return G * CG >= 16 ? 1 : 2;
+}
+
+template <int G>
+struct PieceMeta {
+    int64_t dst;    // whole run: its first output row; partial: the piece id; -1: nothing
+    int64_t run;    // the run whose chunk range is recorded for the merge, or -1
+    int64_t rtile;  // fused append: element offset of the new token's tile, or -1
+    int32_t k0, kn; // the chunk range
+    int32_t ro;     // fused append: the token's offset in its block
+    int32_t whole;
+    float ml[G][2]; // partial: (max, sum) per head
+};
+
+template <int QT, int KT, int D, int G, bool FUSED, int SLOTS>
+struct WaveStage {
+    using S = Shape<QT, KT, D, G>;
+    static constexpr int NS = SLOTS > 0 ? SLOTS : 1;
+    float v[NS][G * S::CG][64];  // value (h, cg) of lane l: the piece's output channel cg * 64 + l
+    PieceMeta<G> meta[NS];
+    // fused append: the new row of each slot, and one more for a piece written at once
+    unsigned char row[FUSED ? SLOTS + 1 : 1][FUSED ? 2 * NewRow<QT, KT, D>::ROW : 16];
+};
+
+__device__ __forceinline__ int64_t uniform64(int64_t x)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 // ---- the streaming kernel ---------------------------------------------------------------
@@ -562,7 +576,9 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
     const int Hkv = a.num_kv_heads, NS = a.num_seqs;
 
     __shared__ __align__(16) unsigned char q_lds[QL ? kDecodeWaves * S::QBYTES : 16];
-    __shared__ __align__(16) unsigned char nrow_lds[kDecodeWaves][FUSED ? 2 * NewRow<QT, KT, D>::ROW : 16];
+    constexpr int SLOTS = PER_RUN ? 0 : defer_slots<G, S::CG>();  // one run per chunk: nothing to defer
+    using Stage = WaveStage<QT, KT, D, G, FUSED, SLOTS>;
+    __shared__ __align__(16) Stage stage_lds[kDecodeWaves];
     extern __shared__ int lctx[];  // clamped context length of every sequence
 
     // All cursor moves read context lengths from LDS, so inside the stream the only global
@@ -652,12 +668,17 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
         // last block, whose entry then feeds the fill-in loads past the end)
         Cursor tc = cursor_at(p0, lctx, ush);
         int tcount = 0;
-        auto fetch_entry = [&](int& e, int& nv, int& g, int& sub, int& cached) {
+        constexpr bool fused = FUSED;
+        auto fetch_entry = [&](int& e, int& nv, int& g, int& sub, int& cached, int& es, int& last) {
             e = tables[(int64_t)tc.s * mbps + (tc.j >> ub)];
             nv = min(1 << ush, tc.ctx - (tc.j << ush));
             g = tc.g;
             sub = tc.j & ub;
             if constexpr (hint) cached = (tc.j >> ub) < lctx[NS + tc.s];
+            if constexpr (fused) {
+                es = tc.s;
+                last = tc.j == tc.nbs - 1;
+            }
             if (tcount + 1 < n) {
                 cursor_next(tc, lctx, NS, Hkv);
                 ++tcount;
@@ -667,11 +688,12 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
         Cursor cc = cursor_at(p0, lctx, ush);
         int piece_j0 = cc.j;
 
-        // entry ring: physical id, valid tokens, kv head and unit of the block, for units
-        // t .. t+NST-1
-        int ent[NST], ent_nv[NST], ent_g[NST], ent_sub[NST], ent_cached[NST] = {};
+        // entry ring: physical id, valid tokens, kv head and unit of the block (with the fused
+        // append: its sequence and whether it is its run's last unit), for units t .. t+NST-1
+        int ent[NST], ent_nv[NST], ent_g[NST], ent_sub[NST], ent_cached[NST] = {}, ent_s[NST] = {}, ent_last[NST] = {};
 #pragma unroll
-        for (int i = 0; i < NST; i++) fetch_entry(ent[i], ent_nv[i], ent_g[i], ent_sub[i], ent_cached[i]);
+        for (int i = 0; i < NST; i++)
+            fetch_entry(ent[i], ent_nv[i], ent_g[i], ent_sub[i], ent_cached[i], ent_s[i], ent_last[i]);
 
         auto query_row = [&](const Cursor& c) {
             return static_cast<const unsigned char*>(a.query) + ((int64_t)c.s * a.num_heads + (int64_t)c.g * G) * D * S::QB;
@@ -688,17 +710,10 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
                 load_q<QT, KT, D, G>(qr, query_row(c), lane & 3);
             }
         };
-        constexpr bool fused = FUSED;
-        unsigned char* const nrow = nrow_lds[wave_in_wg];
-        // a piece that will reach its run's last unit (the run ends inside this chunk) stages the
-        // run's new token
-        auto stage_if_run_ends = [&](const Cursor& c) {
-            if constexpr (fused) {
-                if (c.run_start + c.nbs <= u_end) stage_new_row<QT, KT, D>(a, c.s, c.g, nrow, lane);
-            }
-        };
+        Stage& ws = stage_lds[wave_in_wg];
+        using R = NewRow<QT, KT, D>;
+        int npend = 0;  // pieces in the stage
         load_query(cc);
-        stage_if_run_ends(cc);
         float c2 = a.scale_log2 * (kIsQuant<KT> ? a.k_scale[cc.g] : 1.0f);
 
         Acc<QT, KT, D, G> st;
@@ -715,7 +730,7 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
 
         // ---- end of a piece: fold the 8 token-pair lane groups of l, then write the row (a
         // run covered whole) or the partial result ----
-        auto finish_piece = [&]() {
+        auto finish_piece = [&](bool defer) {
 #pragma unroll
             for (int h = 0; h < G; h++) {
                 float x = st.l[h];
@@ -726,27 +741,54 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
             }
             const int64_t run = (int64_t)cc.s * Hkv + cc.g;
             const bool first = piece_j0 == 0, whole = first && cc.j == cc.nbs - 1;
-            if (first && lane == 0 && !per_run) {
-                // every run with blocks is entered at its block 0 by exactly one wave, which
-                // records the chunk range covering it for the merge
-                const int64_t k_last = cm.of_unit(cc.run_start + cc.nbs - 1);
+            // every run with blocks is entered at its block 0 by exactly one wave, which records
+            // the chunk range covering it for the merge
+            const bool rec = first && !per_run;
+            const int64_t k_last = rec ? cm.of_unit(cc.run_start + cc.nbs - 1) : k;
+            const int64_t piece = run + k;
+            const int64_t row0 = (int64_t)cc.s * a.num_heads + (int64_t)cc.g * G;
+            const float vs = whole && kIsQuant<KT> ? a.v_scale[cc.g] : 1.0f;
+            if constexpr (SLOTS > 0) {
+                if (defer) {
+                    PieceMeta<G>& me = ws.meta[npend];
+                    if (lane == 0) {
+                        me.dst = whole ? row0 : piece < a.max_pieces ? piece : -1;
+                        me.run = rec ? run : -1;
+                        me.rtile = -1;
+                        me.k0 = (int32_t)k;
+                        me.kn = (int32_t)(k_last - k + 1);
+                        me.whole = whole;
+#pragma unroll
+                        for (int h = 0; h < G; h++) {
+                            me.ml[h][0] = st.m[h];
+                            me.ml[h][1] = st.l[h];
+                        }
+                    }
+#pragma unroll
+                    for (int h = 0; h < G; h++) {
+                        const float f = st.l[h] > 0.0f ? vs / st.l[h] : 0.0f;
+#pragma unroll
+                        for (int cg = 0; cg < S::CG; cg++) ws.v[npend][h * S::CG + cg][lane] = st.o[cg][h] * f;
+                    }
+                    ++npend;
+                    return;
+                }
+            }
+            if (rec && lane == 0) {
                 a.run_info[2 * run] = (int32_t)k;
                 a.run_info[2 * run + 1] = (int32_t)(k_last - k + 1);
             }
-            const int64_t piece = run + k;
             if (whole) {
-                const float vs = kIsQuant<KT> ? a.v_scale[cc.g] : 1.0f;
 #pragma unroll
                 for (int h = 0; h < G; h++) {
                     const float f = st.l[h] > 0.0f ? vs / st.l[h] : 0.0f;
-                    const int64_t row = (int64_t)cc.s * a.num_heads + (int64_t)cc.g * G + h;
 #pragma unroll
                     for (int cg = 0; cg < S::CG; cg++) {
                         const float v = st.o[cg][h] * f;
                         if constexpr (QT == kBF16)
-                            static_cast<uint16_t*>(a.out)[row * D + cg * 64 + lane] = f32_to_bf16_bits(v);
+                            static_cast<uint16_t*>(a.out)[(row0 + h) * D + cg * 64 + lane] = f32_to_bf16_bits(v);
                         else
-                            static_cast<float*>(a.out)[row * D + cg * 64 + lane] = v;
+                            static_cast<float*>(a.out)[(row0 + h) * D + cg * 64 + lane] = v;
                     }
                 }
             } else if (piece < a.max_pieces) {
@@ -764,12 +806,68 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
             }
         };
 
+        // fused append: store the new row staged in slot r into the pool (lanes 0..2P-1)
+        auto store_row = [&](int r, int64_t tile, int o) {
+            if constexpr (fused) {
+                if (lane < 2 * R::P) {
+                    const int kv = lane / R::P, piece = lane % R::P;
+                    store_piece_bytes<KT, R::N>(ws.row[r] + kv * R::ROW + piece * R::N * R::EC,
+                                                static_cast<unsigned char*>(kv ? a.v_pool : a.k_pool), tile,
+                                                piece * R::N, o, kv, D, a.block_size);
+                }
+            }
+        };
+
+        // write what the stage holds (after the chunk's last unit)
+        auto flush = [&]() {
+            if constexpr (SLOTS > 0) {
+                for (int i = 0; i < npend; i++) {
+                    const PieceMeta<G>& me = ws.meta[i];
+                    const int64_t dst = uniform64(me.dst), run = uniform64(me.run);
+                    const bool whole = __builtin_amdgcn_readfirstlane(me.whole) != 0;
+                    if (run >= 0 && lane == 0) {
+                        a.run_info[2 * run] = me.k0;
+                        a.run_info[2 * run + 1] = me.kn;
+                    }
+                    if (whole) {
+#pragma unroll
+                        for (int h = 0; h < G; h++)
+#pragma unroll
+                            for (int cg = 0; cg < S::CG; cg++) {
+                                const float v = ws.v[i][h * S::CG + cg][lane];
+                                if constexpr (QT == kBF16)
+                                    static_cast<uint16_t*>(a.out)[(dst + h) * D + cg * 64 + lane] = f32_to_bf16_bits(v);
+                                else
+                                    static_cast<float*>(a.out)[(dst + h) * D + cg * 64 + lane] = v;
+                            }
+                    } else if (dst >= 0) {
+#pragma unroll
+                        for (int h = 0; h < G; h++) {
+#pragma unroll
+                            for (int cg = 0; cg < S::CG; cg++)
+                                a.o_part[(dst * G + h) * D + cg * 64 + lane] = ws.v[i][h * S::CG + cg][lane];
+                            if (lane == 0) {
+                                a.ml_part[(dst * G + h) * 2] = me.ml[h][0];
+                                a.ml_part[(dst * G + h) * 2 + 1] = me.ml[h][1];
+                            }
+                        }
+                    }
+                    if constexpr (fused) {
+                        const int64_t rtile = uniform64(me.rtile);
+                        if (rtile >= 0) store_row(i, rtile, me.ro);
+                    }
+                }
+                npend = 0;
+            }
+        };
+
         // ---- the stream: step t issues block t into ring slot t % NST (blocks past the end
         // re-read the chunk's last block and are never attended), refills the entry ring with
         // block t + NST, and attends block t - (NST - 1) ----
         uint4 kb[NST][S::NCH], vb[NST][S::NCH];
         int kv_nv[NST];
-        int64_t kv_koff[NST], kv_voff[NST];  // byte offsets of the unit's K and V in the pools
+        uint4 nrw[NST];     // fused append: the new row piece loaded with the run's last unit
+        int kv_phys[NST];   // fused append: the unit's physical block
         for (int t0 = 0; t0 < n + NST - 1; t0 += NST) {
 #pragma unroll
             for (int i = 0; i < NST; i++) {
@@ -788,8 +886,6 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
                     const int sub = __builtin_amdgcn_readfirstlane(ent_sub[i]);
                     const int gu = __builtin_amdgcn_readfirstlane(ent_g[i]);
                     const int64_t off = (int64_t)phys * block_stride + (int64_t)gu * btile;
-                    kv_koff[i] = off + sub * 1024;
-                    kv_voff[i] = off + sub * S::TILE;
                     const TileWindow kw(kpool + off + sub * 1024, none ? 0 : btile - sub * 1024);
                     const TileWindow vw(vpool + off + sub * S::TILE, none ? 0 : vwin);
                     // a block shared with other sequences keeps the default cache policy, so its
@@ -805,45 +901,70 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
 #pragma unroll
                         for (int c = 0; c < S::NCH; c++) vb[i][c] = vw.load_stream(lane * 16 + c * 1024);
                     }
+                    if constexpr (fused) {
+                        // with its run's last unit (a valid block): lanes 0..P-1 load the K row's
+                        // pieces, P..2P-1 the V row's; every other lane and step loads the first 16
+                        // bytes of new_key, so the instruction stream stays the same
+                        const int sn = __builtin_amdgcn_readfirstlane(ent_s[i]);
+                        const bool want = !none && __builtin_amdgcn_readfirstlane(ent_last[i]);
+                        const int64_t roff = (((int64_t)sn * Hkv + gu) * D) * R::ES;
+                        const unsigned char* src = static_cast<const unsigned char*>(a.new_key);
+                        if (want && lane < 2 * R::P)
+                            src = lane < R::P ? src + roff + lane * 16
+                                              : static_cast<const unsigned char*>(a.new_value) + roff + (lane - R::P) * 16;
+                        nrw[i] = load16(src);
+                        kv_phys[i] = phys;
+                    }
                 }
-                fetch_entry(ent[i], ent_nv[i], ent_g[i], ent_sub[i], ent_cached[i]);
+                fetch_entry(ent[i], ent_nv[i], ent_g[i], ent_sub[i], ent_cached[i], ent_s[i], ent_last[i]);
 
                 const int ta = t - (NST - 1);
                 if (ta >= 0 && ta < n) {
                     const int j = (i + 1) % NST;  // the slot issued NST-1 steps ago
                     if (ta > 0 && cc.j == 0) {       // a new run: start its piece
                         load_query(cc);
-                        stage_if_run_ends(cc);
                         c2 = a.scale_log2 * (kIsQuant<KT> ? a.k_scale[cc.g] : 1.0f);
                         reset();
                         piece_j0 = 0;
                     }
-                    // fused append: the run's last unit holds the new token at index nv - 1.  The
-                    // ring's copy of that slot may predate this launch's store, so the token's
-                    // K and V are patched in from the staged row before the unit is attended
-                    // (the same values in the same places as after pa_kv_cache_write), and the
-                    // row is stored into the slot.
+                    // fused append: the run's last unit holds the new token at index nv - 1.  Its
+                    // row pieces are encoded and staged in LDS; the ring's copy of the slot may
+                    // predate this launch's store, so the token's K and V are patched in from
+                    // the staged row before the unit is attended.
                     if constexpr (fused) {
                         if (cc.j == cc.nbs - 1 && kv_nv[j] > 0) {
                             const int tn = kv_nv[j] - 1;  // the new token's index in the unit
+                            unsigned char* const nrow = ws.row[npend];  // the slot this piece takes
+                            if (lane < 2 * R::P) {
+                                const int kv = lane / R::P, piece = lane % R::P;
+                                unsigned char* dst = nrow + kv * R::ROW + piece * R::N * R::EC;
+                                if constexpr (R::EC == R::ES) {
+                                    *reinterpret_cast<uint4*>(dst) = nrw[j];
+                                } else {
+                                    static_assert(R::EC == 1 && R::N == 8, "bf16 source, 8-bit cache");
+                                    const int gc = __builtin_amdgcn_readfirstlane(cc.g);
+                                    const float sc = kv ? a.v_scale[gc] : a.k_scale[gc];
+                                    const uint32_t words[4] = {nrw[j].x, nrw[j].y, nrw[j].z, nrw[j].w};
+                                    uint32_t code[R::N];
+#pragma unroll
+                                    for (int e = 0; e < R::N; e++) code[e] = encode_elem<QT, KT>(words, e, sc);
+                                    *reinterpret_cast<uint2*>(dst) =
+                                        make_uint2(code[0] | code[1] << 8 | code[2] << 16 | code[3] << 24,
+                                                   code[4] | code[5] << 8 | code[6] << 16 | code[7] << 24);
+                                }
+                            }
                             const bool mine = (lane >> 2) == tn;  // K: the 4 lanes of token tn
-                            unsigned char* kdst = static_cast<unsigned char*>(a.k_pool) + kv_koff[j];
 #pragma unroll
                             for (int c = 0; c < S::NCH; c++) {
                                 const uint4 kn =
                                     *reinterpret_cast<const uint4*>(nrow + (c * S::W + (lane & 3) * S::KE) * S::EB);
-                                if (mine) {
-                                    kb[j][c] = kn;
-                                    *reinterpret_cast<uint4*>(kdst + c * kstride + lane * 16) = kn;
-                                }
+                                if (mine) kb[j][c] = kn;
                             }
                             // V: lane l holds channel cg * 64 + l; token tn is element tn % TPC of
                             // the channel's 16-byte piece in token group tn / TPC
                             const int qn = tn / S::TPC, en = tn % S::TPC;
                             const int wn = en * S::EB / 4, sh = (en * S::EB % 4) * 8;
                             constexpr uint32_t emask = S::EB == 4 ? 0xFFFFFFFFu : (1u << (8 * S::EB)) - 1u;
-                            unsigned char* vdst = static_cast<unsigned char*>(a.v_pool) + kv_voff[j] +
-                                                  qn * S::CG * 1024 + lane * 16 + en * S::EB;
 #pragma unroll
                             for (int c = 0; c < S::NCH; c++) {  // constant indices keep the ring in VGPRs
                                 const int cg = c % S::CG;
@@ -862,12 +983,6 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
                                 w.y = wn == 1 ? (w.y & keep) | put : w.y;
                                 w.z = wn == 2 ? (w.z & keep) | put : w.z;
                                 w.w = wn == 3 ? (w.w & keep) | put : w.w;
-                                if constexpr (S::EB == 4)
-                                    *reinterpret_cast<uint32_t*>(vdst + cg * 1024) = v;
-                                else if constexpr (S::EB == 2)
-                                    *reinterpret_cast<uint16_t*>(vdst + cg * 1024) = (uint16_t)v;
-                                else
-                                    vdst[cg * 1024] = (unsigned char)v;
                             }
                         }
                     }
@@ -877,11 +992,34 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
                     } else {
                         attend_block<QT, KT, D, G>(st, qr, kb[j], vb[j], kv_nv[j], c2, lane);
                     }
-                    if (cc.j == cc.nbs - 1 || ta == n - 1) finish_piece();
+                    if (cc.j == cc.nbs - 1 || ta == n - 1) {
+                        // a piece ending inside the chunk goes to the stage while it has room
+                        const bool defer = SLOTS > 0 && ta < n - 1 && npend < SLOTS;
+                        const int r = npend;  // its slot (the fused append staged its row there)
+                        finish_piece(defer);
+                        // fused append: the staged row goes into the slot, token
+                        // ((unit & ub) * 16 + tn) of the block
+                        if constexpr (fused) {
+                            if (cc.j == cc.nbs - 1 && kv_nv[j] > 0) {
+                                const int gc = __builtin_amdgcn_readfirstlane(cc.g);
+                                const int64_t tile = ((int64_t)kv_phys[j] * Hkv + gc) * (int64_t)a.block_size * D;
+                                const int o = ((cc.j & ub) << 4) + kv_nv[j] - 1;
+                                if (defer) {
+                                    if (lane == 0) {
+                                        ws.meta[r].rtile = tile;
+                                        ws.meta[r].ro = o;
+                                    }
+                                } else {
+                                    store_row(r, tile, o);
+                                }
+                            }
+                        }
+                    }
                     if (ta < n - 1) cursor_next(cc, lctx, NS, Hkv);
                 }
             }
         }
+        flush();
     }
 }
 
