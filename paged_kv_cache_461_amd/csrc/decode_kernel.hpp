@@ -42,6 +42,8 @@
 
 #include <float.h>
 
+#include <type_traits>
+
 #include "kv_store.hpp"
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
@@ -303,6 +305,159 @@ __device__ __forceinline__ void attend_block(Acc<QT, KT, D, G>& st, const QSrc& 
     }
 }
 
+// ---- the matrix-core form (bf16 and 8-bit caches) ----------------------------------------
+//
+// Per 16-token unit, with the GQA group's G heads as the columns of 16 x 16 MFMA tiles
+// (columns G..15 are zero):
+//   S^T (16 tokens x 16 heads) = K Q^T in D/32 steps of v_mfma_f32_16x16x32_bf16: A = K, lane l
+//     holding token l % 16 and 8 channels (an 8-bit cache: a 16-byte piece of 16 channels,
+//     widened exactly to bf16, feeds two steps); B = the query, lane l holding head l % 16 and
+//     the same channels, in VGPRs for the piece.
+//   Softmax on the accumulator: lane l holds the scores of head l % 16 for tokens
+//     4 (l / 16) .. + 3, which -- rounded to bf16 -- is the B operand of the next product, so
+//     the weights never leave the lane.  The running max of a head is the same in its 4 lanes.
+//   O^T (16 channels x 16 heads) += V^T P^T in D/16 tiles of v_mfma_f32_16x16x16_bf16: A = V,
+//     lane l holding channel l % 16 of the tile and tokens 4 (l / 16) .. + 3 (8 bytes of bf16,
+//     4 bytes of an 8-bit cache: one load per tile, read straight from the pool layout).
+// The accumulator of lane l holds head l % 16, channels 16 t + 4 (l / 16) .. + 3 of tile t.
+typedef __bf16 mf_bf16x8 __attribute__((ext_vector_type(8)));
+typedef short mf_s16x4 __attribute__((ext_vector_type(4)));
+typedef float mf_f32x4 __attribute__((ext_vector_type(4)));
+
+template <int QT, int KT, int D, int G>
+struct MShape {
+    static constexpr int EB = DtypeBytes<KT>::value;
+    static constexpr int NCH = D * EB / 64;  // 1 KiB K slices per unit
+    static constexpr int KS = D / 32;        // S^T steps
+    static constexpr int NT = D / 16;        // O^T tiles
+    using VP = std::conditional_t<EB == 2, uint2, uint32_t>;  // a lane's V piece of one tile
+    static_assert(QT == kBF16 && (EB == 2 || EB == 1), "bf16 queries over a bf16 or 8-bit cache");
+    static_assert(G <= 16, "the GQA group fits the 16 columns of a tile");
+};
+
+template <int QT, int KT, int D, int G>
+struct MQ {
+    mf_bf16x8 w[MShape<QT, KT, D, G>::KS];
+};
+
+template <int QT, int KT, int D, int G>
+struct MAcc {
+    mf_f32x4 o[MShape<QT, KT, D, G>::NT];
+    float m, l;  // of head lane % 16
+};
+
+// Channel c of step st for lane group grp (lanes 16 grp .. 16 grp + 15), element e: the
+// channels that lane's K piece holds (a bf16 slice is 32 channels, 8 per lane group; an 8-bit
+// slice 64, 16 per lane group, split over two steps).
+template <int EB>
+__device__ __forceinline__ int mf_channel(int st, int grp)
+{
+    return EB == 2 ? st * 32 + 8 * grp : (st >> 1) * 64 + 16 * grp + 8 * (st & 1);
+}
+
+template <int QT, int KT, int D, int G>
+__device__ __forceinline__ void load_q_mf(MQ<QT, KT, D, G>& q, const unsigned char* qrow, int lane)
+{
+    using M = MShape<QT, KT, D, G>;
+    const int h = lane & 15, grp = lane >> 4;
+    const int hh = h < G ? h : 0;
+#pragma unroll
+    for (int st = 0; st < M::KS; st++) {
+        const uint4 v = load16(qrow + (hh * D + mf_channel<M::EB>(st, grp)) * 2);
+        const uint4 z = h < G ? v : make_uint4(0u, 0u, 0u, 0u);
+        q.w[st] = __builtin_bit_cast(mf_bf16x8, z);
+    }
+}
+
+// One step of a sum (sum_or_max = false) or max over the four 16-lane groups holding one
+// head: v_permlane16_swap pairs each 16-lane row with its neighbour, v_permlane32_swap each
+// half of the wave with the other.
+__device__ __forceinline__ float mf_swap(float x, bool halves, bool is_max)
+{
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto p = halves ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                          : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const uint32_t p0 = p[0], p1 = p[1];  // (a bit_cast of the vector elements themselves reads
+                                          // element 0 twice with this compiler)
+    const float a = __builtin_bit_cast(float, p0), b = __builtin_bit_cast(float, p1);
+    return is_max ? __builtin_fmaxf(a, b) : a + b;
+}
+
+// Four bf16 (or four 8-bit codes widened to bf16) of lane's V piece, elements at or past
+// `keep` zeroed (they may hold anything, including NaN, and 0 * NaN would leak into the sum).
+template <int KT>
+__device__ __forceinline__ uint2 mf_v_operand(const typename MShape<kBF16, KT, 64, 1>::VP& v, int keep)
+{
+    uint2 r;
+    if constexpr (DtypeBytes<KT>::value == 2)
+        r = v;
+    else
+        r = make_uint2(q8x2_to_bf16x2<KT, false>(v), q8x2_to_bf16x2<KT, true>(v));
+    if (keep < 4) {
+        r.x = keep >= 2 ? r.x : keep == 1 ? r.x & 0xFFFFu : 0u;
+        r.y = keep >= 4 ? r.y : keep == 3 ? r.y & 0xFFFFu : 0u;
+    }
+    return r;
+}
+
+template <int QT, int KT, int D, int G>
+__device__ __forceinline__ void attend_mfma(MAcc<QT, KT, D, G>& st, const MQ<QT, KT, D, G>& q,
+                                            const uint4 (&kb)[MShape<QT, KT, D, G>::NCH],
+                                            const typename MShape<QT, KT, D, G>::VP (&vb)[MShape<QT, KT, D, G>::NT],
+                                            int n_valid, float c2, int lane)
+{
+    using M = MShape<QT, KT, D, G>;
+    mf_f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < M::NCH; c++) {
+        if constexpr (M::EB == 2) {
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mf_bf16x8, kb[c]), q.w[c], sacc, 0, 0, 0);
+        } else {
+            const uint4 k = kb[c];
+            const uint4 lo = make_uint4(q8x2_to_bf16x2<KT, false>(k.x), q8x2_to_bf16x2<KT, true>(k.x),
+                                        q8x2_to_bf16x2<KT, false>(k.y), q8x2_to_bf16x2<KT, true>(k.y));
+            const uint4 hi = make_uint4(q8x2_to_bf16x2<KT, false>(k.z), q8x2_to_bf16x2<KT, true>(k.z),
+                                        q8x2_to_bf16x2<KT, false>(k.w), q8x2_to_bf16x2<KT, true>(k.w));
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mf_bf16x8, lo), q.w[2 * c], sacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mf_bf16x8, hi), q.w[2 * c + 1], sacc, 0, 0, 0);
+        }
+    }
+    const int tb = 4 * (lane >> 4);  // this lane's first token
+    float s2[4] = {sacc[0], sacc[1], sacc[2], sacc[3]};
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        s2[r] *= c2;
+        if (n_valid < kUnitTokens) s2[r] = tb + r < n_valid ? s2[r] : -__builtin_inff();
+    }
+    bool need = false;
+#pragma unroll
+    for (int r = 0; r < 4; r++) need |= s2[r] > st.m + kRescaleMargin;
+    if (__builtin_amdgcn_ballot_w64(need && (lane & 15) < G) != 0) {
+        float mx = __builtin_fmaxf(__builtin_fmaxf(s2[0], s2[1]), __builtin_fmaxf(s2[2], s2[3]));
+        mx = mf_swap(mx, false, true);
+        mx = mf_swap(mx, true, true);
+        const float mn = __builtin_fmaxf(st.m, mx);
+        const float alpha = fast_exp2(st.m - mn);
+        st.m = mn;
+        st.l *= alpha;
+#pragma unroll
+        for (int t = 0; t < M::NT; t++) st.o[t] *= alpha;
+    }
+    const uint32_t pp0 = pack_bf16x2(fast_exp2(s2[0] - st.m), fast_exp2(s2[1] - st.m));
+    const uint32_t pp1 = pack_bf16x2(fast_exp2(s2[2] - st.m), fast_exp2(s2[3] - st.m));
+    // l sums the weights as rounded for the product (each lane its 4 tokens; the 4 lane
+    // groups of a head are folded at the end of the piece)
+    st.l = dot2_bf16(pp0, kBf16OnePair, st.l);
+    st.l = dot2_bf16(pp1, kBf16OnePair, st.l);
+    const mf_s16x4 pb = __builtin_bit_cast(mf_s16x4, make_uint2(pp0, pp1));
+    const int keep = n_valid - tb;
+#pragma unroll
+    for (int t = 0; t < M::NT; t++) {
+        const uint2 av = mf_v_operand<KT>(vb[t], keep);
+        st.o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(mf_s16x4, av), pb, st.o[t], 0, 0, 0);
+    }
+}
+
 // ---- work-list arithmetic ---------------------------------------------------------------
 
 // Context length the kernels use for sequence s: clamped to [0, max_context_len], so a
@@ -500,7 +655,7 @@ template <int QT, int KT, int D, int G, bool FUSED, int SLOTS>
 struct WaveStage {
     using S = Shape<QT, KT, D, G>;
     static constexpr int NS = SLOTS > 0 ? SLOTS : 1;
-    float v[NS][G * S::CG][64];  // value (h, cg) of lane l: the piece's output channel cg * 64 + l
+    float v[NS][G * D];  // the piece's output rows (head-major), normalised
     PieceMeta<G> meta[NS];
     // fused append: the new row of each slot, and one more for a piece written at once
     unsigned char row[FUSED ? SLOTS + 1 : 1][FUSED ? 2 * NewRow<QT, KT, D>::ROW : 16];
@@ -569,6 +724,9 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
     using S = Shape<QT, KT, D, G>;
     constexpr bool QL = Variant<KT>::kQueryInLds;
     constexpr int NST = Variant<KT>::kDepth;
+    constexpr bool MF = KT != kF32;  // the matrix-core form (bf16 and 8-bit caches)
+    constexpr int KM = MF ? KT : kBF16;
+    using M = MShape<kBF16, KM, D, G>;
     const int lane = threadIdx.x & 63;
     const int wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t NW = (int64_t)gridDim.x * kDecodeWaves;
@@ -623,7 +781,15 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
     const int ush = unit_shift(a.block_size);
     const int btile = a.block_size * D * S::EB;  // bytes of one (block, kv head) tile
     const int vwin = btile < S::TILE ? btile : S::TILE;
-    const int kvoff = a.block_size < kUnitTokens && lane >= 32 ? 0x40000000 : lane * 16;
+    // K: lane l reads token l / 4 (matrix-core form: token l % 16), 16 bytes of each slice
+    const int ktok = MF ? (lane & 15) : (lane >> 2);
+    const int kvoff = a.block_size < kUnitTokens && ktok >= 8 ? 0x40000000
+                      : MF                                   ? ktok * 64 + (lane >> 4) * 16
+                                                             : lane * 16;
+    // matrix-core form, V: lane l reads tokens 4 (l / 16) .. + 3 of channel l % 16 of each
+    // 16-channel tile (tile t at t * 256 bytes of the unit's token group)
+    const int mvoff = M::EB == 2 ? (((lane >> 5) * D + (lane & 15)) * 16 + ((lane >> 4) & 1) * 8)
+                                 : ((lane & 15) * 16 + (lane >> 4) * 4);
     const int kstride = a.block_size * 64;
     const int64_t block_stride = (int64_t)Hkv * btile;
     const int32_t* tables = a.block_tables;
@@ -698,7 +864,7 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
         auto query_row = [&](const Cursor& c) {
             return static_cast<const unsigned char*>(a.query) + ((int64_t)c.s * a.num_heads + (int64_t)c.g * G) * D * S::QB;
         };
-        QRegs<QT, KT, D, G> qr;
+        std::conditional_t<MF, MQ<kBF16, KM, D, G>, QRegs<QT, KT, D, G>> qr;
         const int q_off = wave_in_wg * S::QBYTES;
         auto load_query = [&](const Cursor& c) {
             if constexpr (QL) {
@@ -706,6 +872,8 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
                 for (int off = 0; off < S::QBYTES; off += 1024)
                     if (off + lane * 16 < S::QBYTES)
                         *reinterpret_cast<uint4*>(q_lds + q_off + off + lane * 16) = load16(query_row(c) + off + lane * 16);
+            } else if constexpr (MF) {
+                load_q_mf(qr, query_row(c), lane);
             } else {
                 load_q<QT, KT, D, G>(qr, query_row(c), lane & 3);
             }
@@ -716,28 +884,42 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
         load_query(cc);
         float c2 = a.scale_log2 * (kIsQuant<KT> ? a.k_scale[cc.g] : 1.0f);
 
-        Acc<QT, KT, D, G> st;
+        std::conditional_t<MF, MAcc<kBF16, KM, D, G>, Acc<QT, KT, D, G>> st;
         auto reset = [&]() {
+            if constexpr (MF) {
+                st.m = -FLT_MAX;
+                st.l = 0.0f;
 #pragma unroll
-            for (int h = 0; h < G; h++) {
-                st.m[h] = -FLT_MAX;
-                st.l[h] = 0.0f;
+                for (int t = 0; t < M::NT; t++) st.o[t] = mf_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            } else {
 #pragma unroll
-                for (int cg = 0; cg < S::CG; cg++) st.o[cg][h] = 0.0f;
+                for (int h = 0; h < G; h++) {
+                    st.m[h] = -FLT_MAX;
+                    st.l[h] = 0.0f;
+#pragma unroll
+                    for (int cg = 0; cg < S::CG; cg++) st.o[cg][h] = 0.0f;
+                }
             }
         };
         reset();
 
-        // ---- end of a piece: fold the 8 token-pair lane groups of l, then write the row (a
-        // run covered whole) or the partial result ----
+        // ---- end of a piece: fold l over the lanes that summed parts of it (the 8 token-pair
+        // lane groups; matrix-core form: the 4 lane groups of a head), then write the row (a run
+        // covered whole) or the partial result ----
+        const int mh = lane & 15, mtb = 4 * (lane >> 4);  // matrix-core form: lane's head, first channel
         auto finish_piece = [&](bool defer) {
+            if constexpr (MF) {
+                st.l = mf_swap(st.l, false, false);
+                st.l = mf_swap(st.l, true, false);
+            } else {
 #pragma unroll
-            for (int h = 0; h < G; h++) {
-                float x = st.l[h];
-                x += dpp_f32<kDppRowRor8>(x);
-                x += swizzle_xor16(x);
-                x += __shfl_xor(x, 32, 64);
-                st.l[h] = x;
+                for (int h = 0; h < G; h++) {
+                    float x = st.l[h];
+                    x += dpp_f32<kDppRowRor8>(x);
+                    x += swizzle_xor16(x);
+                    x += __shfl_xor(x, 32, 64);
+                    st.l[h] = x;
+                }
             }
             const int64_t run = (int64_t)cc.s * Hkv + cc.g;
             const bool first = piece_j0 == 0, whole = first && cc.j == cc.nbs - 1;
@@ -758,17 +940,33 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
                         me.k0 = (int32_t)k;
                         me.kn = (int32_t)(k_last - k + 1);
                         me.whole = whole;
+                    }
+                    float* v = ws.v[npend];
+                    if constexpr (MF) {
+                        if (lane < G) {
+                            me.ml[lane][0] = st.m;
+                            me.ml[lane][1] = st.l;
+                        }
+                        if (mh < G) {
+                            const float f = st.l > 0.0f ? vs / st.l : 0.0f;
+#pragma unroll
+                            for (int t = 0; t < M::NT; t++)
+                                *reinterpret_cast<mf_f32x4*>(v + mh * D + 16 * t + mtb) = st.o[t] * f;
+                        }
+                    } else {
+                        if (lane == 0) {
+#pragma unroll
+                            for (int h = 0; h < G; h++) {
+                                me.ml[h][0] = st.m[h];
+                                me.ml[h][1] = st.l[h];
+                            }
+                        }
 #pragma unroll
                         for (int h = 0; h < G; h++) {
-                            me.ml[h][0] = st.m[h];
-                            me.ml[h][1] = st.l[h];
+                            const float f = st.l[h] > 0.0f ? vs / st.l[h] : 0.0f;
+#pragma unroll
+                            for (int cg = 0; cg < S::CG; cg++) v[h * D + cg * 64 + lane] = st.o[cg][h] * f;
                         }
-                    }
-#pragma unroll
-                    for (int h = 0; h < G; h++) {
-                        const float f = st.l[h] > 0.0f ? vs / st.l[h] : 0.0f;
-#pragma unroll
-                        for (int cg = 0; cg < S::CG; cg++) ws.v[npend][h * S::CG + cg][lane] = st.o[cg][h] * f;
                     }
                     ++npend;
                     return;
@@ -778,7 +976,28 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
                 a.run_info[2 * run] = (int32_t)k;
                 a.run_info[2 * run + 1] = (int32_t)(k_last - k + 1);
             }
-            if (whole) {
+            if constexpr (MF) {
+                if (mh < G) {
+                    if (whole) {
+                        const float f = st.l > 0.0f ? vs / st.l : 0.0f;
+                        uint16_t* orow = static_cast<uint16_t*>(a.out) + (row0 + mh) * D + mtb;
+#pragma unroll
+                        for (int t = 0; t < M::NT; t++) {
+                            const mf_f32x4 x = st.o[t] * f;
+                            *reinterpret_cast<uint2*>(orow + 16 * t) = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+                        }
+                    } else if (piece < a.max_pieces) {
+                        const float f = st.l > 0.0f ? 1.0f / st.l : 0.0f;
+                        float* op = a.o_part + (piece * G + mh) * D + mtb;
+#pragma unroll
+                        for (int t = 0; t < M::NT; t++) *reinterpret_cast<mf_f32x4*>(op + 16 * t) = st.o[t] * f;
+                        if (lane < G) {
+                            a.ml_part[(piece * G + mh) * 2] = st.m;
+                            a.ml_part[(piece * G + mh) * 2 + 1] = st.l;
+                        }
+                    }
+                }
+            } else if (whole) {
 #pragma unroll
                 for (int h = 0; h < G; h++) {
                     const float f = st.l[h] > 0.0f ? vs / st.l[h] : 0.0f;
@@ -825,27 +1044,50 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
                     const PieceMeta<G>& me = ws.meta[i];
                     const int64_t dst = uniform64(me.dst), run = uniform64(me.run);
                     const bool whole = __builtin_amdgcn_readfirstlane(me.whole) != 0;
+                    const float* v = ws.v[i];
                     if (run >= 0 && lane == 0) {
                         a.run_info[2 * run] = me.k0;
                         a.run_info[2 * run + 1] = me.kn;
                     }
-                    if (whole) {
+                    if constexpr (MF) {
+                        if (mh < G) {
+                            if (whole) {
+                                uint16_t* orow = static_cast<uint16_t*>(a.out) + (dst + mh) * D + mtb;
+#pragma unroll
+                                for (int t = 0; t < M::NT; t++) {
+                                    const mf_f32x4 x = *reinterpret_cast<const mf_f32x4*>(v + mh * D + 16 * t + mtb);
+                                    *reinterpret_cast<uint2*>(orow + 16 * t) =
+                                        make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+                                }
+                            } else if (dst >= 0) {
+                                float* op = a.o_part + (dst * G + mh) * D + mtb;
+#pragma unroll
+                                for (int t = 0; t < M::NT; t++)
+                                    *reinterpret_cast<mf_f32x4*>(op + 16 * t) =
+                                        *reinterpret_cast<const mf_f32x4*>(v + mh * D + 16 * t + mtb);
+                                if (lane < G) {
+                                    a.ml_part[(dst * G + mh) * 2] = me.ml[mh][0];
+                                    a.ml_part[(dst * G + mh) * 2 + 1] = me.ml[mh][1];
+                                }
+                            }
+                        }
+                    } else if (whole) {
 #pragma unroll
                         for (int h = 0; h < G; h++)
 #pragma unroll
                             for (int cg = 0; cg < S::CG; cg++) {
-                                const float v = ws.v[i][h * S::CG + cg][lane];
+                                const float x = v[h * D + cg * 64 + lane];
                                 if constexpr (QT == kBF16)
-                                    static_cast<uint16_t*>(a.out)[(dst + h) * D + cg * 64 + lane] = f32_to_bf16_bits(v);
+                                    static_cast<uint16_t*>(a.out)[(dst + h) * D + cg * 64 + lane] = f32_to_bf16_bits(x);
                                 else
-                                    static_cast<float*>(a.out)[(dst + h) * D + cg * 64 + lane] = v;
+                                    static_cast<float*>(a.out)[(dst + h) * D + cg * 64 + lane] = x;
                             }
                     } else if (dst >= 0) {
 #pragma unroll
                         for (int h = 0; h < G; h++) {
 #pragma unroll
                             for (int cg = 0; cg < S::CG; cg++)
-                                a.o_part[(dst * G + h) * D + cg * 64 + lane] = ws.v[i][h * S::CG + cg][lane];
+                                a.o_part[(dst * G + h) * D + cg * 64 + lane] = v[h * D + cg * 64 + lane];
                             if (lane == 0) {
                                 a.ml_part[(dst * G + h) * 2] = me.ml[h][0];
                                 a.ml_part[(dst * G + h) * 2 + 1] = me.ml[h][1];
@@ -864,7 +1106,9 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
         // ---- the stream: step t issues block t into ring slot t % NST (blocks past the end
         // re-read the chunk's last block and are never attended), refills the entry ring with
         // block t + NST, and attends block t - (NST - 1) ----
-        uint4 kb[NST][S::NCH], vb[NST][S::NCH];
+        uint4 kb[NST][S::NCH];
+        // V: 16 bytes per slice; matrix-core form: one piece per 16-channel tile
+        std::conditional_t<MF, typename M::VP, uint4> vb[NST][MF ? M::NT : S::NCH];
         int kv_nv[NST];
         uint4 nrw[NST];     // fused append: the new row piece loaded with the run's last unit
         int kv_phys[NST];   // fused append: the unit's physical block
@@ -890,7 +1134,20 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
                     const TileWindow vw(vpool + off + sub * S::TILE, none ? 0 : vwin);
                     // a block shared with other sequences keeps the default cache policy, so its
                     // other readers find it cached; the rest are read once and streamed (nt)
-                    if (hint && __builtin_amdgcn_readfirstlane(ent_cached[i])) {
+                    if constexpr (MF) {
+                        const bool cached = hint && __builtin_amdgcn_readfirstlane(ent_cached[i]);
+                        if (cached) {
+#pragma unroll
+                            for (int c = 0; c < S::NCH; c++) kb[i][c] = kw.load_cached(kvoff, c * kstride);
+#pragma unroll
+                            for (int t = 0; t < M::NT; t++) vb[i][t] = vw.template load_piece<typename M::VP>(mvoff, t * 256, true);
+                        } else {
+#pragma unroll
+                            for (int c = 0; c < S::NCH; c++) kb[i][c] = kw.load_stream(kvoff, c * kstride);
+#pragma unroll
+                            for (int t = 0; t < M::NT; t++) vb[i][t] = vw.template load_piece<typename M::VP>(mvoff, t * 256, false);
+                        }
+                    } else if (hint && __builtin_amdgcn_readfirstlane(ent_cached[i])) {
 #pragma unroll
                         for (int c = 0; c < S::NCH; c++) kb[i][c] = kw.load_cached(kvoff, c * kstride);
 #pragma unroll
@@ -953,42 +1210,68 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
                                                    code[4] | code[5] << 8 | code[6] << 16 | code[7] << 24);
                                 }
                             }
-                            const bool mine = (lane >> 2) == tn;  // K: the 4 lanes of token tn
+                            // K: the lanes of token tn (lane / 4; matrix-core form: lane % 16) take
+                            // their channels of each slice from the row
+                            const bool mine = ktok == tn;
+                            const int kq = MF ? (lane >> 4) : (lane & 3);
 #pragma unroll
                             for (int c = 0; c < S::NCH; c++) {
-                                const uint4 kn =
-                                    *reinterpret_cast<const uint4*>(nrow + (c * S::W + (lane & 3) * S::KE) * S::EB);
+                                const uint4 kn = *reinterpret_cast<const uint4*>(nrow + (c * S::W + kq * S::KE) * S::EB);
                                 if (mine) kb[j][c] = kn;
                             }
-                            // V: lane l holds channel cg * 64 + l; token tn is element tn % TPC of
-                            // the channel's 16-byte piece in token group tn / TPC
-                            const int qn = tn / S::TPC, en = tn % S::TPC;
-                            const int wn = en * S::EB / 4, sh = (en * S::EB % 4) * 8;
-                            constexpr uint32_t emask = S::EB == 4 ? 0xFFFFFFFFu : (1u << (8 * S::EB)) - 1u;
+                            if constexpr (MF) {
+                                // V: lane l holds tokens 4 (l / 16) .. + 3 of channel 16 t + l % 16;
+                                // the lanes of token tn replace element tn % 4
+                                const bool vmine = (lane >> 4) == (tn >> 2);
+                                const int en = tn & 3;
 #pragma unroll
-                            for (int c = 0; c < S::NCH; c++) {  // constant indices keep the ring in VGPRs
-                                const int cg = c % S::CG;
-                                if (c / S::CG != qn) continue;
-                                const unsigned char* e = nrow + NewRow<QT, KT, D>::ROW + (cg * 64 + lane) * S::EB;
-                                uint32_t v;
-                                if constexpr (S::EB == 4)
-                                    v = *reinterpret_cast<const uint32_t*>(e);
-                                else if constexpr (S::EB == 2)
-                                    v = *reinterpret_cast<const uint16_t*>(e);
-                                else
-                                    v = *e;
-                                uint4& w = vb[j][c];
-                                const uint32_t put = v << sh, keep = ~(emask << sh);
-                                w.x = wn == 0 ? (w.x & keep) | put : w.x;
-                                w.y = wn == 1 ? (w.y & keep) | put : w.y;
-                                w.z = wn == 2 ? (w.z & keep) | put : w.z;
-                                w.w = wn == 3 ? (w.w & keep) | put : w.w;
+                                for (int t = 0; t < M::NT; t++) {
+                                    const unsigned char* e = nrow + R::ROW + (16 * t + (lane & 15)) * M::EB;
+                                    if constexpr (M::EB == 2) {
+                                        const uint32_t v = *reinterpret_cast<const uint16_t*>(e);
+                                        const uint32_t sh = 16 * (en & 1), keep = ~(0xFFFFu << sh);
+                                        uint2& w = vb[j][t];
+                                        w.x = vmine && en < 2 ? (w.x & keep) | (v << sh) : w.x;
+                                        w.y = vmine && en >= 2 ? (w.y & keep) | (v << sh) : w.y;
+                                    } else {
+                                        const uint32_t v = *e;
+                                        const uint32_t sh = 8 * en, keep = ~(0xFFu << sh);
+                                        vb[j][t] = vmine ? (vb[j][t] & keep) | (v << sh) : vb[j][t];
+                                    }
+                                }
+                            } else {
+                                // V: lane l holds channel cg * 64 + l; token tn is element tn % TPC
+                                // of the channel's 16-byte piece in token group tn / TPC
+                                const int qn = tn / S::TPC, en = tn % S::TPC;
+                                const int wn = en * S::EB / 4, sh = (en * S::EB % 4) * 8;
+                                constexpr uint32_t emask = S::EB == 4 ? 0xFFFFFFFFu : (1u << (8 * S::EB)) - 1u;
+#pragma unroll
+                                for (int c = 0; c < S::NCH; c++) {  // constant indices keep the ring in VGPRs
+                                    const int cg = c % S::CG;
+                                    if (c / S::CG != qn) continue;
+                                    const unsigned char* e = nrow + R::ROW + (cg * 64 + lane) * S::EB;
+                                    uint32_t v;
+                                    if constexpr (S::EB == 4)
+                                        v = *reinterpret_cast<const uint32_t*>(e);
+                                    else if constexpr (S::EB == 2)
+                                        v = *reinterpret_cast<const uint16_t*>(e);
+                                    else
+                                        v = *e;
+                                    auto& w = vb[j][c];
+                                    const uint32_t put = v << sh, keep = ~(emask << sh);
+                                    w.x = wn == 0 ? (w.x & keep) | put : w.x;
+                                    w.y = wn == 1 ? (w.y & keep) | put : w.y;
+                                    w.z = wn == 2 ? (w.z & keep) | put : w.z;
+                                    w.w = wn == 3 ? (w.w & keep) | put : w.w;
+                                }
                             }
                         }
                     }
                     if constexpr (QL) {
                         const QLds qo{q_lds, opaque(q_off)};
                         attend_block<QT, KT, D, G>(st, qo, kb[j], vb[j], kv_nv[j], c2, lane);
+                    } else if constexpr (MF) {
+                        attend_mfma<kBF16, KM, D, G>(st, qr, kb[j], vb[j], kv_nv[j], c2, lane);
                     } else {
                         attend_block<QT, KT, D, G>(st, qr, kb[j], vb[j], kv_nv[j], c2, lane);
                     }

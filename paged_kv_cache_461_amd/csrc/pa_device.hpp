@@ -247,6 +247,36 @@ struct TileWindow {
         const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, offset, soffset, 0);
         return make_uint4(v.x, v.y, v.z, v.w);
     }
+    // 8- and 4-byte forms of the same loads
+    __device__ __forceinline__ uint2 load_stream_b64(int offset, int soffset = 0) const
+    {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, offset, soffset, kBufferNontemporal);
+        const uint32_t v0 = v[0], v1 = v[1];
+        return make_uint2(v0, v1);
+    }
+    __device__ __forceinline__ uint2 load_cached_b64(int offset, int soffset = 0) const
+    {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, offset, soffset, 0);
+        const uint32_t v0 = v[0], v1 = v[1];
+        return make_uint2(v0, v1);
+    }
+    __device__ __forceinline__ uint32_t load_stream_b32(int offset, int soffset = 0) const
+    {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, offset, soffset, kBufferNontemporal);
+    }
+    __device__ __forceinline__ uint32_t load_cached_b32(int offset, int soffset = 0) const
+    {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, offset, soffset, 0);
+    }
+    // a uint2 or uint32_t piece, streamed or cached
+    template <class T>
+    __device__ __forceinline__ T load_piece(int offset, int soffset, bool cached) const
+    {
+        if constexpr (sizeof(T) == 8)
+            return cached ? load_cached_b64(offset, soffset) : load_stream_b64(offset, soffset);
+        else
+            return cached ? load_cached_b32(offset, soffset) : load_stream_b32(offset, soffset);
+    }
     static constexpr int kBufferNontemporal = 2;  // the cache-policy bit printed as "nt"
 };
 
