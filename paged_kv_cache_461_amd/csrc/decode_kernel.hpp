@@ -21,23 +21,22 @@
 // run + chunk, which is one-to-one over non-empty pieces (a later run can only meet a later
 // chunk), so the workspace size depends only on the numbers of runs and chunks.
 //
-// Inside a wave, per 16-token block (pool layout in include/pagedattn.h) NCH K loads and NCH V
-// loads of 16 bytes per lane each read one contiguous 1 KiB slice, with the nontemporal hint
-// (every K/V byte is read once per launch):
-//   QK^T: lane l holds channels of token l/4; bf16/fp8 K is multiplied with bf16 query pairs
-//         (held in VGPRs for the piece) by v_dot2c_f32_bf16 (fp8 first widened exactly to bf16
-//         pairs), fp32 K with FMAs; the 4 lanes of a token finish the dot product with two DPP
-//         quad moves.
-//   softmax: online, in base 2.  The running max is wave-uniform and only moved when a score
-//         exceeds it by more than 8 (then o and l are rescaled), so most blocks skip the
-//         rescale; weights stay below 2^8, and normalisation happens once per piece.
-//   PV:   the block's weights are packed to bf16 pairs (the partner token's weight comes from
-//         the neighbouring quad by one ds_swizzle) and read into scalar registers; each V load
-//         gives every lane one channel of 8 (bf16) or 16 (fp8) consecutive tokens, contracted
-//         with the pairs by v_dot2c_f32_bf16 (fp32: FMAs).  The accumulator is one fp32 per
-//         (channel group, head) per lane.
+// Inside a wave, per 16-token block (pool layout in include/pagedattn.h), the K loads read one
+// contiguous 1 KiB slice each and the V loads whole 16-channel tiles or 1 KiB slices, with the
+// nontemporal hint (every K/V byte is read once per launch).
+//   bf16 and 8-bit caches (the matrix-core form, described beside attend_mfma): S^T = K Q^T and
+//     O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 / v_mfma_f32_16x16x16_bf16 with the GQA heads as
+//     the tile columns, an 8-bit cache widened exactly to bf16 first, the online softmax on the
+//     accumulator, whose lanes already hold the next product's weights.
+//   fp32 caches (the vector form): lane l holds channels of token l/4, multiplied with the query
+//     (in LDS) by FMAs and finished with two DPP quad moves; the weights are read into scalar
+//     registers and each V load gives every lane one channel of 4 consecutive tokens.
+//   softmax: online, in base 2.  The running max only moves when a score exceeds it by more than
+//     8 (then o and l are rescaled), so most blocks skip the rescale; weights stay below 2^8, and
+//     normalisation happens once per piece.
 // An NST-deep ring of register buffers keeps NST-1 blocks of K and V in flight while one is
-// attended; all loop bounds are wave-uniform, so the waits on the ring stay counted.
+// attended; all loop bounds are wave-uniform, so the waits on the ring stay counted.  Results of
+// pieces that end inside a chunk wait in LDS until the chunk's last unit (deferred stores).
 #pragma once
 
 #include <float.h>
