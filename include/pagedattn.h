@@ -58,8 +58,7 @@
  * reads a whole 1 KiB K slice (16 tokens x 32 channels) or a 1 KiB V piece (8 tokens x 64
  * channels).
  *
- * Supported shapes: head_dim 64 or 128; block_size 16 or 32 for attention, also 8 with an
- * F32 or BF16 cache (the pages weigh
+ * Supported shapes: head_dim 64 or 128; block_size 8, 16 or 32 for attention (the pages weigh
  * block size against fragmentation and access efficiency: page 2, the PagedAttention section;
  * the append takes any block size the layout allows); num_heads / num_kv_heads in
  * {1, 2, 4, 8}; (q dtype, cache dtype) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3),

@@ -131,9 +131,6 @@ int32_t check_decode_shape(int32_t num_seqs, int32_t num_heads, int32_t num_kv_h
     if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
     if (block_size != 8 && block_size != 16 && block_size != 32)
         return fail(PA_ERR_UNSUPPORTED, "block_size %d (supported: 8, 16, 32)", block_size);
-    if (block_size == 8 && is_quant(cache_dtype))
-        return fail(PA_ERR_UNSUPPORTED, "8-token blocks need a 16- or 32-bit cache (an 8-bit V group of 8 tokens "
-                    "does not fill the kernels' 16-byte V pieces)");
     const bool combo = (q_dtype == PA_F32 && cache_dtype == PA_F32) || (q_dtype == PA_BF16 && cache_dtype == PA_BF16) ||
                        (q_dtype == PA_BF16 && is_quant(cache_dtype));
     if (!combo) return fail(PA_ERR_UNSUPPORTED, "(q dtype %d, cache dtype %d) not supported", q_dtype, cache_dtype);

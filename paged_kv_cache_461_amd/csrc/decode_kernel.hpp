@@ -786,9 +786,14 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
                       : MF                                   ? ktok * 64 + (lane >> 4) * 16
                                                              : lane * 16;
     // matrix-core form, V: lane l reads tokens 4 (l / 16) .. + 3 of channel l % 16 of each
-    // 16-channel tile (tile t at t * 256 bytes of the unit's token group)
-    const int mvoff = M::EB == 2 ? (((lane >> 5) * D + (lane & 15)) * 16 + ((lane >> 4) & 1) * 8)
-                                 : ((lane & 15) * 16 + (lane >> 4) * 4);
+    // 16-channel tile: element (token o, channel d) of a unit's V is at ((o / T) D + d) T + o % T
+    // with T = min(16 / e, B) tokens per channel piece, so tile t starts 16 T e bytes after tile
+    // t - 1.  With 8-token blocks of an 8-bit cache (T = 8) the lanes of tokens 8..15 fall past
+    // the block's bytes, outside the window, and read nothing.
+    const int vT = 16 / M::EB < a.block_size ? 16 / M::EB : a.block_size;
+    const int mtok = 4 * (lane >> 4);
+    const int mvoff = ((mtok / vT) * D + (lane & 15)) * vT * M::EB + (mtok % vT) * M::EB;
+    const int mvtile = 16 * vT * M::EB;
     const int kstride = a.block_size * 64;
     const int64_t block_stride = (int64_t)Hkv * btile;
     const int32_t* tables = a.block_tables;
@@ -1139,12 +1144,12 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
 #pragma unroll
                             for (int c = 0; c < S::NCH; c++) kb[i][c] = kw.load_cached(kvoff, c * kstride);
 #pragma unroll
-                            for (int t = 0; t < M::NT; t++) vb[i][t] = vw.template load_piece<typename M::VP>(mvoff, t * 256, true);
+                            for (int t = 0; t < M::NT; t++) vb[i][t] = vw.template load_piece<typename M::VP>(mvoff, t * mvtile, true);
                         } else {
 #pragma unroll
                             for (int c = 0; c < S::NCH; c++) kb[i][c] = kw.load_stream(kvoff, c * kstride);
 #pragma unroll
-                            for (int t = 0; t < M::NT; t++) vb[i][t] = vw.template load_piece<typename M::VP>(mvoff, t * 256, false);
+                            for (int t = 0; t < M::NT; t++) vb[i][t] = vw.template load_piece<typename M::VP>(mvoff, t * mvtile, false);
                         }
                     } else if (hint && __builtin_amdgcn_readfirstlane(ent_cached[i])) {
 #pragma unroll

@@ -172,8 +172,8 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// B8: the 8-token-block form (bf16 cache only), a separate instance so that its second table
-// entry per unit costs the other block sizes nothing.
+// B8: the 8-token-block form, a separate instance so that its second table entry per unit costs
+// the other block sizes nothing.
 //
 // Ping-pong schedule.  The 8 waves form two groups, A = waves 0..3 and B = waves 4..7, one wave
 // of each per SIMD.  Each wave alternates two phases per iteration it: M(it) on the matrix
@@ -307,10 +307,9 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_kernel(PrefillArgs
     // A block of 16 << ub tokens holds 1 << ub units; unit u of the range is unit u & ub of
     // table entry u >> ub.  Inside a 32-token block's tile, unit `sub` has its K slices at
     // sub * 1 KiB + slice * (B * 64) and its V at sub * TILE_BYTES (include/pagedattn.h).
-    // 8-token blocks (bf16 cache only): unit u is blocks 2u (tokens 0..7) and 2u+1 (8..15).
+    // 8-token blocks: unit u is blocks 2u (tokens 0..7) and 2u+1 (8..15).
     const int ub = a.block_size > kUnitTokens ? 1 : 0;
     constexpr bool b8 = B8;
-    static_assert(!B8 || KT == kBF16, "8-token blocks with a bf16 cache only");
     const int kstride = a.block_size * 64;
     const int64_t btile = (int64_t)a.block_size * D * EB;  // bytes of one (block, kv head) tile
     const int last_unit = kstop > 0 ? (kstop - 1) >> 4 : 0;
@@ -348,8 +347,17 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_kernel(PrefillArgs
                 // K: the piece's token (off >> 6 within its 1 KiB slice) picks the block
                 const int tok = (off & 1023) >> 6;
                 kr[SET][j] = load16(kpool + (tok < 8 ? t1 : t2) + (off >> 10) * kstride + (tok & 7) * 64 + (off & 63));
-                const int og = (off >> 4) / D;
-                vr[SET][j] = load16(vpool + (og ? t2 : t1) + (off - og * D * 16));
+                if constexpr (kIsQuant<KT>) {
+                    // V: the 16-token piece of channel d is 8 bytes (8 tokens) of each block
+                    const int d = off >> 4;
+                    const uint2 lo = *reinterpret_cast<const uint2*>(vpool + t1 + d * 8);
+                    const uint2 hi = *reinterpret_cast<const uint2*>(vpool + t2 + d * 8);
+                    vr[SET][j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                } else {
+                    // V: a piece is one 8-token group; the first D pieces are block 1's
+                    const int og = (off >> 4) / D;
+                    vr[SET][j] = load16(vpool + (og ? t2 : t1) + (off - og * D * 16));
+                }
             } else {
                 const int sub = ((kbase >> 4) + b) & ub;
                 const int64_t tile = ((int64_t)(ok ? phys : 0) * a.num_kv_heads + g) * btile;
@@ -705,11 +713,8 @@ template <int KT, int D, int G>
 hipError_t launch_one(const PrefillArgs& a, int grid, hipStream_t stream)
 {
     if (a.block_size < kUnitTokens) {
-        if constexpr (KT == kBF16)
-            hipLaunchKernelGGL((prefill_kernel<KT, D, G, kPrefillRowTiles, true>), dim3((unsigned)grid),
-                               dim3(kPrefillThreads), 0, stream, a);
-        else
-            return hipErrorInvalidValue;  // rejected by the host checks before this point
+        hipLaunchKernelGGL((prefill_kernel<KT, D, G, kPrefillRowTiles, true>), dim3((unsigned)grid),
+                           dim3(kPrefillThreads), 0, stream, a);
     } else {
         hipLaunchKernelGGL((prefill_kernel<KT, D, G, kPrefillRowTiles, false>), dim3((unsigned)grid),
                            dim3(kPrefillThreads), 0, stream, a);

@@ -74,7 +74,6 @@ def _decode(lib, **kw):
     (dict(Hq=30), ops.PA_ERR_INVALID_ARG),                  # 30 % 8 != 0
     (dict(Hq=24, Hkv=2), ops.PA_ERR_UNSUPPORTED),            # GQA 12
     (dict(D=96), ops.PA_ERR_UNSUPPORTED),
-    (dict(B=8, cache_dtype=FP8), ops.PA_ERR_UNSUPPORTED),  # fp8 V groups of 8 tokens
     (dict(B=4), ops.PA_ERR_UNSUPPORTED),
     (dict(B=64), ops.PA_ERR_UNSUPPORTED),
     (dict(B=32, P=48), ops.PA_ERR_INVALID_ARG),              # partition not a multiple of the block
@@ -86,7 +85,6 @@ def _decode(lib, **kw):
     (dict(q_dtype=F32, cache_dtype=E5M2), ops.PA_ERR_UNSUPPORTED),
     (dict(cache_dtype=5), ops.PA_ERR_INVALID_ARG),           # unknown dtype code
     (dict(cache_dtype=I8), ops.PA_ERR_INVALID_ARG),          # INT8 without scales
-    (dict(B=8, cache_dtype=I8, k_scale=FAKE, v_scale=FAKE), ops.PA_ERR_UNSUPPORTED),
     (dict(q_dtype=F32, cache_dtype=I8, k_scale=FAKE, v_scale=FAKE), ops.PA_ERR_UNSUPPORTED),
     (dict(q_dtype=I8, cache_dtype=I8), ops.PA_ERR_INVALID_ARG),
     (dict(P=100), ops.PA_ERR_INVALID_ARG),                   # not a multiple of 16
@@ -141,6 +139,14 @@ def test_decode_accepts_32_token_blocks(lib):
     """Block size 32 passes the host checks (with a table long enough for it); the call then
     stops at the workspace check, before any launch."""
     assert _decode(lib, B=32, mbps=128, ws=None, ws_bytes=0) == ops.PA_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("cache", [FP8, E5M2, I8])
+def test_decode_accepts_8_token_blocks_of_8_bit_caches(lib, cache):
+    """Block size 8 passes the host checks for the 8-bit caches too (their V pieces are then 8
+    tokens of a channel); the call then stops at the workspace check, before any launch."""
+    assert _decode(lib, B=8, mbps=512, cache_dtype=cache, k_scale=FAKE, v_scale=FAKE, ws=None,
+                   ws_bytes=0) == ops.PA_ERR_WORKSPACE
 
 
 def test_decode_empty_batch_is_ok_without_launch(lib):

@@ -63,11 +63,12 @@ def test_block_size_32(cache, P):
     step_and_compare(b, partition_size=P)
 
 
-@pytest.mark.parametrize("cache", [W.BF16, W.F32])
+@pytest.mark.parametrize("cache", [W.BF16, W.F32, W.FP8_E4M3, W.FP8_E5M2, W.INT8])
 @pytest.mark.parametrize("P,short", [(0, False), (8, False), (64, False), (0, True)])
 def test_block_size_8(cache, P, short):
-    """8-token blocks (16- and 32-bit caches): one block per 16-token unit, its upper half
-    empty.  short: contexts <= 64, so the automatic split is one chunk per run."""
+    """8-token blocks: one block per 16-token unit, its upper half empty (an 8-bit cache's V
+    pieces are then 8 tokens of a channel).  short: contexts <= 64, so the automatic split is
+    one chunk per run."""
     q = W.F32 if cache == W.F32 else W.BF16
     ctx = [1, 7, 8, 9, 40, 63, 64] if short else [1, 7, 8, 9, 15, 16, 17, 100, 511, 1000]
     b = W.build_batch(ctx, num_heads=16, num_kv_heads=4, head_dim=128, block_size=8, q_dtype=q, cache_dtype=cache,
@@ -306,7 +307,7 @@ def _fused(db, k_pool, v_pool, partition_size=0):
     (W.FP8_E4M3, 64, 16, False), (W.FP8_E5M2, 0, 16, False), (W.F32, 0, 16, False), (W.F32, 32, 16, False),
     (W.BF16, 0, 32, False), (W.FP8_E4M3, 32, 32, False), (W.BF16, 0, 16, True), (W.FP8_E4M3, 0, 32, True),
     (W.BF16, 0, 8, False), (W.F32, 16, 8, True), (W.INT8, 0, 16, False), (W.INT8, 64, 32, False),
-    (W.INT8, 0, 16, True)])
+    (W.INT8, 0, 16, True), (W.FP8_E4M3, 0, 8, False), (W.FP8_E4M3, 8, 8, False), (W.INT8, 0, 8, True)])
 def test_fused_append_equals_separate_calls(cache, P, B, short):
     """pa_paged_attention_decode_append writes the same pool bytes as pa_kv_cache_write and
     returns the same output bits as the decode that follows it; both match the oracle.  The

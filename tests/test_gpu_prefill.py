@@ -50,12 +50,14 @@ def test_mixed_chunks(cache, gqa, head_dim):
     prefill_and_compare(b)
 
 
+@pytest.mark.parametrize("cache", [W.BF16, W.FP8_E4M3, W.INT8])
 @pytest.mark.parametrize("P", [0, 24, 64])
-def test_block_size_8(P):
-    """8-token blocks (bf16 cache): every 16-token unit of an iteration comes from two blocks;
-    split ranges of 24 keys start inside a unit."""
+def test_block_size_8(cache, P):
+    """8-token blocks: every 16-token unit of an iteration comes from two blocks (an 8-bit
+    cache's V piece of a channel is 8 bytes of each); split ranges of 24 keys start inside a
+    unit."""
     b = W.build_batch(MIXED[0], num_heads=16, num_kv_heads=4, head_dim=128, block_size=8, q_dtype=W.BF16,
-                      cache_dtype=W.BF16, seed=80 + P, query_lens=MIXED[1])
+                      cache_dtype=cache, seed=80 + P, query_lens=MIXED[1])
     prefill_and_compare(b, partition_size=P)
 
 
