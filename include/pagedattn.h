@@ -320,6 +320,26 @@ int64_t pa_pool_bytes(int64_t num_blocks, int32_t num_kv_heads, int32_t head_dim
                       int32_t block_size, int32_t cache_dtype);
 
 /*
+ * Debug check, on host copies, of the device-resident data the calls above take on trust
+ * (the block table and slot mapping of page 1, section 4).  No GPU work; host pointers.
+ *   block_tables    int32 [num_seqs][max_blocks_per_seq]; context_lens int32 [num_seqs].
+ *   Every sequence must have 0 <= context_lens[s] <= max_context_len and
+ *   ceil(context_lens[s] / block_size) <= max_blocks_per_seq, and each of those table entries
+ *   must be a block id in [0, num_blocks) (entries past them are not looked at).
+ *   slots           int64 [num_slots] or NULL: the write slots of a pa_kv_cache_write call.
+ *                   A negative slot (a skipped token) is allowed; the others must be below
+ *                   num_blocks * block_size and distinct.
+ *   block_refcounts int32 [num_blocks] or NULL (only with slots): the block manager's reference
+ *                   counts; a slot in a block whose count is not 1 is a write into an unowned
+ *                   or shared block (a missed copy-on-write).
+ * Returns PA_OK, or PA_ERR_INVALID_ARG naming the first offending sequence, entry or slot in
+ * pa_last_error().
+ */
+int32_t pa_validate_tables(const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t max_context_len, int32_t block_size, int64_t num_blocks,
+                           const int64_t* slots, int32_t num_slots, const int32_t* block_refcounts);
+
+/*
  * Measurement helper (not part of the attention path): read num_reads 4 KiB tiles of buf, tile
  * order[i] for i = 0 .. num_reads-1, with grid_workgroups x 256 threads (two tiles per wave and
  * iteration, 16-byte nontemporal loads, each wave load one contiguous 1 KiB).  Timing it with a random

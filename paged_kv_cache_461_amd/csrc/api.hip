@@ -7,8 +7,11 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "../../include/pagedattn.h"
 #include "pa_internal.hpp"
@@ -233,6 +236,58 @@ int64_t pa_pool_bytes(int64_t num_blocks, int32_t num_kv_heads, int32_t head_dim
     const int e = elem_bytes(cache_dtype);
     if (!e || num_blocks < 0 || num_kv_heads < 0 || head_dim < 0 || block_size < 0) return -1;
     return num_blocks * num_kv_heads * (int64_t)block_size * head_dim * e;
+}
+
+int32_t pa_validate_tables(const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t max_context_len, int32_t block_size, int64_t num_blocks,
+                           const int64_t* slots, int32_t num_slots, const int32_t* block_refcounts)
+{
+    if (num_seqs < 0 || max_blocks_per_seq < 0 || max_context_len < 0 || block_size < 1 || num_blocks < 0 ||
+        num_slots < 0)
+        return fail(PA_ERR_INVALID_ARG, "negative size (num_seqs=%d max_blocks_per_seq=%d max_context_len=%d "
+                    "block_size=%d num_blocks=%lld num_slots=%d)", num_seqs, max_blocks_per_seq, max_context_len,
+                    block_size, (long long)num_blocks, num_slots);
+    if (num_seqs > 0 && (!context_lens || (max_blocks_per_seq > 0 && !block_tables)))
+        return fail(PA_ERR_INVALID_ARG, "null block_tables or context_lens");
+    for (int32_t s = 0; s < num_seqs; s++) {
+        const int32_t ctx = context_lens[s];
+        if (ctx < 0 || ctx > max_context_len)
+            return fail(PA_ERR_INVALID_ARG, "sequence %d: context length %d outside [0, %d]", s, ctx,
+                        max_context_len);
+        const int64_t nb = ((int64_t)ctx + block_size - 1) / block_size;
+        if (nb > max_blocks_per_seq)
+            return fail(PA_ERR_INVALID_ARG, "sequence %d: context length %d needs %lld blocks, the table holds %d",
+                        s, ctx, (long long)nb, max_blocks_per_seq);
+        for (int64_t j = 0; j < nb; j++) {
+            const int32_t b = block_tables[(int64_t)s * max_blocks_per_seq + j];
+            if (b < 0 || b >= num_blocks)
+                return fail(PA_ERR_INVALID_ARG, "sequence %d: table entry %lld is block %d, outside [0, %lld)", s,
+                            (long long)j, b, (long long)num_blocks);
+        }
+    }
+    if (slots && num_slots > 0) {
+        const int64_t cap = num_blocks * block_size;
+        std::vector<std::pair<int64_t, int32_t>> used;  // (slot, token)
+        used.reserve((size_t)num_slots);
+        for (int32_t t = 0; t < num_slots; t++) {
+            const int64_t sl = slots[t];
+            if (sl < 0) continue;  // a skipped token
+            if (sl >= cap)
+                return fail(PA_ERR_INVALID_ARG, "token %d: slot %lld outside [0, %lld)", t, (long long)sl,
+                            (long long)cap);
+            if (block_refcounts && block_refcounts[sl / block_size] != 1)
+                return fail(PA_ERR_INVALID_ARG, "token %d: slot %lld is in block %lld with reference count %d "
+                            "(only a block its sequence alone holds may be written)", t, (long long)sl,
+                            (long long)(sl / block_size), block_refcounts[sl / block_size]);
+            used.emplace_back(sl, t);
+        }
+        std::sort(used.begin(), used.end());
+        for (size_t i = 1; i < used.size(); i++)
+            if (used[i].first == used[i - 1].first)
+                return fail(PA_ERR_INVALID_ARG, "tokens %d and %d write the same slot %lld", used[i - 1].second,
+                            used[i].second, (long long)used[i].first);
+    }
+    return ok();
 }
 
 int32_t pa_kv_cache_write(const void* key, const void* value, int32_t src_dtype, void* k_pool, void* v_pool,

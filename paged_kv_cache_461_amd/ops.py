@@ -37,7 +37,7 @@ EXPORTS = (
     "pa_chunked_prefill_workspace_size", "pa_paged_attention_chunked_prefill", "pa_paged_attention_decode_append",
     "pa_paged_attention_decode_shared", "pa_copy_blocks", "pa_bm_create", "pa_bm_destroy", "pa_bm_add_sequence", "pa_bm_append_token", "pa_bm_fork",
     "pa_bm_free_sequence", "pa_bm_block_table", "pa_bm_refcount", "pa_bm_get_stats",
-    "pa_paged_attention_decode_noalloc", "pa_decode_noalloc_max_workspace",
+    "pa_paged_attention_decode_noalloc", "pa_decode_noalloc_max_workspace", "pa_validate_tables",
 )
 
 
@@ -87,6 +87,8 @@ def library():
         lib.pa_kv_bytes_per_token.argtypes = [I32, I32, I32, I32]
         lib.pa_pool_bytes.restype = I64
         lib.pa_pool_bytes.argtypes = [I64, I32, I32, I32, I32]
+        lib.pa_validate_tables.restype = I32
+        lib.pa_validate_tables.argtypes = [P, I32, P, I32, I32, I32, I64, P, I32, P]
         lib.pa_probe_tile_read.restype = I32
         lib.pa_probe_tile_read.argtypes = [P, I64, P, I64, I32, P, P]
         lib.pa_copy_blocks.restype = I32
@@ -454,6 +456,34 @@ def kv_bytes_per_token(num_layers, num_kv_heads, head_dim, cache_dtype) -> int:
 
 def pool_bytes(num_blocks, num_kv_heads, head_dim, block_size, cache_dtype) -> int:
     return int(library().pa_pool_bytes(num_blocks, num_kv_heads, head_dim, block_size, cache_dtype))
+
+
+def validate_tables(block_tables, context_lens, max_context_len, block_size, num_blocks, slots=None,
+                    block_refcounts=None):
+    """Debug check of host copies of a call's block tables, context lengths and (optionally)
+    write slots and the block manager's reference counts (pa_validate_tables).  Arrays are
+    numpy arrays or CPU tensors; raises PagedAttnError naming the first violation."""
+    import numpy as np
+
+    def host(x, dt):
+        if x is None:
+            return None
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().numpy()
+        return np.ascontiguousarray(np.asarray(x), dtype=dt)
+
+    bt = host(block_tables, np.int32)
+    cl = host(context_lens, np.int32)
+    sl = host(slots, np.int64)
+    rc = host(block_refcounts, np.int32)
+    if bt.ndim != 2 or cl.ndim != 1 or bt.shape[0] != cl.shape[0]:
+        raise ValueError("block_tables must be [num_seqs][max_blocks_per_seq] and context_lens [num_seqs]")
+    if rc is not None and (sl is None or rc.shape != (int(num_blocks),)):
+        raise ValueError("block_refcounts needs slots and one count per block")
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p) if a is not None and a.size else None
+    _check(library().pa_validate_tables(ptr(bt), bt.shape[1], ptr(cl), cl.shape[0], int(max_context_len),
+                                        int(block_size), int(num_blocks), ptr(sl), 0 if sl is None else sl.size,
+                                        ptr(rc)))
 
 
 def probe_tile_read(buf, order, sink, grid_workgroups=2048, stream=None):
