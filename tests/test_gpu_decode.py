@@ -335,6 +335,33 @@ def test_fused_append_equals_separate_calls(cache, P, B, short):
     assert_close(b, out_to_f64(out2), oracle_attention(b, kp_h, vp_h))
 
 
+@pytest.mark.parametrize("cache", [W.BF16, W.FP8_E4M3, W.F32, W.INT8])
+@pytest.mark.parametrize("P", [0, 128])
+def test_many_piece_ends_in_one_chunk(cache, P):
+    """Chunks that end many runs (one- and two-unit sequences beside a long one, so the split is
+    balanced rather than one chunk per run): the results of the pieces that end inside a chunk
+    wait in a per-wave stage of two slots and are written after the chunk's last unit, and a
+    piece that finds the stage full is written at once; with the fused append the staged new
+    rows go with them.  Plain and fused calls give the same bits, and both match the oracle."""
+    q = W.F32 if cache == W.F32 else W.BF16
+    ctx = [16] * 12 + [5, 9, 30, 31, 1, 17] * 3 + [2000] + [16] * 9
+    b = W.build_batch(ctx, num_heads=16, num_kv_heads=4, head_dim=128, q_dtype=q, cache_dtype=cache, seed=77 + P)
+    kp_h, vp_h = oracle_pool(b, include_new=False)
+    db = DeviceBatch(b)
+    kp1, vp1 = to_dev(kp_h, cache), to_dev(vp_h, cache)
+    db.write_new_tokens(kp1, vp1)
+    out1 = db.decode(kp1, vp1, partition_size=P)
+    kp2, vp2 = to_dev(kp_h, cache), to_dev(vp_h, cache)
+    out2 = _fused(db, kp2, vp2, partition_size=P)
+    raw = lambda t: to_host_raw(t).view(np.uint8)
+    assert np.array_equal(raw(kp1), raw(kp2)) and np.array_equal(raw(vp1), raw(vp2)), "pools differ"
+    assert np.array_equal(raw(out1), raw(out2)), "outputs differ"
+    k, v, slots = b.new_tokens()
+    oracle.kv_cache_write(k, v, b.src_dtype, kp_h, vp_h, b.cache_dtype, slots, b.num_kv_heads, b.head_dim,
+                          b.block_size, b.k_scale, b.v_scale)
+    assert_close(b, out_to_f64(out1), oracle_attention(b, kp_h, vp_h))
+
+
 def _two_phase(db, kp, vp, partition_size=0):
     """Reference bits: phase 1 (partials) then the separate merge kernel (phase 2)."""
     b = db.b
