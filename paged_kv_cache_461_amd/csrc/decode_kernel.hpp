@@ -617,7 +617,7 @@ __device__ __forceinline__ void next_run(Cursor& c, const int* lctx, int num_seq
 // slot may or may not include the store, and either way the attention sees the same values in
 // the same places as after a separate append.  The row travels with the unit's loads, so
 // nothing waits for it.  Nothing in the launch waits for the store either; the pool bytes are
-// those of the append kernel (encode_elem, store_piece_codes).
+// those of the append kernel (encode_elem, store_piece_bytes -> store_piece_codes).
 template <int QT, int KT, int D>
 struct NewRow {
     static constexpr int ES = DtypeBytes<QT>::value;  // source element bytes (query dtype)

@@ -1,9 +1,10 @@
 // kv_store.hpp -- store one 16-byte piece of a new token's K or V row into its pool slot.
 //
 // The append kernel stores with store_kv_piece; the decode kernel's fused append encodes with
-// encode_elem and stores with store_piece_codes, so both write the same bytes.  Each decode step stores the new token's K/V in
-// the cache (page 1, section 1, the prefill/decode diagram) at its slot, the physical block from the sequence's block table and
-// the offset inside it (page 1, section 4).  Layouts are those of include/pagedattn.h: a K
+// encode_elem and stores the encoded bytes with store_piece_bytes, and both end in
+// store_piece_codes, so both write the same bytes.  Each decode step stores the new token's K/V
+// in the cache (page 1, section 1, the prefill/decode diagram) at its slot, the physical block
+// from the sequence's block table and the offset inside it (page 1, section 4).  Layouts are those of include/pagedattn.h: a K
 // piece lands contiguously inside one 64-byte channel slice of the (block, kv head) tile; a V
 // piece is spread over its channels' token groups, so V is written with element-sized stores
 // that touch only this token's bytes.  Same-dtype append copies bits; bf16/fp32 -> OCP E4M3 or
