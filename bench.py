@@ -53,6 +53,7 @@ EXTRA_DEFAULT = ("tiny_fp32", "long_context", "mixed_continuous_batch", "fp8_chu
 LAYERS = {"tiny_fp32": 2, "llama3_8b_decode": 2, "long_context": 4, "mixed_continuous_batch": 2,
           "fp8_chunked_prefill": 2, "fp8_e5m2_chunked_prefill": 2, "int8_chunked_prefill": 2}
 PARTITIONS = {"long_context": (0, 256, 512, 1024)}
+GRAPH_LAYERS = 32  # steps per graph in the all-layers graph replay (Llama-3-8B has 32 layers)
 WORKLOAD_NAMES = ("llama3_8b_decode", "long_context", "mixed_continuous_batch", "fp8_chunked_prefill",
                   "fp8_e5m2_chunked_prefill", "int8_chunked_prefill", "tiny_fp32")
 
@@ -435,13 +436,26 @@ def measure(batch, dev, layers, steps, warmup, partitions=(0,), fused=False, gra
                 with torch.cuda.graph(g, stream=side):
                     step(r)
                 graphs.append(g)
+            # a model's decode iteration is one graph over all its layers: GRAPH_LAYERS steps
+            # (cycling the layer pools) in one graph, so the replay's own cost is paid once per
+            # GRAPH_LAYERS steps
+            g_all = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_all, stream=side):
+                for i in range(GRAPH_LAYERS):
+                    step(i % len(pools))
         cur[0] = stream
         torch.cuda.synchronize()
         for i in range(max(warmup, 1)):
             graphs[i % len(graphs)].replay()
         gms = region(lambda i: graphs[i % len(graphs)].replay(), steps)
+        g_all.replay()
+        reps = max(2, steps // GRAPH_LAYERS)
+        gms_all = region(lambda i: g_all.replay(), reps) / GRAPH_LAYERS
         graph_res = {"ms_per_step": round(gms, 5), "eager_ms_per_step": round(ms_per_step, 5), "replays": steps,
-                     "what": "the same steps replayed from HIP graphs (one per layer pool), against eager launches"}
+                     "what": "the same steps replayed from HIP graphs (one per layer pool), against eager launches",
+                     "layers_per_graph": GRAPH_LAYERS, "ms_per_step_layers_per_graph": round(gms_all, 5),
+                     "what_layers_per_graph": "%d steps (one per layer, the layer pools cycled) captured in one graph, "
+                                              "replayed %d times: ms per step" % (GRAPH_LAYERS, reps)}
 
     kernels = {"kv_write": round(launches(write, steps), 2)} if Rw else {}
     if Sp:
