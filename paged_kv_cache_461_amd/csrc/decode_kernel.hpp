@@ -307,7 +307,7 @@ __device__ __forceinline__ void attend_block(Acc<QT, KT, D, G>& st, const QSrc& 
 // ---- the matrix-core form (bf16 and 8-bit caches) ----------------------------------------
 //
 // Per 16-token unit, with the GQA group's G heads as the columns of 16 x 16 MFMA tiles
-// (columns G..15 are zero):
+// (columns G..15 repeat them and are never read):
 //   S^T (16 tokens x 16 heads) = K Q^T in D/32 steps of v_mfma_f32_16x16x32_bf16: A = K, lane l
 //     holding token l % 16 and 8 channels (an 8-bit cache: a 16-byte piece of 16 channels,
 //     widened exactly to bf16, feeds two steps); B = the query, lane l holding head l % 16 and
@@ -354,18 +354,18 @@ __device__ __forceinline__ int mf_channel(int st, int grp)
     return EB == 2 ? st * 32 + 8 * grp : (st >> 1) * 64 + 16 * grp + 8 * (st & 1);
 }
 
+// Columns G..15 of the tile repeat heads 0..G-1 (lane l loads head (l % 16) mod G): a product
+// column depends on its own B column only, so they cost nothing but are never read, and the
+// loaded values go straight into the operand -- a select on them would make the wave wait for
+// the load at once, and with it for every K/V load in flight.
 template <int QT, int KT, int D, int G>
 __device__ __forceinline__ void load_q_mf(MQ<QT, KT, D, G>& q, const unsigned char* qrow, int lane)
 {
     using M = MShape<QT, KT, D, G>;
-    const int h = lane & 15, grp = lane >> 4;
-    const int hh = h < G ? h : 0;
+    const int hh = (lane & 15) % G, grp = lane >> 4;
 #pragma unroll
-    for (int st = 0; st < M::KS; st++) {
-        const uint4 v = load16(qrow + (hh * D + mf_channel<M::EB>(st, grp)) * 2);
-        const uint4 z = h < G ? v : make_uint4(0u, 0u, 0u, 0u);
-        q.w[st] = __builtin_bit_cast(mf_bf16x8, z);
-    }
+    for (int st = 0; st < M::KS; st++)
+        q.w[st] = __builtin_bit_cast(mf_bf16x8, load16(qrow + (hh * D + mf_channel<M::EB>(st, grp)) * 2));
 }
 
 // One step of a sum (sum_or_max = false) or max over the four 16-lane groups holding one
