@@ -660,6 +660,17 @@ struct WaveStage {
     unsigned char row[FUSED ? SLOTS + 1 : 1][FUSED ? 2 * NewRow<QT, KT, D>::ROW : 16];
 };
 
+// The kernel's arguments read again from the kernarg segment at a point of use (scalar loads
+// behind an empty asm the compiler cannot see through), for the paths that run once per piece:
+// it keeps their pointers out of the registers the streaming loop holds.
+typedef const __attribute__((address_space(4))) DecodeArgs KernArgs;
+__device__ __forceinline__ KernArgs& kernel_args()
+{
+    KernArgs* p = (KernArgs*)(__builtin_amdgcn_kernarg_segment_ptr());
+    asm volatile("" : "+s"(p));
+    return *p;
+}
+
 __device__ __forceinline__ int64_t uniform64(int64_t x)
 {
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
@@ -866,6 +877,7 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
             fetch_entry(ent[i], ent_nv[i], ent_g[i], ent_sub[i], ent_cached[i], ent_s[i], ent_last[i]);
 
         auto query_row = [&](const Cursor& c) {
+            KernArgs& a = kernel_args();
             return static_cast<const unsigned char*>(a.query) + ((int64_t)c.s * a.num_heads + (int64_t)c.g * G) * D * S::QB;
         };
         std::conditional_t<MF, MQ<kBF16, KM, D, G>, QRegs<QT, KT, D, G>> qr;
@@ -912,6 +924,7 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
         // covered whole) or the partial result ----
         const int mh = lane & 15, mtb = 4 * (lane >> 4);  // matrix-core form: lane's head, first channel
         auto finish_piece = [&](bool defer) {
+            KernArgs& a = kernel_args();
             if constexpr (MF) {
                 st.l = mf_swap(st.l, false, false);
                 st.l = mf_swap(st.l, true, false);
@@ -1031,6 +1044,7 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
 
         // fused append: store the new row staged in slot r into the pool (lanes 0..2P-1)
         auto store_row = [&](int r, int64_t tile, int o) {
+            KernArgs& a = kernel_args();
             if constexpr (fused) {
                 if (lane < 2 * R::P) {
                     const int kv = lane / R::P, piece = lane % R::P;
@@ -1043,6 +1057,7 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
 
         // write what the stage holds (after the chunk's last unit)
         auto flush = [&]() {
+            KernArgs& a = kernel_args();
             if constexpr (SLOTS > 0) {
                 for (int i = 0; i < npend; i++) {
                     const PieceMeta<G>& me = ws.meta[i];
