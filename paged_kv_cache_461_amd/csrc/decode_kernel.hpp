@@ -9,11 +9,14 @@
 // (page 1, section 10).
 //
 // Work decomposition.  The K/V blocks of every (sequence, kv head) pair -- a "run" -- are
-// laid end to end, sequence-major then kv head, into one list of U units (one unit = one
-// 16-token block of one kv head).  The list is cut into chunks of C units and the waves of a
-// persistent grid take one chunk each, or chunks w, w + NW, ... for a caller-given size (by
-// default C = ceil(U / NW): one chunk per wave, so every wave moves the same number of bytes
-// and the kernel has no tail).  Chunk k runs on XCD k mod 8.
+// laid end to end, kv head by kv head and in sequence order within a kv head, into one list of
+// U units (one unit = one 16-token block of one kv head); run (s, g) is run number g S + s.
+// The list is cut into chunks of C units and the waves of a persistent grid take one chunk
+// each, or chunks w, w + NW, ... for a caller-given size (by default C = ceil(U / NW): one chunk
+// per wave, so every wave moves the same number of bytes and the kernel has no tail).  Chunk k
+// runs on XCD k mod 8; with the shared-block hint the chunks are dealt to the XCDs in 8
+// contiguous ranges instead, so the sharers of a prefix block of one kv head (whose runs lie in
+// one stretch of the list) read it through one L2.
 // A chunk that covers runs r1..r2 attends each covered piece of a run on its own (online
 // softmax state reset per piece) and stores the piece's normalised row and (max, sum) as a
 // partial result; a run covered by one piece writes its output row directly.  The merge
@@ -494,7 +497,8 @@ struct Pos {
 
 // The list's total U and the position of unit chunk_start(U), from the clamped context
 // lengths in LDS.  Lane l holds sequences base + 16 l .. base + 16 l + 15 of each
-// 1024-sequence window.
+// 1024-sequence window.  Every kv head lists the same T units (the sum over the sequences),
+// so unit u is in kv head u / T at offset u mod T of the sequences' units.
 struct Plan {
     int64_t U;
     Pos p;
@@ -523,7 +527,9 @@ __device__ __forceinline__ Plan plan_wave(const DecodeArgs& a, const int* lctx, 
     pl.p.g = pl.p.j = 0;
     pl.p.run_start = pl.U;
     if (u0 >= pl.U) return pl;
-    // locate u0
+    // locate u0: kv head g0, offset r0 in the sequences' units
+    const int g0 = (int)(u0 / total);
+    const int64_t r0 = u0 - (int64_t)g0 * total;
     int64_t before = 0;
     for (int base = 0; base < S; base += kScanWindow) {
         int nb[kScanPerLane];
@@ -535,32 +541,31 @@ __device__ __forceinline__ Plan plan_wave(const DecodeArgs& a, const int* lctx, 
             part += nb[i];
         }
         const int incl = wave_incl_scan(part, lane);
-        const uint64_t hit = __builtin_amdgcn_ballot_w64(before + (int64_t)incl * Hkv > u0);
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(before + incl > r0);
         if (hit) {
             const int L = __builtin_ctzll(hit);
-            int64_t u = before + (int64_t)(__builtin_amdgcn_readlane(incl, L) - __builtin_amdgcn_readlane(part, L)) * Hkv;
+            int64_t u = before + (__builtin_amdgcn_readlane(incl, L) - __builtin_amdgcn_readlane(part, L));
 #pragma unroll
             for (int i = 0; i < kScanPerLane; i++) {
                 const int n = __builtin_amdgcn_readlane(nb[i], L);
-                const int64_t span = (int64_t)n * Hkv;
-                if (u0 < u + span) {
-                    const int64_t off = u0 - u;
+                if (r0 < u + n) {
                     pl.p.s = base + L * kScanPerLane + i;
-                    pl.p.g = (int)(off / n);
-                    pl.p.j = (int)(off % n);
-                    pl.p.run_start = u + (int64_t)pl.p.g * n;
+                    pl.p.g = g0;
+                    pl.p.j = (int)(r0 - u);
+                    pl.p.run_start = (int64_t)g0 * total + u;
                     return pl;
                 }
-                u += span;
+                u += n;
             }
         }
-        before += (int64_t)__builtin_amdgcn_readlane(incl, 63) * Hkv;
+        before += __builtin_amdgcn_readlane(incl, 63);
     }
     return pl;  // not reached
 }
 
 // A position in the work list that moves block by block: (sequence, kv head, block) with
-// the run's context length.  Sequences with no context are skipped.
+// the run's context length.  Sequences with no context are skipped; past the list's end the
+// cursor rests at (num_seqs, num_kv_heads) with no context.
 struct Cursor {
     int s, g, j, ctx, nbs;
     int ush;  // unit_shift of the block size
@@ -580,32 +585,30 @@ __device__ __forceinline__ Cursor cursor_at(const Pos& p, const int* lctx, int u
     return c;
 }
 
-__device__ __forceinline__ void cursor_next(Cursor& c, const int* lctx, int num_seqs, int num_kv_heads)
-{
-    if (++c.j < c.nbs) return;
-    c.run_start += c.nbs;
-    c.j = 0;
-    if (++c.g < num_kv_heads) return;
-    c.g = 0;
-    do {
-        ++c.s;
-        c.ctx = c.s < num_seqs ? lctx[c.s] : 0;
-    } while (c.ctx == 0 && c.s < num_seqs);
-    c.nbs = nunits(c.ctx, c.ush);
-}
-
-// Move the cursor to block 0 of the next run (next kv head, or the next non-empty sequence).
+// Move the cursor to block 0 of the next run: the next non-empty sequence of this kv head, else
+// the first non-empty one of the next kv head.
 __device__ __forceinline__ void next_run(Cursor& c, const int* lctx, int num_seqs, int num_kv_heads)
 {
     c.run_start += c.nbs;
     c.j = 0;
-    if (++c.g < num_kv_heads) return;
-    c.g = 0;
-    do {
-        ++c.s;
-        c.ctx = c.s < num_seqs ? lctx[c.s] : 0;
-    } while (c.ctx == 0 && c.s < num_seqs);
+    for (;;) {
+        if (++c.s == num_seqs) {
+            if (++c.g == num_kv_heads) {
+                c.ctx = 0;
+                break;
+            }
+            c.s = 0;
+        }
+        c.ctx = lctx[c.s];
+        if (c.ctx != 0) break;
+    }
     c.nbs = nunits(c.ctx, c.ush);
+}
+
+__device__ __forceinline__ void cursor_next(Cursor& c, const int* lctx, int num_seqs, int num_kv_heads)
+{
+    if (++c.j < c.nbs) return;
+    next_run(c, lctx, num_seqs, num_kv_heads);
 }
 
 // Fused append.  The chunk that holds a run's last unit is the only one that reads the new
@@ -764,21 +767,30 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
     // the 8 XCDs round-robin; the wave's first chunk is chosen so that chunk k runs on XCD
     // k mod 8, which gives every XCD the same mix of sequences, kv heads and block ranges (with
     // 4 consecutive chunks per workgroup, an XCD would see a fixed part of every run).
-    const int64_t first = (gridDim.x & 7) == 0
-                              ? 8 * kDecodeWaves * (int64_t)(blockIdx.x >> 3) + 8 * wave_in_wg + (blockIdx.x & 7)
-                              : w;
+    const bool xcd8 = (gridDim.x & 7) == 0;
+    const int64_t first =
+        xcd8 ? 8 * kDecodeWaves * (int64_t)(blockIdx.x >> 3) + 8 * wave_in_wg + (blockIdx.x & 7) : w;
+    // with the hint, slot kk (on XCD kk mod 8) takes chunk (kk mod 8) q + kk / 8, q = ceil(chunks / 8):
+    // XCD x runs chunks x q .. x q + q - 1
+    auto chunk_of = [&](int64_t kk, int64_t nch) -> int64_t {
+        if (!hint || !xcd8) return kk;
+        return (kk & 7) * ((nch + 7) >> 3) + (kk >> 3);
+    };
     // chunk_blocks < 0: one chunk per run.  The host picks it when every run fits in one
     // minimum chunk, so no run is split, nothing is merged and the merge launch is skipped
     // (small batches, where a launch costs more than the work).  Chunk k is then run k.
     constexpr bool per_run = PER_RUN;
     ChunkMap cm{};
+    auto count_chunks = [&](int64_t U) { return U > 0 ? min(cm.of_unit(U - 1) + 1, a.max_chunks) : (int64_t)0; };
     const Plan pl = per_run ? Plan{0, Pos{NS, 0, 0, 0}} : plan_wave(a, lctx, lane, [&](int64_t U) {
         cm.C = a.chunk_blocks > 0 ? (int64_t)a.chunk_blocks : max((U + NW - 1) / NW, (int64_t)kMinChunkBlocks);
-        return cm.start(first);
+        return cm.start(chunk_of(first, count_chunks(U)));
     });
     const int64_t U = pl.U;
-    const int64_t nchunks =
-        per_run ? (int64_t)NS * Hkv : (U > 0 ? min(cm.of_unit(U - 1) + 1, a.max_chunks) : 0);
+    const int64_t nchunks = per_run ? (int64_t)NS * Hkv : count_chunks(U);
+    // slots kk = first, first + NW, ... below kk_end map onto the chunks (the hint's dealing
+    // leaves up to 7 slots without a chunk)
+    const int64_t kk_end = hint && xcd8 ? 8 * ((nchunks + 7) >> 3) : nchunks;
 
     const unsigned char* kpool = static_cast<const unsigned char*>(a.k_pool);
     const unsigned char* vpool = static_cast<const unsigned char*>(a.v_pool);
@@ -828,7 +840,9 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
         }
     }
 
-    for (int64_t k = first; k < nchunks; k += NW) {
+    for (int64_t kk = first; kk < kk_end; kk += NW) {
+        const int64_t k = chunk_of(kk, nchunks);  // the chunk
+        if (k >= nchunks) continue;
         int n;           // units of this chunk
         Pos p0;          // its first unit
         int64_t u_end;   // list index one past its last unit
@@ -841,7 +855,7 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
             }
         } else {
             n = (int)min(cm.size(k), U - cm.start(k));  // >= 1
-            p0 = k == first ? pl.p : plan_wave(a, lctx, lane, [&](int64_t) { return cm.start(k); }).p;
+            p0 = kk == first ? pl.p : plan_wave(a, lctx, lane, [&](int64_t) { return cm.start(k); }).p;
             u_end = cm.start(k) + n;
         }
 
@@ -938,7 +952,7 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
                     st.l[h] = x;
                 }
             }
-            const int64_t run = (int64_t)cc.s * Hkv + cc.g;
+            const int64_t run = (int64_t)cc.g * NS + cc.s;  // the run's number in list order
             const bool first = piece_j0 == 0, whole = first && cc.j == cc.nbs - 1;
             // every run with blocks is entered at its block 0 by exactly one wave, which records
             // the chunk range covering it for the merge

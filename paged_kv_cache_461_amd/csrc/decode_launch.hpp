@@ -26,9 +26,10 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(const De
     constexpr int PER = D / 64;
     constexpr int UN = G * PER >= 8 ? 64 / (G * PER) : 8;  // pieces whose rows are loaded together
     const int lane = threadIdx.x & 63;
+    // runs are numbered as the streaming kernel lists them: run g S + s
     const int64_t run = (int64_t)blockIdx.x * kMergeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (run >= (int64_t)a.num_seqs * a.num_kv_heads) return;
-    const int s = (int)(run / a.num_kv_heads), g = (int)(run % a.num_kv_heads);
+    const int s = (int)(run % a.num_seqs), g = (int)(run / a.num_seqs);
     const int ctx = seq_ctx(a, s);
     const int64_t k0 = a.run_info[2 * run];
     const int np = a.run_info[2 * run + 1];

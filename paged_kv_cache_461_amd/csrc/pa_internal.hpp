@@ -63,7 +63,7 @@ struct DecodeArgs {
     int64_t max_pieces;       // pieces the workspace has room for (runs + max_chunks)
     float* o_part;            // [max_pieces][G][D]  normalised partial rows
     float* ml_part;           // [max_pieces][G][2]  (running max in base 2, softmax sum)
-    int32_t* run_info;        // [S * Hkv][2]        (first chunk, number of pieces)
+    int32_t* run_info;        // [Hkv * S][2]        (first chunk, number of pieces) of run g S + s
 };
 
 // Chunked prefill: MFMA attention kernel (+ merge kernel when the keys are split).
