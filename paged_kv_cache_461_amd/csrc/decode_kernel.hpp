@@ -845,18 +845,15 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
         if (k >= nchunks) continue;
         int n;           // units of this chunk
         Pos p0;          // its first unit
-        int64_t u_end;   // list index one past its last unit
         if constexpr (per_run) {
             p0 = Pos{(int)(k / Hkv), (int)(k % Hkv), 0, 0};
             n = __builtin_amdgcn_readfirstlane(nunits(lctx[p0.s], ush));  // uniform: keeps loop control scalar
-            u_end = n;
             if (n == 0) {  // empty sequence: its zero rows were written above
                 continue;
             }
         } else {
             n = (int)min(cm.size(k), U - cm.start(k));  // >= 1
             p0 = kk == first ? pl.p : plan_wave(a, lctx, lane, [&](int64_t) { return cm.start(k); }).p;
-            u_end = cm.start(k) + n;
         }
 
         // table cursor: the block whose table entry is fetched next (it stops at the chunk's
