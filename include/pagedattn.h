@@ -237,10 +237,12 @@ int32_t pa_paged_attention_chunked_prefill(void* out, const void* query, int32_t
  *   shared_blocks  device int32 [num_seqs], or NULL (= pa_paged_attention_decode_phase): block j
  *                  of sequence s with j < shared_blocks[s] is read with the default cache policy,
  *                  so the sequence's other readers of that block can find it cached; every other
- *                  block is read once per call and streamed past the caches.  The hint changes
- *                  only the loads' cache policy: the output is the same, bit for bit, for any
- *                  values (an inaccurate hint only costs time).  The host knows the counts from
- *                  its block refcounts (the leading blocks with refcount > 1).
+ *                  block is read once per call and streamed past the caches.  With the hint the
+ *                  work chunks are also placed so that the sharers of one kv head's blocks run on
+ *                  one XCD (one L2).  The hint changes only the loads' cache policy and where the
+ *                  chunks run: the output is the same, bit for bit, for any values (an
+ *                  inaccurate hint only costs time).  The host knows the counts from its block
+ *                  refcounts (the leading blocks with refcount > 1).
  * num_seqs must be <= 8192 when shared_blocks is given (the counts are staged in LDS beside the
  * context lengths).  Other arguments, errors and the workspace as for
  * pa_paged_attention_decode_phase.
