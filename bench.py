@@ -78,8 +78,9 @@ def parse_args():
                    help="how the headline step appends the decode rows' new tokens: inside the decode call "
                         "(pa_paged_attention_decode_append, default) or by pa_kv_cache_write before it; the "
                         "other workloads always use pa_kv_cache_write")
-    p.add_argument("--graph", action="store_true",
-                   help="also replay the headline step from HIP graphs and report it under graph_step")
+    p.add_argument("--no-graph", action="store_true",
+                   help="skip the HIP-graph replay of the headline step (graph_step, measured after the "
+                        "timed region; the tiny fp32 step is always replayed)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device copy (HBM counter calibration) and exit")
@@ -596,7 +597,7 @@ def main():
         parts = PARTITIONS.get(name, (0,))
         if headline and args.partition_size >= 0:
             parts = (args.partition_size,)
-        graph = (args.graph and headline) or name == "tiny_fp32"
+        graph = (headline and not args.no_graph) or name == "tiny_fp32"
         return measure(batch, dev, layers, args.steps, args.warmup, parts, args.append == "fused" and headline, graph,
                        args.per_step)
 
