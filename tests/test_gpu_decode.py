@@ -477,31 +477,44 @@ def test_shared_block_hint_changes_nothing_but_cache_policy(cache, B):
 def test_shared_block_hint_chunk_placement(cache, B, hkv, P):
     """With the hint the chunks are placed on the XCDs in contiguous ranges of the run list
     instead of round-robin.  Partitions of 1-4 units give several chunks per wave (more chunks
-    than the grid has waves), kv head counts that do and do not divide the 8 XCDs, and the
-    automatic split: every unit is still attended once, the output bits equal the decode's
-    without the hint, and it matches the oracle."""
+    than the grid has waves), kv head counts that do and do not divide the 8 XCDs, the
+    automatic split, and empty sequences between the runs: every unit is still attended once,
+    the output bits equal the decode's without the hint, and it matches the oracle."""
     rng = np.random.default_rng(hkv * 100 + P)
     ctx = rng.integers(1, 3000, size=48)
     sharing = list(range(1, 48, 2))
     ctx[sharing] = 513 + rng.integers(0, 2500, size=len(sharing))  # the 512-token prefix and more
-    ctx[::14] = 0  # empty sequences between the runs
     b = W.build_batch(ctx, num_heads=hkv * 4, num_kv_heads=hkv, head_dim=128, q_dtype=W.BF16, cache_dtype=cache,
-                      seed=43, block_size=B, query_lens=(ctx > 0).astype(np.int32), shared_prefix_len=512,
-                      sharing=sharing)
+                      seed=43, block_size=B, shared_prefix_len=512, sharing=sharing)
     kp_h, vp_h = oracle_pool(b, include_new=True)
     db = DeviceBatch(b)
     kp, vp = to_dev(kp_h, b.cache_dtype), to_dev(vp_h, b.cache_dtype)
-    base = db.decode(kp, vp, partition_size=P)
-    assert_close(b, out_to_f64(base), oracle_attention(b, kp_h, vp_h))
-    counts = b.shared_block_counts()
-    assert counts.max() > 0
+    counts = torch.from_numpy(b.shared_block_counts()).cuda()
+    assert int(counts.max()) > 0
     ws = ops.decode_workspace(b.num_seqs, b.num_heads, b.num_kv_heads, b.head_dim, b.max_context_len, b.block_size, P)
-    out = torch.empty_like(db.query)
-    ops.paged_attention_decode(out, db.query, kp, vp, db.tables, db.ctx, max_context_len=b.max_context_len,
-                               num_kv_heads=b.num_kv_heads, scale=b.scale, block_size=b.block_size,
-                               k_scale=db.k_scale, v_scale=db.v_scale, partition_size=P, workspace=ws,
-                               shared_blocks=torch.from_numpy(counts).cuda())
-    assert torch.equal(out.view(torch.uint8), base.view(torch.uint8))
+
+    def hinted():
+        out = torch.empty_like(db.query)
+        ops.paged_attention_decode(out, db.query, kp, vp, db.tables, db.ctx, max_context_len=b.max_context_len,
+                                   num_kv_heads=b.num_kv_heads, scale=b.scale, block_size=b.block_size,
+                                   k_scale=db.k_scale, v_scale=db.v_scale, partition_size=P, workspace=ws,
+                                   shared_blocks=counts)
+        return out
+
+    base = db.decode(kp, vp, partition_size=P)
+    ref = oracle_attention(b, kp_h, vp_h)
+    assert_close(b, out_to_f64(base), ref)
+    assert torch.equal(hinted().view(torch.uint8), base.view(torch.uint8))
+    # empty sequences between the runs
+    db.ctx = db.ctx.clone()
+    db.ctx[::14] = 0
+    base0 = db.decode(kp, vp, partition_size=P)
+    got0 = hinted()
+    assert torch.equal(got0.view(torch.uint8), base0.view(torch.uint8))
+    assert torch.count_nonzero(got0[::14].float()) == 0
+    keep = np.ones(b.num_seqs, bool)
+    keep[::14] = False
+    assert_close(b, out_to_f64(got0)[keep], ref[keep])  # the others' chunks are cut elsewhere now
 
 
 def test_shared_block_hint_short_contexts():
