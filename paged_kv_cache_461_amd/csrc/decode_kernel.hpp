@@ -778,7 +778,8 @@ __global__ __launch_bounds__(kDecodeThreads, (stream_min_waves<KT, D, G, FUSED>(
     };
     // chunk_blocks < 0: one chunk per run.  The host picks it when every run fits in one
     // minimum chunk, so no run is split, nothing is merged and the merge launch is skipped
-    // (small batches, where a launch costs more than the work).  Chunk k is then run k.
+    // (small batches, where a launch costs more than the work).  Chunk k is then the run of
+    // sequence k / Hkv and kv head k mod Hkv (no run records, so the numbering is free).
     constexpr bool per_run = PER_RUN;
     ChunkMap cm{};
     auto count_chunks = [&](int64_t U) { return U > 0 ? min(cm.of_unit(U - 1) + 1, a.max_chunks) : (int64_t)0; };
