@@ -385,21 +385,14 @@ __device__ __forceinline__ float mf_swap(float x, bool halves, bool is_max)
     return is_max ? __builtin_fmaxf(a, b) : a + b;
 }
 
-// Four bf16 (or four 8-bit codes widened to bf16) of lane's V piece, elements at or past
-// `keep` zeroed (they may hold anything, including NaN, and 0 * NaN would leak into the sum).
+// Four bf16 (or four 8-bit codes widened to bf16) of lane's V piece.
 template <int KT>
-__device__ __forceinline__ uint2 mf_v_operand(const typename MShape<kBF16, KT, 64, 1>::VP& v, int keep)
+__device__ __forceinline__ uint2 mf_v_operand(const typename MShape<kBF16, KT, 64, 1>::VP& v)
 {
-    uint2 r;
     if constexpr (DtypeBytes<KT>::value == 2)
-        r = v;
+        return v;
     else
-        r = make_uint2(q8x2_to_bf16x2<KT, false>(v), q8x2_to_bf16x2<KT, true>(v));
-    if (keep < 4) {
-        r.x = keep >= 2 ? r.x : keep == 1 ? r.x & 0xFFFFu : 0u;
-        r.y = keep >= 4 ? r.y : keep == 3 ? r.y & 0xFFFFu : 0u;
-    }
-    return r;
+        return make_uint2(q8x2_to_bf16x2<KT, false>(v), q8x2_to_bf16x2<KT, true>(v));
 }
 
 template <int QT, int KT, int D, int G>
@@ -429,7 +422,7 @@ __device__ __forceinline__ void attend_mfma(MAcc<QT, KT, D, G>& st, const MQ<QT,
 #pragma unroll
     for (int r = 0; r < 4; r++) {
         s2[r] *= c2;
-        if (n_valid < kUnitTokens) s2[r] = tb + r < n_valid ? s2[r] : -__builtin_inff();
+        if (__builtin_amdgcn_readfirstlane(n_valid) < kUnitTokens) s2[r] = tb + r < n_valid ? s2[r] : -__builtin_inff();
     }
     bool need = false;
 #pragma unroll
@@ -452,10 +445,20 @@ __device__ __forceinline__ void attend_mfma(MAcc<QT, KT, D, G>& st, const MQ<QT,
     st.l = dot2_bf16(pp0, kBf16OnePair, st.l);
     st.l = dot2_bf16(pp1, kBf16OnePair, st.l);
     const mf_s16x4 pb = __builtin_bit_cast(mf_s16x4, make_uint2(pp0, pp1));
-    const int keep = n_valid - tb;
+    // V elements of tokens at or past n_valid are zeroed: in a ragged unit they may hold anything,
+    // including NaN, and 0 * NaN would leak into the sum.  The lane's tokens tb..tb+3 are the four
+    // bf16 of its operand; the masks are worked out once per unit, and only for a ragged one.
+    uint32_t kx = 0xFFFFFFFFu, ky = 0xFFFFFFFFu;
+    if (__builtin_amdgcn_readfirstlane(n_valid) < kUnitTokens) {
+        const int keep = n_valid - tb;
+        kx = keep >= 2 ? 0xFFFFFFFFu : keep == 1 ? 0xFFFFu : 0u;
+        ky = keep >= 4 ? 0xFFFFFFFFu : keep == 3 ? 0xFFFFu : 0u;
+    }
 #pragma unroll
     for (int t = 0; t < M::NT; t++) {
-        const uint2 av = mf_v_operand<KT>(vb[t], keep);
+        uint2 av = mf_v_operand<KT>(vb[t]);
+        av.x &= kx;
+        av.y &= ky;
         st.o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(mf_s16x4, av), pb, st.o[t], 0, 0, 0);
     }
 }
